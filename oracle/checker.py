@@ -1,0 +1,85 @@
+"""Tolerance checker comparing a tested O / LSE with the fp64 oracle.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/attention.py``).
+
+Bars (element by element, over every compared row):
+  * O (bfloat16 result expanded to float64): max |dO| <= 2e-2 and mean |dO| <= 2e-3;
+    any NaN or Inf fails; a row the oracle marks fully masked must be exactly 0.
+  * LSE (float32 result): |dLSE| <= 1e-3 on rows with a finite oracle value;
+    a fully masked row must be exactly -inf; any NaN fails.
+Why these bars hold for a correct bf16 kernel: O is a convex combination of V
+rows, so |O| <= max|V| and its final bf16 rounding is at most half an ulp
+(2**-7 for |O| < 4); the fp32 running state adds far less.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+O_MAX_ABS = 2e-2
+O_MEAN_ABS = 2e-3
+LSE_MAX_ABS = 1e-3
+
+
+@dataclass
+class CheckResult:
+    ok: bool
+    o_max_abs: float
+    o_mean_abs: float
+    lse_max_abs: float
+    reasons: list
+
+    def __str__(self) -> str:
+        state = "PASS" if self.ok else "FAIL"
+        return (f"{state} O max|d|={self.o_max_abs:.3e} mean|d|={self.o_mean_abs:.3e} "
+                f"LSE max|d|={self.lse_max_abs:.3e} {'; '.join(self.reasons)}")
+
+
+def check(o_test: np.ndarray, o_ref: np.ndarray, lse_test: Optional[np.ndarray] = None,
+          lse_ref: Optional[np.ndarray] = None) -> CheckResult:
+    """Compare float64 views of the tested outputs with the oracle's.
+
+    ``o_test``/``o_ref``: [..., R, d]; ``lse_test``/``lse_ref``: [..., R].
+    A row is fully masked when its oracle LSE is -inf (the oracle's O is 0 there).
+    """
+    o_test = np.asarray(o_test, dtype=np.float64)
+    o_ref = np.asarray(o_ref, dtype=np.float64)
+    reasons = []
+    if o_test.shape != o_ref.shape:
+        return CheckResult(False, np.inf, np.inf, np.inf, [f"O shape {o_test.shape} != {o_ref.shape}"])
+    if not np.all(np.isfinite(o_test)):
+        reasons.append(f"O has {int(np.sum(~np.isfinite(o_test)))} non-finite values")
+    diff = np.abs(o_test - o_ref)
+    diff = np.where(np.isfinite(diff), diff, np.inf)
+    o_max = float(diff.max()) if diff.size else 0.0
+    o_mean = float(diff.mean()) if diff.size else 0.0
+    if o_max > O_MAX_ABS:
+        reasons.append(f"O max abs {o_max:.3e} > {O_MAX_ABS}")
+    if o_mean > O_MEAN_ABS:
+        reasons.append(f"O mean abs {o_mean:.3e} > {O_MEAN_ABS}")
+    lse_max = 0.0
+    if lse_ref is not None:
+        lse_ref = np.asarray(lse_ref, dtype=np.float64)
+        dead = np.isneginf(lse_ref)
+        if np.any(dead):
+            rows_nonzero = np.any(o_test[dead] != 0.0, axis=-1) if o_test[dead].size else np.zeros(0, bool)
+            if np.any(rows_nonzero):
+                reasons.append(f"{int(rows_nonzero.sum())} fully masked rows have nonzero O")
+        if lse_test is not None:
+            lse_test = np.asarray(lse_test, dtype=np.float64)
+            if lse_test.shape != lse_ref.shape:
+                return CheckResult(False, o_max, o_mean, np.inf, [f"LSE shape {lse_test.shape} != {lse_ref.shape}"])
+            if np.any(np.isnan(lse_test)):
+                reasons.append(f"LSE has {int(np.isnan(lse_test).sum())} NaN values")
+            if np.any(dead) and not np.all(np.isneginf(lse_test[dead])):
+                reasons.append("fully masked rows have LSE != -inf")
+            live = ~dead
+            if np.any(live):
+                d = np.abs(lse_test[live] - lse_ref[live])
+                d = np.where(np.isfinite(d), d, np.inf)
+                lse_max = float(d.max())
+                if lse_max > LSE_MAX_ABS:
+                    reasons.append(f"LSE max abs {lse_max:.3e} > {LSE_MAX_ABS}")
+    return CheckResult(not reasons, o_max, o_mean, lse_max, reasons)

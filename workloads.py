@@ -1,0 +1,130 @@
+"""Seeded synthetic inputs for the attention forward pass.
+
+This module is shared by the CPU oracle's tests and by the GPU path's tests and
+benchmark. It only draws random numbers and encodes them as bfloat16 bit
+patterns; it holds none of the attention arithmetic.
+
+The pages describe random-tensor workloads in the ``[batch, heads, seq,
+head_dim]`` layout at sequence lengths 2048/4096 and head dims 64/128
+(codechina.net "GPU memory wall ... FlashAttention", §2.2 and the §5.2 table;
+"Profiling in PyTorch (part 3)", flash-backend section). They name no dataset,
+so every tensor here is iid Gaussian noise drawn from a fixed seed.
+
+Recipe (the same for every shape):
+  * one ``numpy.random.Generator(PCG64(seed))`` per workload;
+  * draw Q, then K, then V as float32 standard normals in ``[B, H, N, d]``
+    order, multiply by that tensor's standard deviation, round to bfloat16
+    (round-to-nearest-even), keep the 16-bit patterns;
+  * for a variable-length workload, draw ``seqlens_k`` after V with
+    ``integers(lo, hi + 1, size=B)``; the rows masked through ``q_start`` are
+    fixed by the workload, not drawn.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import numpy as np
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bits.
+
+    NaN inputs are not expected here (Gaussian draws are finite).
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> 16) & 1) + np.uint32(0x7FFF)
+    return ((u + bias) >> 16).astype(np.uint16)
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One attention forward problem: shapes, mask rule and input distribution."""
+
+    name: str
+    B: int
+    H: int
+    N_q: int
+    N_k: int
+    d: int
+    causal: bool
+    seed: int
+    sigma_q: float = 1.0
+    sigma_k: float = 1.0
+    sigma_v: float = 1.0
+    # variable-length keys: seqlens_k[b] ~ U{lo..hi}; None = every key valid
+    seqlens_range: Optional[tuple] = None
+    # batches whose first ``q_start_rows`` query rows attend to nothing
+    q_start_batches: Sequence[int] = field(default_factory=tuple)
+    q_start_rows: int = 0
+
+    @property
+    def scale(self) -> np.float32:
+        """Default softmax scale head_dim ** -0.5, as the float32 the kernel receives."""
+        return np.float32(1.0 / np.sqrt(np.float64(self.d)))
+
+    def flops(self) -> float:
+        """Counted flops: 4*B*H*N_q*N_k*d, halved when causal (mask-independent otherwise)."""
+        f = 4.0 * self.B * self.H * self.N_q * self.N_k * self.d
+        return f / 2 if self.causal else f
+
+    def algorithmic_bytes(self) -> float:
+        """Q, K, V read once (bf16), O written once (bf16), LSE written once (fp32)."""
+        return 2.0 * self.B * self.H * (self.N_q * self.d * 2 + self.N_k * self.d * 2) + 4.0 * self.B * self.H * self.N_q
+
+
+# The five workloads of the benchmark statement, in order.
+WORKLOADS = {
+    "tiny_causal_d64": Workload("tiny_causal_d64", B=1, H=2, N_q=256, N_k=256, d=64, causal=True, seed=1001),
+    "causal_n2048_d128": Workload("causal_n2048_d128", B=4, H=16, N_q=2048, N_k=2048, d=128, causal=True, seed=1002),
+    "causal_n4096_d128": Workload("causal_n4096_d128", B=1, H=32, N_q=4096, N_k=4096, d=128, causal=True, seed=1003),
+    "noncausal_n4096_d128": Workload("noncausal_n4096_d128", B=1, H=32, N_q=4096, N_k=4096, d=128, causal=False, seed=1003),
+    "varlen_n1024_d64": Workload("varlen_n1024_d64", B=8, H=32, N_q=1024, N_k=1024, d=64, causal=False, seed=1004,
+                                 seqlens_range=(256, 1024), q_start_batches=(1, 5), q_start_rows=64),
+    "causal_n16384_d128_stress": Workload("causal_n16384_d128_stress", B=1, H=8, N_q=16384, N_k=16384, d=128,
+                                          causal=True, seed=1005, sigma_q=2.0),
+}
+
+HEADLINE = "causal_n4096_d128"
+
+
+@dataclass
+class Inputs:
+    """bf16 bit patterns (uint16) in [B, H, N, d] plus the optional int32 mask vectors."""
+
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    seqlens_k: Optional[np.ndarray]
+    q_start: Optional[np.ndarray]
+    scale: np.float32
+    causal: bool
+
+
+def make_inputs(w: Workload) -> Inputs:
+    """Draw the workload's tensors from its seed."""
+    g = np.random.Generator(np.random.PCG64(w.seed))
+    shp_q = (w.B, w.H, w.N_q, w.d)
+    shp_k = (w.B, w.H, w.N_k, w.d)
+    q = f32_to_bf16_bits(g.standard_normal(shp_q, dtype=np.float32) * np.float32(w.sigma_q))
+    k = f32_to_bf16_bits(g.standard_normal(shp_k, dtype=np.float32) * np.float32(w.sigma_k))
+    v = f32_to_bf16_bits(g.standard_normal(shp_k, dtype=np.float32) * np.float32(w.sigma_v))
+    seqlens = None
+    if w.seqlens_range is not None:
+        lo, hi = w.seqlens_range
+        seqlens = g.integers(lo, hi + 1, size=w.B).astype(np.int32)
+    q_start = None
+    if w.q_start_batches:
+        q_start = np.zeros(w.B, dtype=np.int32)
+        for b in w.q_start_batches:
+            q_start[b] = w.q_start_rows
+    return Inputs(q=q, k=k, v=v, seqlens_k=seqlens, q_start=q_start, scale=w.scale, causal=w.causal)
+
+
+def make_random(B: int, H: int, N_q: int, N_k: int, d: int, seed: int, sigma=(1.0, 1.0, 1.0)):
+    """Seeded bf16 Q, K, V bits for an arbitrary shape (edge-case tests)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    q = f32_to_bf16_bits(g.standard_normal((B, H, N_q, d), dtype=np.float32) * np.float32(sigma[0]))
+    k = f32_to_bf16_bits(g.standard_normal((B, H, N_k, d), dtype=np.float32) * np.float32(sigma[1]))
+    v = f32_to_bf16_bits(g.standard_normal((B, H, N_k, d), dtype=np.float32) * np.float32(sigma[2]))
+    return q, k, v
