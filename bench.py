@@ -1,0 +1,168 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one call of the C-ABI ``attn_fwd`` over the whole workload (one
+kernel launch: tile schedule, Q/K/V staging, QK^T, mask, online softmax, PV,
+epilogue). Inputs are synthetic seeded bf16 tensors already resident in HBM
+when the timed region starts. W untimed warmup steps, then exactly K timed
+steps bracketed by a device synchronisation on both sides; per-launch times
+come from HIP events recorded on the stream the kernel is launched on.
+
+Prints ONE JSON line on stdout. ``value`` is TFLOP/s with the counted flops
+4*B*H*N_q*N_k*d (halved when causal). ``roofline`` prices the kernel against
+the MI355X dense bf16 MFMA peak; ``cpu_baseline`` times the fp64 CPU oracle on
+a bounded sample of the same workload (test infrastructure, never the product
+path).
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import HEADLINE, WORKLOADS, make_inputs  # noqa: E402
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+METRIC = "attention fwd TFLOP/s (bf16, causal, N=4096, d=128) + % of MFMA bf16 peak"
+KERNEL_SRC = os.path.join(ROOT, "tiled_attention_16_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_hbm_traffic.md")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when the summary is missing, covers another workload or an older kernel."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE, encoding="utf-8").read()
+    src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not src or src.group(1) != kernel_source_hash():
+        return None
+    m = re.search(rf"traffic_bytes_per_launch\[{re.escape(workload)}\]:\s*([0-9.eE+]+)", text)
+    return float(m.group(1)) if m else None
+
+
+def cpu_baseline(w, inp, budget_s: float = 12.0):
+    """Time the fp64 oracle on whole heads of the workload until the budget is spent."""
+    import threadpoolctl
+
+    from oracle import attention, bf16_bits_to_f64
+
+    heads_done = 0
+    t0 = time.perf_counter()
+    b = 0
+    for h in range(w.H):
+        sl = None if inp.seqlens_k is None else inp.seqlens_k[b:b + 1]
+        qs = None if inp.q_start is None else inp.q_start[b:b + 1]
+        attention(bf16_bits_to_f64(inp.q[b:b + 1, h:h + 1]), bf16_bits_to_f64(inp.k[b:b + 1, h:h + 1]),
+                  bf16_bits_to_f64(inp.v[b:b + 1, h:h + 1]), float(inp.scale), w.causal, seqlens_k=sl, q_start=qs)
+        heads_done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = w.flops() / (w.B * w.H) * heads_done
+    blas = [d.get("num_threads", 1) for d in threadpoolctl.threadpool_info() if d.get("user_api") == "blas"]
+    cores = max(blas) if blas else 1
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 oracle on {heads_done} of {w.B * w.H} (batch, head) pairs of {w.name}, all "
+                      f"{w.N_q} rows each, {dt:.1f} s wall; {len(os.sched_getaffinity(0))} host cores visible",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention forward of this library runs on a single "
+              "MI355X; multi-GPU runs are not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tiled_attention_16_amd as ta
+
+    ta.load_library()
+    w = WORKLOADS[args.workload]
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    sl = torch.from_numpy(inp.seqlens_k).to(dev) if inp.seqlens_k is not None else None
+    qs = torch.from_numpy(inp.q_start).to(dev) if inp.q_start is not None else None
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N_q), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ta.attn_fwd(q, k, v, causal=w.causal, scale=float(inp.scale), seqlens_k=sl, q_start=qs, out=o, lse=lse,
+                    stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i].record(stream)
+        step()
+    ev[args.steps].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])   # ms per launch
+    total_ms = ev[0].elapsed_time(ev[args.steps])
+    ms_per_step = total_ms / args.steps
+    flops = w.flops()
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    avg_launch_s = float(per.mean()) * 1e-3
+    achieved = flops / avg_launch_s / 1e12
+    traffic = measured_traffic(w.name)
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.N_q, "N_k": w.N_k, "d": w.d,
+                   "causal": w.causal, "varlen": inp.seqlens_k is not None},
+        "pct_of_mfma_bf16_peak": round(100.0 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic},
+        "launch_ms": {"mean": round(float(per.mean()), 5), "median": round(float(np.median(per)), 5),
+                      "min": round(float(per.min()), 5)},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

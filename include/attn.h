@@ -1,0 +1,101 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) fused attention forward library.
+ *
+ * Pages cited:
+ *   [PT2CUDA]  aiknowledge.cn, "4.5 注意力优化实战：从PyTorch到CUDA的完整流程".
+ *   [MEMWALL]  codechina.net, "GPU 内存墙 ... FlashAttention" article.
+ *   [PROFILE3] "Profiling in PyTorch (part 3): Attention is all you profile".
+ *
+ * The operation (one call = one fused kernel launch):
+ *
+ *   O[b,h] = softmax(Q[b,h] K[b,h]^T * scale + mask) V[b,h]
+ *
+ * as written unfused in [PT2CUDA] step 1 (baseline implementation) and
+ * [PROFILE3] (naive attention module), computed tile by tile with the online
+ * softmax of [PT2CUDA] step 3.1 and [MEMWALL] §3.2 so that the [N_q, N_k]
+ * score matrix never reaches device memory.
+ *
+ * The mask is a rule, not a tensor. Query row i of batch b may attend to key j
+ * iff all of:
+ *   j <  kv_len[b]   with kv_len[b] = clamp(seqlens_k[b], 0, N_k), or N_k when
+ *                    seqlens_k is NULL (variable-length keys marked by a
+ *                    valid length, [MEMWALL] §6.2);
+ *   i >= qs[b]       with qs[b] = clamp(q_start[b], 0, N_q), or 0 when q_start
+ *                    is NULL (leading query rows that attend to nothing);
+ *   j <= i           when causal != 0 (the lower-triangular mask of [PROFILE3];
+ *                    top-left aligned when N_q != N_k).
+ * A row with no allowed key outputs O = +0 and LSE = -inf, never NaN (the
+ * NaN-safe softmax of [PROFILE3], math-backend section). Keys at or beyond
+ * kv_len[b] are ignored entirely: their K and V contents are never used, so
+ * padding may hold any bit pattern.
+ *
+ * LSE[b,h,i] = ln(sum over allowed j of exp(S_ij)), S = Q K^T * scale: the
+ * natural-log log-sum-exp of the scaled scores, in float32.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by attn_fwd. */
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,      /* a required pointer is NULL                          */
+  ATTN_ERR_SHAPE = 2,     /* a size is negative or the problem is too large      */
+  ATTN_ERR_HEAD_DIM = 3,  /* d is not 64 or 128                                  */
+  ATTN_ERR_SCALE = 4,     /* scale is NaN or infinite                            */
+  ATTN_ERR_ALIGN = 5,     /* q, k, v or o not 16-byte aligned, lse not 4-byte    */
+  ATTN_ERR_ALIAS = 6,     /* o or lse overlaps an input or each other            */
+  ATTN_ERR_LAUNCH = 7     /* the kernel launch failed (hipGetLastError)          */
+} attn_status;
+
+/*
+ * attn_fwd - fused scaled-dot-product attention forward, bf16 in, bf16 out.
+ *
+ * Arguments (all pointers are DEVICE memory owned by the caller; the library
+ * never allocates, frees, synchronises or keeps state, so calls are
+ * reentrant and may run on any stream):
+ *   q          bf16 [B, H, N_q, d], contiguous, d innermost, read only.
+ *   k, v       bf16 [B, H, N_k, d], contiguous, read only. May be NULL iff N_k == 0.
+ *   o          bf16 [B, H, N_q, d], contiguous, written in full (every element,
+ *              fully masked rows included).
+ *   lse        float32 [B, H, N_q] or NULL; when given, written in full.
+ *   B, H       batch and head counts (>= 0).
+ *   N_q, N_k   query and key sequence lengths (>= 0).
+ *   d          head dimension: 64 or 128.
+ *   scale      multiplier of Q K^T, any finite value (the usual d^-0.5 of
+ *              [PT2CUDA] step 1).
+ *   causal     nonzero: key j is visible to row i only when j <= i.
+ *   seqlens_k  int32 [B] device array or NULL: valid key count per batch,
+ *              clamped to [0, N_k] on the device.
+ *   q_start    int32 [B] device array or NULL: rows i < q_start[b] of batch b
+ *              attend to nothing, clamped to [0, N_q] on the device.
+ *   stream     HIP stream to launch on (0 = null stream).
+ *
+ * Errors: argument errors are detected on the host and returned BEFORE any HIP
+ * call (nothing is launched, no device state is touched). When B*H*N_q == 0
+ * the call returns ATTN_OK without launching; then q, o may be NULL. A launch
+ * failure returns ATTN_ERR_LAUNCH. Faults inside the kernel surface at the
+ * caller's next synchronisation, as usual for HIP. The values of seqlens_k and
+ * q_start are never read on the host.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int N_q, int N_k, int d, float scale, int causal,
+             const int32_t* seqlens_k, const int32_t* q_start, hipStream_t stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* attn_status_str(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,97 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any HIP call (CPU only: nothing is launched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import tiled_attention_16_amd as ta
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "tiled_attention_16_amd", "libattn.so")
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "attn.h"), encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libattn.so is not built: run __graft_entry__.build()")
+    return ta.load_library()
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(ta.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_version_and_status_strings(lib):
+    assert ta.attn_version() == 100
+    for code in range(8):
+        s = ta.attn_status_str(code)
+        assert s and s != "unknown status"
+    assert ta.attn_status_str(99) == "unknown status"
+
+
+A16 = 0x10000   # a 16-byte aligned fake address: never dereferenced, the call returns first
+
+
+def call(**kw):
+    args = dict(q=A16, k=A16 * 2, v=A16 * 3, o=A16 * 4, lse=A16 * 5, B=1, H=2, N_q=8, N_k=8, d=64, scale=0.125,
+                causal=False, seqlens_k=0, q_start=0, stream=0)
+    args.update(kw)
+    return ta.attn_fwd_raw(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), ta.ATTN_ERR_SHAPE),
+    (dict(N_k=-3), ta.ATTN_ERR_SHAPE),
+    (dict(d=96), ta.ATTN_ERR_HEAD_DIM),
+    (dict(d=0), ta.ATTN_ERR_HEAD_DIM),
+    (dict(scale=float("nan")), ta.ATTN_ERR_SCALE),
+    (dict(scale=float("inf")), ta.ATTN_ERR_SCALE),
+    (dict(q=0), ta.ATTN_ERR_NULL),
+    (dict(o=0), ta.ATTN_ERR_NULL),
+    (dict(k=0), ta.ATTN_ERR_NULL),
+    (dict(q=A16 + 8), ta.ATTN_ERR_ALIGN),
+    (dict(v=A16 * 3 + 2), ta.ATTN_ERR_ALIGN),
+    (dict(lse=A16 * 5 + 2), ta.ATTN_ERR_ALIGN),
+    (dict(o=A16 + 16), ta.ATTN_ERR_ALIAS),          # o overlaps q (2*8*64*2 bytes long)
+    (dict(lse=A16 * 4 + 64), ta.ATTN_ERR_ALIAS),    # lse inside o
+    (dict(B=1 << 20, H=1 << 12, N_q=1 << 12), ta.ATTN_ERR_SHAPE),   # too many workgroups
+])
+def test_argument_errors_return_before_any_hip_call(lib, kw, status):
+    assert call(**kw) == status
+
+
+def test_empty_problem_is_a_noop(lib):
+    # nothing to write: returns OK without touching the (NULL) pointers or the GPU
+    assert call(B=0, q=0, o=0, lse=0) == ta.ATTN_OK
+    assert call(N_q=0, q=0, o=0, lse=0, k=0, v=0) == ta.ATTN_OK
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ta.attn_fwd(q, q, q)
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(ta, "_lib", None)
+    monkeypatch.setattr(ta, "_LIB_PATH", "/nonexistent/libattn.so")
+    with pytest.raises(RuntimeError):
+        ta.load_library()

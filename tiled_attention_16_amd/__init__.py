@@ -1,0 +1,119 @@
+"""Python binding of the MI355X fused attention forward library (``libattn.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernel behind ``attn_fwd`` in ``include/attn.h``. PyTorch supplies device
+memory and the current stream. There is no fallback: if the library is
+missing or the tensors are not on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+ATTN_OK = 0
+ATTN_ERR_NULL = 1
+ATTN_ERR_SHAPE = 2
+ATTN_ERR_HEAD_DIM = 3
+ATTN_ERR_SCALE = 4
+ATTN_ERR_ALIGN = 5
+ATTN_ERR_ALIAS = 6
+ATTN_ERR_LAUNCH = 7
+
+# every symbol include/attn.h declares
+EXPORTS = ("attn_fwd", "attn_status_str", "attn_version")
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load ``libattn.so`` (built by ``tiled_attention_16_amd.build``); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m tiled_attention_16_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_status_str.argtypes = [ctypes.c_int]
+    lib.attn_version.restype = ctypes.c_int
+    lib.attn_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def attn_status_str(status: int) -> str:
+    return load_library().attn_status_str(int(status)).decode()
+
+
+def attn_version() -> int:
+    return int(load_library().attn_version())
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(f"attn_fwd failed: {attn_status_str(status)} (status {status})")
+        self.status = status
+
+
+def attn_fwd_raw(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N_q: int, N_k: int, d: int,
+                 scale: float, causal: bool, seqlens_k: int, q_start: int, stream: int) -> int:
+    """The C entry point with plain integers for pointers; returns the status code."""
+    return int(load_library().attn_fwd(q or None, k or None, v or None, o or None, lse or None,
+                                       int(B), int(H), int(N_q), int(N_k), int(d), ctypes.c_float(scale),
+                                       1 if causal else 0, seqlens_k or None, q_start or None, stream or None))
+
+
+def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None, seqlens_k=None, q_start=None,
+             return_lse: bool = True, out=None, lse=None, stream=None) -> Tuple[object, Optional[object]]:
+    """Fused attention forward on bf16 ``[B, H, N, d]`` CUDA (HIP) tensors.
+
+    Returns ``(o, lse)``; ``lse`` is None unless ``return_lse``. ``scale``
+    defaults to ``d ** -0.5``. ``seqlens_k`` / ``q_start`` are optional int32
+    device tensors of shape ``[B]``. The kernel is launched on ``stream`` (a
+    ``torch.cuda.Stream``) or on torch's current stream.
+    """
+    import torch
+
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise ValueError(f"{name} must be a bfloat16 GPU tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+    B, H, N_q, d = q.shape
+    if k.shape[:2] != (B, H) or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    N_k = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    for name, t in (("seqlens_k", seqlens_k), ("q_start", q_start)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_cuda or t.numel() != B or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 GPU tensor of {B} elements")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, N_q) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, N_q] tensor")
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    status = lib.attn_fwd(q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None,
+                          out.data_ptr() or None, (lse.data_ptr() or None) if lse is not None else None,
+                          B, H, N_q, N_k, d, ctypes.c_float(scale), 1 if causal else 0,
+                          seqlens_k.data_ptr() if seqlens_k is not None else None,
+                          q_start.data_ptr() if q_start is not None else None,
+                          ctypes.c_void_p(st.cuda_stream))
+    if status != ATTN_OK:
+        raise AttnError(status)
+    return out, (lse if return_lse else None)
