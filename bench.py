@@ -33,7 +33,7 @@ from workloads import HEADLINE, WORKLOADS, make_inputs  # noqa: E402
 MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 METRIC = "attention fwd TFLOP/s (bf16, causal, N=4096, d=128) + % of MFMA bf16 peak"
 KERNEL_SRC = os.path.join(ROOT, "tiled_attention_16_amd", "csrc", "attn_fwd.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_hbm_traffic.md")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash() -> str:
@@ -44,9 +44,10 @@ def kernel_source_hash() -> str:
 def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when the summary is missing, covers another workload or an older kernel."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = os.path.join(PROFILES, f"attn_fwd_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE, encoding="utf-8").read()
+    text = open(path, encoding="utf-8").read()
     src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     if not src or src.group(1) != kernel_source_hash():
         return None
@@ -81,6 +82,19 @@ def cpu_baseline(w, inp, budget_s: float = 12.0):
             "seconds": dt}
 
 
+def copy_calibration(torch, mib: int):
+    """Plain device-to-device copies of a known size: each launch reads and writes
+    exactly ``mib`` MiB, so the counters it reads calibrate the attention kernel's."""
+    n = mib << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -88,6 +102,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run 5 plain device copies of MIB MiB each (the reference "
+                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the attention forward of this library runs on a single "
@@ -95,6 +112,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
+        return
 
     import tiled_attention_16_amd as ta
 
