@@ -10,46 +10,56 @@
 // Work decomposition ([MEMWALL] §2.2, outer loop over query blocks, inner loop
 // over key/value blocks): one workgroup of 4 wave64s owns a 128-row query tile
 // of one (batch, head); each wave owns 32 of those rows for the whole launch.
-// The workgroup walks the 64-key K/V tiles its rows can see. Causal tiles above
-// the diagonal are never visited; tiles past the batch's valid key length are
-// never visited.
+// The workgroup walks the 64-key K/V tiles its rows can see; causal tiles above
+// the diagonal and tiles past the batch's valid key length are never visited,
+// and a wave skips the arithmetic of tiles that lie wholly above its own rows.
+//
+// Data movement ([MEMWALL] §4.3 double buffering; [PT2CUDA] step 5): K and V
+// tiles go from global memory straight into LDS with the gfx950 16-byte
+// global_load_lds copy, no register staging. K and V each have two LDS stages;
+// the copies for K tile j+2 and V tile j+1 are in flight while tile j is
+// computed, and one barrier per tile both publishes the landed tiles and frees
+// the stages read in the previous step. Inside a stage, row r's 16-byte chunk c
+// sits at chunk position c ^ swz(r): the MFMA operand reads (ds_read_b128 for K,
+// the transposing ds_read_b64_tr_b16 for V) then touch distinct banks.
 //
 // Per K/V tile, per wave (the online softmax of [PT2CUDA] step 3.1 and
 // [MEMWALL] §3.2, in the exp2 domain with c = |scale| * log2(e)):
 //   S^T = K Q^T on MFMA 32x32x16 bf16 -> fp32. Computing the transpose puts one
 //         query row in each lane (32 keys per lane, the other 32 keys of the
-//         tile in lane ^ 32), so the row max is an in-register max plus one
+//         tile in lane ^ 32): the row max is an in-register max plus one
 //         permlane32 swap, and the row sum needs no cross-lane step until the
 //         very end.
 //   mask  only on tiles that cross the causal diagonal, the valid key length or
 //         the masked leading rows: the score becomes -inf.
-//   m, l  running max (exp2 domain) and per-lane partial running sum. The
-//         rescale of l and O by alpha = exp2(m_old - m_new) is taken only when
-//         some row's max grew by more than kTau; otherwise the stale max keeps
-//         serving as the subtrahend. O / l is unchanged by the choice of
-//         subtrahend, so this is exactly the pages' recurrence in exact
-//         arithmetic; the exponentials stay below 2^kTau, far from overflow.
+//   m     running max of S*c per row. It is raised only when the tile's max
+//         exceeds it by more than kTau; otherwise the stale max stays the
+//         exponent's subtrahend. O / l does not depend on the subtrahend, so
+//         this is the pages' recurrence in exact arithmetic; the exponentials
+//         stay below 2^kTau. When m rises, l and O are scaled by
+//         alpha = exp2(m_old - m_new) (O lazily, before the next P V).
 //   P     = exp2(S*c - m) in fp32, summed into l in fp32, then rounded to bf16.
 //         Its accumulator layout is already the B operand layout of the next
 //         MFMA, so P never leaves registers.
-//   O^T  += V^T P^T on MFMA 32x32x16 bf16 -> fp32, V^T fetched from LDS with
-//         the gfx950 transposing read ds_read_b64_tr_b16.
+//   O^T  += V^T P^T on MFMA 32x32x16 bf16 -> fp32, V^T read from LDS with the
+//         transposing read.
+// The loop is software pipelined inside each wave: while the MFMA unit
+// computes S for tile j+1, the VALU exponentiates tile j; while it computes
+// O += P V for tile j, the VALU takes the row max of tile j+1 and forms
+// S*c - m. Two such waves share each SIMD.
 // Epilogue ([PT2CUDA] step 4.1, one division per row at the end): O = O / l
 // (0 when l = 0), LSE = ln2 * (m + log2 l) (-inf when l = 0), bf16 store.
 //
-// Data movement: Q is read once into VGPRs as MFMA operands. K and V tiles are
-// prefetched into VGPRs one tile ahead and written into one of two LDS stages
-// (double buffering, [MEMWALL] §4.3; [PT2CUDA] step 5), one barrier per tile.
-// LDS rows are padded (K: +16 B, V: 352-byte stride) so that the K operand reads
-// and the transposing V reads hit distinct banks.
-//
-// Everything is written for wave64 and the gfx950 MFMA lane layouts:
-//   32x32x16 bf16, A (M x K): lane L holds row L%32, k = 8*(L/32) + 0..7;
+// gfx950 MFMA 32x32x16 bf16 lane layouts:
+//   A (M x K): lane L holds row L%32, k = 8*(L/32) + 0..7;
 //   B (K x N): lane L holds column L%32, the same k;
 //   C (M x N): lane L reg r holds row 8*(r/4) + 4*(L/32) + r%4, column L%32.
+// ds_read_b64_tr_b16, per 16-lane group: lane 4j+k supplies 4 consecutive
+// elements of row j; afterwards lane i holds element i of each of the 4 rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
+#include <type_traits>
 
 #include "attn.h"
 
@@ -63,27 +73,38 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-constexpr int kBM = 128;       // query rows per workgroup
 constexpr int kBN = 64;        // keys per K/V tile
 constexpr int kWaves = 4;      // wave64s per workgroup, 32 query rows each
+constexpr int kBM = 32 * kWaves;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 units
 constexpr float kLn2 = 0.69314718055994530942f;
 
 template <int D>
 struct Tile {
-  static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
-  static constexpr int kKStride = 2 * D + 16;            // LDS bytes per K row
-  static constexpr int kVStride = 352;                   // LDS bytes per V row (= 96 mod 256)
-  static constexpr int kKBytes = kBN * kKStride;
-  static constexpr int kStage = kKBytes + kBN * kVStride;
-  static constexpr int kLds = 2 * kStage;
-  static constexpr int kRowsPerPass = kThreads / kChunks;  // rows one pass of 256 threads covers
-  static constexpr int kPasses = kBN / kRowsPerPass;
-  static_assert(kVStride >= 2 * D, "V row must fit its stride");
-  static_assert(kLds <= 80 * 1024, "two workgroups must fit the 160 KB LDS of a CU");
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kBytes = kBN * kRowBytes;            // one K or V stage
+  static constexpr int kLds = 4 * kBytes;                   // K0, K1, V0, V1
+  static constexpr int kCopies = kBytes / 1024;             // 1 KB wave copies per stage
+  static constexpr int kCopiesPerWave = kCopies / kWaves;
+  static constexpr int kRowsPerCopy = 1024 / kRowBytes;
+  static constexpr int kLanesPerRow = 64 / kRowsPerCopy;
+  static_assert(kCopies % kWaves == 0, "copies must split evenly over the waves");
+  static_assert(2 * kLds <= 160 * 1024, "two workgroups must fit the 160 KB LDS of a CU");
 };
+
+// Chunk position of 16-byte chunk c of row r is c ^ swz(r). For D = 128 a row
+// is 256 bytes (one sweep of the banks): 16 consecutive rows get 16 distinct
+// swizzles, and 4 consecutive rows x 2 adjacent chunks stay distinct too. For
+// D = 64 two rows share a sweep, so row bit 0 picks the half and bits 1-3 the
+// swizzle.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -104,6 +125,8 @@ __device__ __forceinline__ float lane_swap_add(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -111,11 +134,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     int causal, const int32_t* __restrict__ seqlens_k, const int32_t* __restrict__ q_start, int n_qt,
     int n_wg) {
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[T::kLds];
+  __shared__ __attribute__((aligned(1024))) char smem[T::kLds];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  const int hf = lane >> 5;
 
   // ---- work decomposition: blockIdx -> (batch*head, query tile) ----
   // Consecutive workgroup ids are dealt round-robin over the 8 XCDs; regroup so
@@ -134,18 +158,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   int qs = 0;
   if (q_start) qs = min(max(q_start[b], 0), N_q);
 
+  const int q_end = min(q0 + kBM, N_q);
   int kv_end = kv;                                 // keys this workgroup can see
-  if (causal) kv_end = min(kv_end, min(q0 + kBM, N_q));
-  if (qs >= min(q0 + kBM, N_q)) kv_end = 0;         // every row of the tile is masked
+  if (causal) kv_end = min(kv_end, q_end);
+  if (qs >= q_end) kv_end = 0;                     // every row of the tile is masked
   const int n_tiles = (kv_end + kBN - 1) / kBN;
 
-  const int row_lo = q0 + 32 * wave;                // this wave's rows: row_lo .. row_lo + 31
-  const int row_hi = row_lo + 31;
+  const int row_lo = q0 + 32 * wave;               // this wave's rows: row_lo .. row_lo + 31
+  const int row_hi = min(row_lo + 31, N_q - 1);
   const bool wave_live = row_lo < N_q && row_hi >= qs;
   const int my_row = row_lo + (lane & 31);
 
   const size_t q_base = (size_t)bh * N_q * D;
-  const size_t kv_base = (size_t)bh * N_k * D;
+  const char* kg = (const char*)(K + (size_t)bh * N_k * D);
+  const char* vg = (const char*)(V + (size_t)bh * N_k * D);
 
   // ---- Q tile -> VGPRs as the B operand of S^T = K Q^T ----
   bf16x8 qreg[D / 16];
@@ -154,152 +180,251 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (my_row < N_q)
-        x = *(const u32x4*)(Q + q_base + (size_t)my_row * D + kc * 16 + (lane >> 5) * 8);
+      if (my_row < N_q) x = *(const u32x4*)(Q + q_base + (size_t)my_row * D + kc * 16 + hf * 8);
       x ^= flip;
       qreg[kc] = as_bf16x8(x);
     }
   }
 
-  // ---- K/V tile staging: global -> VGPRs -> LDS ----
-  const int ld_row = tid / T::kChunks;   // row within a pass
-  const int ld_chunk = tid % T::kChunks;
-  u32x4 stage_k[T::kPasses], stage_v[T::kPasses];
-
-  auto load_tile = [&](int j) {
+  // ---- K/V tile copies: global -> LDS, 1 KB per wave instruction ----
+  // Copy q of this wave fills LDS bytes [1024*qi, 1024*qi + 1024) of a stage,
+  // qi = wave * kCopiesPerWave + q: lane L lands at byte 16*L, which is row
+  // qi*kRowsPerCopy + L / kLanesPerRow, chunk position L % kLanesPerRow, so it
+  // fetches logical chunk (position ^ swz(row)) of that row.
+  int cp_row[T::kCopiesPerWave], cp_off[T::kCopiesPerWave];
 #pragma unroll
-    for (int p = 0; p < T::kPasses; ++p) {
-      const int key = j * kBN + p * T::kRowsPerPass + ld_row;
-      u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
-      if (key < kv) {   // keys past the valid length are never read
-        const size_t off = kv_base + (size_t)key * D + ld_chunk * 8;
-        xk = *(const u32x4*)(K + off);
-        xv = *(const u32x4*)(V + off);
+  for (int q = 0; q < T::kCopiesPerWave; ++q) {
+    const int qi = wave * T::kCopiesPerWave + q;
+    const int r = qi * T::kRowsPerCopy + lane / T::kLanesPerRow;
+    cp_row[q] = r;
+    cp_off[q] = r * T::kRowBytes + (((lane % T::kLanesPerRow) ^ swz<D>(r)) << 4);
+  }
+  // Copy the 64 rows starting at key k0 of a head's K or V into stage dst.
+  // Rows outside [0, kv) are never read: those lanes fetch a clamped row whose
+  // data the mask ignores.
+  auto copy_tile = [&](const char* src, int k0, char* dst) __attribute__((always_inline)) {
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst +
+                          wave * T::kCopiesPerWave * 1024;
+    const bool ragged = k0 < 0 || k0 + kBN > kv;
+    const char* base = ragged ? src : src + (ptrdiff_t)k0 * T::kRowBytes;
+#pragma unroll
+    for (int q = 0; q < T::kCopiesPerWave; ++q) {
+      uint32_t voff = (uint32_t)cp_off[q];
+      if (ragged) {
+        const int key = min(max(k0 + cp_row[q], 0), kv - 1);
+        voff += (uint32_t)((key - cp_row[q]) * T::kRowBytes);
       }
-      stage_k[p] = xk;
-      stage_v[p] = xv;
+      // The copy is issued as inline assembly so that the compiler does not
+      // treat it as a pending write to every LDS address (it would then wait
+      // for it before each LDS read); completion is awaited explicitly with
+      // wait_copies() before the barrier that publishes the tile.
+      // (readfirstlane returns a signed int: widen through uint32_t so the low
+      // half is zero-extended, never sign-extended into the high half)
+      const uint32_t base_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
+      const uint32_t base_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uintptr_t)base >> 32));
+      const uint64_t sbase = ((uint64_t)base_hi << 32) | (uint64_t)base_lo;
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(__builtin_amdgcn_readfirstlane(lds0 + q * 1024)), "v"(voff), "s"(sbase)
+                   : "memory", "m0");
     }
   };
-  auto store_tile = [&](int s) {
-    char* kb = smem + s * T::kStage;
-    char* vb = kb + T::kKBytes;
-#pragma unroll
-    for (int p = 0; p < T::kPasses; ++p) {
-      const int r = p * T::kRowsPerPass + ld_row;
-      *(u32x4*)(kb + r * T::kKStride + ld_chunk * 16) = stage_k[p];
-      *(u32x4*)(vb + r * T::kVStride + ld_chunk * 16) = stage_v[p];
-    }
-  };
+  char* const kst[2] = {smem, smem + T::kBytes};
+  char* const vst[2] = {smem + 2 * T::kBytes, smem + 3 * T::kBytes};
 
-  // per-lane LDS offsets of the MFMA operand reads
-  const int k_lane_off = (lane & 31) * T::kKStride + (lane >> 5) * 16;
-  // transposing V read: 16-lane group g, lane i in it: lanes 4j..4j+3 of a group
-  // fetch row j, four consecutive 4-element pieces of 16 columns; after the
-  // transpose lane i holds column i of those 4 rows.
-  const int g16 = lane >> 4;
-  const int v_lane_off = (4 * (lane >> 5) + ((lane & 15) >> 2)) * T::kVStride + (16 * (g16 & 1) + 4 * (lane & 3)) * 2;
+  // ---- per-lane LDS offsets of the MFMA operand reads ----
+  // K (A operand of S^T = K Q^T): lane L reads row L%32 of a 32-key half
+  // tile, logical chunk 2*kc + L/32.
+  int k_off[D / 16];
+  {
+    const int r = lane & 31;
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) k_off[kc] = r * T::kRowBytes + (((2 * kc + hf) ^ swz<D>(r)) << 4);
+  }
+  // V (A operand of O^T += V^T P^T, via the transposing read): 16-key chunk cc,
+  // half hi: lane L of group g = L/16 supplies row 16*cc + 8*hi + 4*(L/32) +
+  // (L%16)/4, columns 32*db + 16*(g%2) + 4*(L%4) .. +3. After the transpose,
+  // lane L holds column 32*db + L%32 of keys 16*cc + 8*hi + 4*(L/32) + 0..3,
+  // which pairs with P's registers 8*(cc%2) + 4*hi + 0..3 of the half tile.
+  int v_off[2][D / 32];
+  {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int r = 8 * hi + 4 * hf + ((lane & 15) >> 2);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int byte = 64 * db + 32 * (g & 1) + 8 * (lane & 3);
+        v_off[hi][db] = r * T::kRowBytes + (((byte >> 4) ^ swz<D>(r)) << 4) + (byte & 15);
+      }
+    }
+  }
 
   f32x16 o_acc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o_acc[db] = (f32x16){};
   float m_run = -INFINITY;   // running max of S*c for this lane's row (same in lane ^ 32)
+  float msub = 0.f;          // subtrahend of the exponent: m_run, or 0 while m_run = -inf
   float l_run = 0.f;         // partial running sum over this lane's half of the keys
+  float alpha = 1.f;         // pending rescale of o_acc
+  bool o_stale = false;      // some lane of the wave has alpha != 1 pending
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int s = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1);
-
-    const int k_lo = j * kBN;
-    const bool skip = !wave_live || (causal && k_lo > row_hi);
-    if (!skip) {
-      const char* kb = smem + s * T::kStage;
-      const char* vb = kb + T::kKBytes;
-
-      // S^T = K Q^T for two 32-key blocks
-      f32x16 sc[2];
+  // The pipeline runs over 32-key half tiles h (keys 32h .. 32h+31).
+  // S^T of a half tile = K_h Q^T: one 32x32 block, 32 keys x 32 rows; kb
+  // points at the half tile's first K row in LDS.
+  auto qk = [&](const char* kb, f32x16& s) __attribute__((always_inline)) {
+    s = (f32x16){};
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        sc[sb] = (f32x16){};
+    for (int kc = 0; kc < D / 16; ++kc) {
+      const u32x4 a = *(const lds_u32x4*)(kb + k_off[kc]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qreg[kc], s, 0, 0, 0);
+    }
+  };
+  // Key j is allowed for this lane's row iff j <= klim (klim folds the valid
+  // length, the causal limit and the masked leading rows into one bound).
+  const int klim = my_row < qs ? -1 : min(kv - 1, causal ? my_row : 0x7fffffff);
+  // masking is needed only where the half tile crosses that bound for some row
+  auto need_mask = [&](int h) __attribute__((always_inline)) {
+    const int k0 = h * 32;
+    return (k0 + 31 >= kv) || (causal && k0 + 31 > row_lo) || (row_lo < qs);
+  };
+  auto mask = [&](int h, f32x16& s) __attribute__((always_inline)) {
+    const int lim = klim - h * 32 - 4 * hf;   // key offset within the half tile must be <= lim
 #pragma unroll
-        for (int kc = 0; kc < D / 16; ++kc) {
-          const u32x4 a = *(const u32x4*)(kb + k_lane_off + sb * 32 * T::kKStride + kc * 32);
-          sc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qreg[kc], sc[sb], 0, 0, 0);
-        }
-      }
-
-      // mask: only where the tile crosses the key length, the diagonal or masked rows
-      const bool need_mask = (k_lo + kBN > kv) || (causal && k_lo + kBN - 1 > row_lo) || (row_lo < qs);
-      if (need_mask) {
-        const bool row_ok = my_row >= qs;
+    for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3)) <= lim ? s[r] : -INFINITY;
+  };
+  // row max, running-max update, and S <- S*c - m (in place)
+  auto rowmax_shift = [&](f32x16& s, bool live) __attribute__((always_inline)) {
+    const float a0 = fmaxf(fmaxf(s[0], s[1]), s[2]), a1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
+    const float a2 = fmaxf(fmaxf(s[6], s[7]), s[8]), a3 = fmaxf(fmaxf(s[9], s[10]), s[11]);
+    const float a4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
+    const float mx = lane_swap_max(fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), s[15])));
+    const float tmax = live ? mx * c : -INFINITY;   // c > 0, so -inf stays -inf
+    const bool grow = tmax > m_run + kTau;
+    const float m_new = grow ? tmax : m_run;
+    const float a = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // m_run = -inf gives 0
+    l_run *= a;
+    alpha *= a;
+    m_run = m_new;
+    msub = (m_run == -INFINITY) ? 0.f : m_run;
+    o_stale = o_stale || __builtin_amdgcn_ballot_w64(grow) != 0;
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+    for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], c, -msub);
+  };
+  // P = exp2(S*c - m): fp32 into the row sum, bf16 into the PV operand
+  auto expo = [&](const f32x16& s, bf16x8 (&pb)[2]) __attribute__((always_inline)) {
+    float p[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k_lo + 32 * sb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const bool ok = row_ok && key < kv && (!causal || key <= my_row);
-            sc[sb][r] = ok ? sc[sb][r] : -INFINITY;
-          }
-      }
-
-      // row max over this lane's 32 keys, then over the partner lane's 32
-      float mx = sc[0][0];
+    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(s[r]);
+    l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])) +
+             (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 w = {pack2(p[8 * h + 0], p[8 * h + 1]), pack2(p[8 * h + 2], p[8 * h + 3]),
+                       pack2(p[8 * h + 4], p[8 * h + 5]), pack2(p[8 * h + 6], p[8 * h + 7])};
+      pb[h] = as_bf16x8(w);
+    }
+  };
+  // O^T += V^T P^T for a half tile whose first V row is at vb: 16-key chunk cc
+  // pairs with P registers 8*cc..
+  auto pv = [&](const char* vb, const bf16x8 (&pb)[2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
-      mx = lane_swap_max(mx);
-      const float tmax = mx * c;   // c > 0, so -inf stays -inf
-
-      if (__builtin_amdgcn_ballot_w64(tmax > m_run + kTau)) {
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o_acc[db] *= alpha;
-      }
-      const float msub = (m_run == -INFINITY) ? 0.f : m_run;
-
-      // P = exp2(S*c - m): fp32 into the row sum, bf16 into the PV operand
-      bf16x8 pb[4];
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(fmaf(sc[sb][r], c, -msub));
-          l_run += p[r];
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const u32x4 w = {pack2(p[8 * h + 0], p[8 * h + 1]), pack2(p[8 * h + 2], p[8 * h + 3]),
-                           pack2(p[8 * h + 4], p[8 * h + 5]), pack2(p[8 * h + 6], p[8 * h + 7])};
-          pb[2 * sb + h] = as_bf16x8(w);
-        }
-      }
-
-      // O^T += V^T P^T: 16-key chunk cc pairs with P registers 8*(cc%2).. of block cc/2
+    for (int cc = 0; cc < 2; ++cc) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const char* p0 = vb + v_lane_off + (16 * cc) * T::kVStride + 64 * db;
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 8 * T::kVStride));
-          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc], o_acc[db], 0, 0, 0);
-        }
+        const char* p0 = vb + 16 * cc * T::kRowBytes;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + v_off[0][db]));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + v_off[1][db]));
+        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc], o_acc[db], 0, 0, 0);
       }
     }
+  };
 
-    if (j + 1 < n_tiles) store_tile(s ^ 1);
+  // Half tiles: nh_wg for the workgroup, nh (a prefix) for this wave.
+  const int nh_wg = (kv_end + 31) / 32;
+  int nh = wave_live ? nh_wg : 0;
+  if (causal) nh = min(nh, row_hi / 32 + 1);
+
+  // One pipelined half step h: S of half h is in sc (already shifted); S of
+  // half h+1 goes to sn. kb: K rows of half h+1; vb: V rows of half h.
+  // Phase A: S of h+1 on the MFMA unit while the VALU exponentiates h.
+  // Phase B: O += P V of h on the MFMA unit while the VALU takes the row max
+  // of h+1 and forms S*c - m.
+  auto half_step = [&](int h, const char* kb, const char* vb, f32x16& sc, f32x16& sn) __attribute__((always_inline)) {
+    if (h >= nh) return;
+    if (o_stale) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o_acc[db] *= alpha;
+      alpha = 1.f;
+      o_stale = false;
+    }
+    // Half h+1 may lie past this wave's last half (then its S is computed from
+    // whatever the stage holds and discarded: no branch splits the phase).
+    const bool nxt = h + 1 < nh;
+    bf16x8 pb[2];
+    qk(kb, sn);
+    expo(sc, pb);
+    // keep P and l in this block (the compiler would otherwise sink them
+    // past the mask branch, away from the MFMAs they are meant to overlap)
+    asm volatile("" :: "v"(pb[0]), "v"(pb[1]), "v"(l_run));
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // DS read
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 40 / (D / 16), 0);   // VALU
+    }
+    if (nxt && need_mask(h + 1)) mask(h + 1, sn);
+    pv(vb, pb);
+    rowmax_shift(sn, nxt);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x002, 32 / (D / 16), 1);
+    }
+  };
+
+  // K tile t holds keys 64t .. 64t+63; V tile t holds keys 64t-32 .. 64t+31,
+  // half a tile earlier, so that step t (half steps 2t+1 and 2t+2, which read
+  // K halves 2t+2, 2t+3 and V halves 2t+1, 2t+2) reads exactly K tile t+1 and
+  // V tile t+1, from stage (t+1) % 2, while tiles t+2 are copied into the
+  // other stage. Half step 0 runs before the loop from K tile 0 and V tile 0.
+  const int n_kt = (nh_wg + 1) / 2;   // K tiles needed
+  const int n_vt = nh_wg / 2 + 1;     // V tiles needed (when nh_wg > 0)
+  constexpr int kHalf = 32 * T::kRowBytes;
+  f32x16 sa, sb;
+  if (nh_wg > 0) {
+    copy_tile(kg, 0, kst[0]);
+    if (n_kt > 1) copy_tile(kg, kBN, kst[1]);
+    copy_tile(vg, -32, vst[0]);
+    if (n_vt > 1) copy_tile(vg, kBN - 32, vst[1]);
+    wait_copies();
     __syncthreads();
+    if (nh > 0) {
+      qk(kst[0], sa);
+      if (need_mask(0)) mask(0, sa);
+      rowmax_shift(sa, true);
+    }
+    half_step(0, kst[0] + kHalf, vst[0] + kHalf, sa, sb);
+  }
+  auto step = [&](auto stage, int t) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage)::value;   // == (t + 1) % 2
+    wait_copies();
+    __syncthreads();   // tiles t+1 have landed; the stage of tiles t is free
+    if (t + 2 < n_kt) copy_tile(kg, (t + 2) * kBN, kst[S ^ 1]);
+    if (t + 2 < n_vt) copy_tile(vg, (t + 2) * kBN - 32, vst[S ^ 1]);
+    half_step(2 * t + 1, kst[S], vst[S], sb, sa);
+    half_step(2 * t + 2, kst[S] + kHalf, vst[S] + kHalf, sa, sb);
+  };
+  for (int t = 0; 2 * t + 1 < nh_wg; t += 2) {
+    step(std::integral_constant<int, 1>{}, t);
+    if (2 * t + 3 < nh_wg) step(std::integral_constant<int, 0>{}, t + 1);
+  }
+  if (o_stale) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o_acc[db] *= alpha;
   }
 
   // ---- epilogue: O / l, LSE, bf16 store ----
@@ -313,7 +438,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       for (int g = 0; g < 4; ++g) {
         const u32x2 w = {pack2(o_acc[db][4 * g + 0] * inv, o_acc[db][4 * g + 1] * inv),
                          pack2(o_acc[db][4 * g + 2] * inv, o_acc[db][4 * g + 3] * inv)};
-        *(u32x2*)(orow + 32 * db + 8 * g + 4 * (lane >> 5)) = w;
+        *(u32x2*)(orow + 32 * db + 8 * g + 4 * hf) = w;
       }
     }
     if (LSE && lane < 32)
