@@ -148,9 +148,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   // (the last one, under a causal mask) starts first.
   int lin = blockIdx.x;
   if ((n_wg & 7) == 0) lin = (lin & 7) * (n_wg >> 3) + (lin >> 3);
-  const int bh = lin / n_qt;
-  const int qt = n_qt - 1 - (lin - bh * n_qt);
+  const int n_pairs = (n_qt + 1) / 2;
+  const int bh = lin / n_pairs;
+  const int pr = lin - bh * n_pairs;
   const int b = bh / H;
+  // A workgroup owns the pair of query tiles (n_qt-1-pr, pr): under a causal
+  // mask their key counts add up to the same total for every pair, so all
+  // workgroups carry equal work and none is left running alone at the end.
+  // The tile with more keys goes first.
+  const int n_mine = (n_qt - 1 - pr != pr) ? 2 : 1;
+#pragma nounroll
+  for (int it = 0; it < n_mine; ++it) {
+  const int qt = it == 0 ? n_qt - 1 - pr : pr;
+  if (it > 0) __syncthreads();   // every wave is done reading the previous tile's stages
   const int q0 = qt * kBM;
 
   int kv = N_k;
@@ -444,6 +454,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     if (LSE && lane < 32)
       LSE[(size_t)bh * N_q + my_row] = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   }
+  }   // tiles of the pair
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -464,7 +475,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   if (!q || !o) return ATTN_ERR_NULL;
   if (N_k > 0 && (!k || !v)) return ATTN_ERR_NULL;
   const long long n_qt = (N_q + kBM - 1) / kBM;
-  const long long n_wg = (long long)B * H * n_qt;
+  const long long n_wg = (long long)B * H * ((n_qt + 1) / 2);   // one workgroup per pair of query tiles
   if (n_wg > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   if ((long long)B * H > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   const size_t q_bytes = (size_t)B * H * N_q * d * 2;
