@@ -76,7 +76,8 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr int kBN = 64;        // keys per K/V tile
-constexpr int kWaves = 4;      // wave64s per workgroup, 32 query rows each
+constexpr int kWaves = 8;      // wave64s per workgroup (two per SIMD), 32 query rows each
+constexpr int kStages = 4;     // LDS ring depth for K and V tiles: three tiles of copy lookahead
 constexpr int kBM = 32 * kWaves;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 units
@@ -86,13 +87,13 @@ template <int D>
 struct Tile {
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kBytes = kBN * kRowBytes;            // one K or V stage
-  static constexpr int kLds = 4 * kBytes;                   // K0, K1, V0, V1
+  static constexpr int kLds = 2 * kStages * kBytes;         // K stages, then V stages
   static constexpr int kCopies = kBytes / 1024;             // 1 KB wave copies per stage
   static constexpr int kCopiesPerWave = kCopies / kWaves;
   static constexpr int kRowsPerCopy = 1024 / kRowBytes;
   static constexpr int kLanesPerRow = 64 / kRowsPerCopy;
   static_assert(kCopies % kWaves == 0, "copies must split evenly over the waves");
-  static_assert(2 * kLds <= 160 * 1024, "two workgroups must fit the 160 KB LDS of a CU");
+  static_assert(kLds <= 160 * 1024, "the stages must fit the 160 KB LDS of a CU");
 };
 
 // Chunk position of 16-byte chunk c of row r is c ^ swz(r). For D = 128 a row
@@ -125,10 +126,16 @@ __device__ __forceinline__ float lane_swap_add(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's copies are still in flight (copies
+// complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int H, int N_q, int N_k, float c, int neg_scale,
     int causal, const int32_t* __restrict__ seqlens_k, const int32_t* __restrict__ q_start, int n_qt,
@@ -238,8 +245,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                    : "memory", "m0");
     }
   };
-  char* const kst[2] = {smem, smem + T::kBytes};
-  char* const vst[2] = {smem + 2 * T::kBytes, smem + 3 * T::kBytes};
+  auto kst = [&](int st) __attribute__((always_inline)) { return smem + st * T::kBytes; };
+  auto vst = [&](int st) __attribute__((always_inline)) { return smem + (kStages + st) * T::kBytes; };
 
   // ---- per-lane LDS offsets of the MFMA operand reads ----
   // K (A operand of S^T = K Q^T): lane L reads row L%32 of a 32-key half
@@ -399,39 +406,52 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   // K tile t holds keys 64t .. 64t+63; V tile t holds keys 64t-32 .. 64t+31,
   // half a tile earlier, so that step t (half steps 2t+1 and 2t+2, which read
   // K halves 2t+2, 2t+3 and V halves 2t+1, 2t+2) reads exactly K tile t+1 and
-  // V tile t+1, from stage (t+1) % 2, while tiles t+2 are copied into the
-  // other stage. Half step 0 runs before the loop from K tile 0 and V tile 0.
-  const int n_kt = (nh_wg + 1) / 2;   // K tiles needed
-  const int n_vt = nh_wg / 2 + 1;     // V tiles needed (when nh_wg > 0)
+  // V tile t+1. Tiles live in stage t % kStages. Step t waits for tiles t+1
+  // (tiles t+2, t+3 may still be in flight), then, behind the barrier that
+  // also retires step t-1's reads of stage t % kStages, copies tiles t+4 into
+  // it. Copies are issued for every step, also past the last tile (those
+  // lanes re-read the clamped last valid row), so that the number in flight,
+  // and with it every wait count, is the same in every step. Half step 0 runs
+  // before the loop from tiles 0.
+  constexpr int kC = 2 * T::kCopiesPerWave;   // copies per wave per K+V tile pair
   constexpr int kHalf = 32 * T::kRowBytes;
+  auto copy_tiles = [&](int t) __attribute__((always_inline)) {
+    const int st = t % kStages;
+    copy_tile(kg, t * kBN, kst(st));
+    copy_tile(vg, t * kBN - 32, vst(st));
+  };
   f32x16 sa, sb;
   if (nh_wg > 0) {
-    copy_tile(kg, 0, kst[0]);
-    if (n_kt > 1) copy_tile(kg, kBN, kst[1]);
-    copy_tile(vg, -32, vst[0]);
-    if (n_vt > 1) copy_tile(vg, kBN - 32, vst[1]);
-    wait_copies();
+#pragma unroll
+    for (int t = 0; t < kStages; ++t) copy_tiles(t);
+    wait_copies<(kStages - 1) * kC>();
     __syncthreads();
     if (nh > 0) {
-      qk(kst[0], sa);
+      qk(kst(0), sa);
       if (need_mask(0)) mask(0, sa);
       rowmax_shift(sa, true);
     }
-    half_step(0, kst[0] + kHalf, vst[0] + kHalf, sa, sb);
+    half_step(0, kst(0) + kHalf, vst(0) + kHalf, sa, sb);
   }
   auto step = [&](auto stage, int t) __attribute__((always_inline)) {
-    constexpr int S = decltype(stage)::value;   // == (t + 1) % 2
-    wait_copies();
-    __syncthreads();   // tiles t+1 have landed; the stage of tiles t is free
-    if (t + 2 < n_kt) copy_tile(kg, (t + 2) * kBN, kst[S ^ 1]);
-    if (t + 2 < n_vt) copy_tile(vg, (t + 2) * kBN - 32, vst[S ^ 1]);
-    half_step(2 * t + 1, kst[S], vst[S], sb, sa);
-    half_step(2 * t + 2, kst[S] + kHalf, vst[S] + kHalf, sa, sb);
+    constexpr int S = decltype(stage)::value;   // == (t + 1) % kStages
+    wait_copies<(kStages - 2) * kC>();
+    __syncthreads();   // tiles t+1 have landed; stage t % kStages is no longer read
+    copy_tiles(t + kStages);
+    half_step(2 * t + 1, kst(S), vst(S), sb, sa);
+    half_step(2 * t + 2, kst(S) + kHalf, vst(S) + kHalf, sa, sb);
   };
-  for (int t = 0; 2 * t + 1 < nh_wg; t += 2) {
+  static_assert(kStages == 4, "the step loop below is unrolled for four stages");
+  for (int t = 0; 2 * t + 1 < nh_wg; t += 4) {
     step(std::integral_constant<int, 1>{}, t);
-    if (2 * t + 3 < nh_wg) step(std::integral_constant<int, 0>{}, t + 1);
+    if (2 * t + 3 >= nh_wg) break;
+    step(std::integral_constant<int, 2>{}, t + 1);
+    if (2 * t + 5 >= nh_wg) break;
+    step(std::integral_constant<int, 3>{}, t + 2);
+    if (2 * t + 7 >= nh_wg) break;
+    step(std::integral_constant<int, 0>{}, t + 3);
   }
+  wait_copies<0>();   // no copy may still be writing LDS when the next tile (or wave) starts
   if (o_stale) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o_acc[db] *= alpha;
