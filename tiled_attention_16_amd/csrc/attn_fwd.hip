@@ -146,19 +146,98 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  const int grp = wave >> 2;   // waves w and w+4 share a SIMD: one of each group
   const int hf = lane >> 5;
 
-  // ---- work decomposition: blockIdx -> (batch*head, query tile) ----
+  // ---- work decomposition: blockIdx -> (batch*head, pair of query tiles) ----
   // Consecutive workgroup ids are dealt round-robin over the 8 XCDs; regroup so
   // that each XCD gets a contiguous range of (head, tile) pairs and the K/V of a
-  // head stay in one XCD's L2. Within a head, the tile with the most keys
-  // (the last one, under a causal mask) starts first.
+  // head stay in one XCD's L2.
   int lin = blockIdx.x;
   if ((n_wg & 7) == 0) lin = (lin & 7) * (n_wg >> 3) + (lin >> 3);
   const int n_pairs = (n_qt + 1) / 2;
   const int bh = lin / n_pairs;
   const int pr = lin - bh * n_pairs;
   const int b = bh / H;
+  const char* kg = (const char*)(K + (size_t)bh * N_k * D);
+  const char* vg = (const char*)(V + (size_t)bh * N_k * D);
+
+  int kv = N_k;
+  if (seqlens_k) kv = min(max(seqlens_k[b], 0), N_k);
+  int qs = 0;
+  if (q_start) qs = min(max(q_start[b], 0), N_q);
+
+  // ---- K/V tile copies: global -> LDS, 1 KB per wave instruction ----
+  // Copy q of this wave fills LDS bytes [1024*qi, 1024*qi + 1024) of a stage,
+  // qi = wave * kCopiesPerWave + q: lane L lands at byte 16*L, which is row
+  // qi*kRowsPerCopy + L / kLanesPerRow, chunk position L % kLanesPerRow, so it
+  // fetches logical chunk (position ^ swz(row)) of that row.
+  auto cp_row = [&](int q) __attribute__((always_inline)) {
+    return (wave * T::kCopiesPerWave + q) * T::kRowsPerCopy + lane / T::kLanesPerRow;
+  };
+  int cp_off[T::kCopiesPerWave];
+#pragma unroll
+  for (int q = 0; q < T::kCopiesPerWave; ++q) {
+    const int r = cp_row(q);
+    cp_off[q] = r * T::kRowBytes + (((lane % T::kLanesPerRow) ^ swz<D>(r)) << 4);
+  }
+  // Copy the 64 rows starting at key k0 of a head's K or V into stage dst.
+  // Rows outside [0, kv) are never read: those lanes fetch a clamped row whose
+  // data the mask ignores (or that is multiplied by a zero probability).
+  auto copy_tile = [&](const char* src, int k0, const char* dst) __attribute__((always_inline)) {
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)dst +
+                          wave * T::kCopiesPerWave * 1024;
+    const bool ragged = k0 < 0 || k0 + kBN > kv;
+    const char* base = ragged ? src : src + (ptrdiff_t)k0 * T::kRowBytes;
+    // (readfirstlane returns a signed int: widen through uint32_t so the low
+    // half is zero-extended, never sign-extended into the high half)
+    const uint32_t base_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
+    const uint32_t base_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uintptr_t)base >> 32));
+    const uint64_t sbase = ((uint64_t)base_hi << 32) | (uint64_t)base_lo;
+#pragma unroll
+    for (int q = 0; q < T::kCopiesPerWave; ++q) {
+      uint32_t voff = (uint32_t)cp_off[q];
+      if (ragged) {
+        const int key = min(max(k0 + cp_row(q), 0), kv - 1);
+        voff += (uint32_t)((key - cp_row(q)) * T::kRowBytes);
+      }
+      // The copy is issued as inline assembly so that the compiler does not
+      // treat it as a pending write to every LDS address (it would then wait
+      // for it before each LDS read); completion is awaited explicitly with
+      // wait_copies() before the barrier that publishes the tile.
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(__builtin_amdgcn_readfirstlane(lds0 + q * 1024)), "v"(voff), "s"(sbase)
+                   : "memory", "m0");
+    }
+  };
+  // Stage st: K rows at kst(st), V rows at vst(st).
+  auto kst = [&](int st) __attribute__((always_inline)) { return (const char*)smem + st * T::kBytes; };
+  auto vst = [&](int st) __attribute__((always_inline)) { return (const char*)smem + (kStages + st) * T::kBytes; };
+
+  // ---- per-lane LDS offsets of the MFMA operand reads ----
+  // K (A operand of S^T = K Q^T): lane L reads row L%32 of a 32-key half
+  // tile, logical chunk 2*kc + L/32, at byte r*kRowBytes + ((2kc + L/32) ^
+  // swz(r))*16. The swizzle only flips chunk bits, so the offset for chunk
+  // pair kc is k_off0 ^ (32*kc).
+  // V (A operand of O^T += V^T P^T, via the transposing read): 16-key chunk cc,
+  // half hi: lane L of group g = L/16 supplies row 16*cc + 8*hi + 4*(L/32) +
+  // (L%16)/4, columns 32*db + 16*(g%2) + 4*(L%4) .. +3. After the transpose,
+  // lane L holds column 32*db + L%32 of keys 16*cc + 8*hi + 4*(L/32) + 0..3,
+  // which pairs with P's registers 8*(cc%2) + 4*hi + 0..3 of the half tile.
+  // Its offset is v_off0 ^ (hi*(8*kRowBytes + 16)) ^ (64*db) (row +8 flips
+  // swizzle bit 0), plus 16*cc rows as an immediate.
+  // Every base these are added to is a multiple of 16 rows, so base + (off ^ x)
+  // == (base + off) ^ x and the bases stay immediate offsets.
+  int k_off0, v_off0;
+  {
+    const int r = lane & 31;
+    k_off0 = r * T::kRowBytes + ((hf ^ swz<D>(r)) << 4);
+    const int g = lane >> 4;
+    const int rv = 4 * hf + ((lane & 15) >> 2);
+    const int byte = 32 * (g & 1) + 8 * (lane & 3);
+    v_off0 = rv * T::kRowBytes + (((byte >> 4) ^ swz<D>(rv)) << 4) + (byte & 15);
+  }
+
   // A workgroup owns the pair of query tiles (n_qt-1-pr, pr): under a causal
   // mask their key counts add up to the same total for every pair, so all
   // workgroups carry equal work and none is left running alone at the end.
@@ -167,30 +246,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
 #pragma nounroll
   for (int it = 0; it < n_mine; ++it) {
   const int qt = it == 0 ? n_qt - 1 - pr : pr;
-  if (it > 0) __syncthreads();   // every wave is done reading the previous tile's stages
   const int q0 = qt * kBM;
-
-  int kv = N_k;
-  if (seqlens_k) kv = min(max(seqlens_k[b], 0), N_k);
-  int qs = 0;
-  if (q_start) qs = min(max(q_start[b], 0), N_q);
-
   const int q_end = min(q0 + kBM, N_q);
   int kv_end = kv;                                 // keys this workgroup can see
   if (causal) kv_end = min(kv_end, q_end);
   if (qs >= q_end) kv_end = 0;                     // every row of the tile is masked
-  const int n_tiles = (kv_end + kBN - 1) / kBN;
 
   const int row_lo = q0 + 32 * wave;               // this wave's rows: row_lo .. row_lo + 31
   const int row_hi = min(row_lo + 31, N_q - 1);
   const bool wave_live = row_lo < N_q && row_hi >= qs;
   const int my_row = row_lo + (lane & 31);
-
   const size_t q_base = (size_t)bh * N_q * D;
-  const char* kg = (const char*)(K + (size_t)bh * N_k * D);
-  const char* vg = (const char*)(V + (size_t)bh * N_k * D);
 
-  // ---- Q tile -> VGPRs as the B operand of S^T = K Q^T ----
+  // 32-key half tiles h (keys 32h .. 32h+31): nh_wg for the workgroup, nh (a
+  // prefix) for this wave.
+  const int nh_wg = (kv_end + 31) / 32;
+  int nh = wave_live ? nh_wg : 0;
+  if (causal) nh = min(nh, row_hi / 32 + 1);
+
+  // ---- Q rows -> VGPRs as the B operand of S^T = K Q^T ----
   bf16x8 qreg[D / 16];
   {
     const uint32_t flip = neg_scale ? 0x80008000u : 0u;   // negative scale: negate Q exactly
@@ -203,99 +277,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     }
   }
 
-  // ---- K/V tile copies: global -> LDS, 1 KB per wave instruction ----
-  // Copy q of this wave fills LDS bytes [1024*qi, 1024*qi + 1024) of a stage,
-  // qi = wave * kCopiesPerWave + q: lane L lands at byte 16*L, which is row
-  // qi*kRowsPerCopy + L / kLanesPerRow, chunk position L % kLanesPerRow, so it
-  // fetches logical chunk (position ^ swz(row)) of that row.
-  int cp_row[T::kCopiesPerWave], cp_off[T::kCopiesPerWave];
-#pragma unroll
-  for (int q = 0; q < T::kCopiesPerWave; ++q) {
-    const int qi = wave * T::kCopiesPerWave + q;
-    const int r = qi * T::kRowsPerCopy + lane / T::kLanesPerRow;
-    cp_row[q] = r;
-    cp_off[q] = r * T::kRowBytes + (((lane % T::kLanesPerRow) ^ swz<D>(r)) << 4);
-  }
-  // Copy the 64 rows starting at key k0 of a head's K or V into stage dst.
-  // Rows outside [0, kv) are never read: those lanes fetch a clamped row whose
-  // data the mask ignores.
-  auto copy_tile = [&](const char* src, int k0, char* dst) __attribute__((always_inline)) {
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst +
-                          wave * T::kCopiesPerWave * 1024;
-    const bool ragged = k0 < 0 || k0 + kBN > kv;
-    const char* base = ragged ? src : src + (ptrdiff_t)k0 * T::kRowBytes;
-#pragma unroll
-    for (int q = 0; q < T::kCopiesPerWave; ++q) {
-      uint32_t voff = (uint32_t)cp_off[q];
-      if (ragged) {
-        const int key = min(max(k0 + cp_row[q], 0), kv - 1);
-        voff += (uint32_t)((key - cp_row[q]) * T::kRowBytes);
-      }
-      // The copy is issued as inline assembly so that the compiler does not
-      // treat it as a pending write to every LDS address (it would then wait
-      // for it before each LDS read); completion is awaited explicitly with
-      // wait_copies() before the barrier that publishes the tile.
-      // (readfirstlane returns a signed int: widen through uint32_t so the low
-      // half is zero-extended, never sign-extended into the high half)
-      const uint32_t base_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
-      const uint32_t base_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uintptr_t)base >> 32));
-      const uint64_t sbase = ((uint64_t)base_hi << 32) | (uint64_t)base_lo;
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                   :: "s"(__builtin_amdgcn_readfirstlane(lds0 + q * 1024)), "v"(voff), "s"(sbase)
-                   : "memory", "m0");
-    }
-  };
-  auto kst = [&](int st) __attribute__((always_inline)) { return smem + st * T::kBytes; };
-  auto vst = [&](int st) __attribute__((always_inline)) { return smem + (kStages + st) * T::kBytes; };
-
-  // ---- per-lane LDS offsets of the MFMA operand reads ----
-  // K (A operand of S^T = K Q^T): lane L reads row L%32 of a 32-key half
-  // tile, logical chunk 2*kc + L/32.
-  int k_off[D / 16];
-  {
-    const int r = lane & 31;
-#pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) k_off[kc] = r * T::kRowBytes + (((2 * kc + hf) ^ swz<D>(r)) << 4);
-  }
-  // V (A operand of O^T += V^T P^T, via the transposing read): 16-key chunk cc,
-  // half hi: lane L of group g = L/16 supplies row 16*cc + 8*hi + 4*(L/32) +
-  // (L%16)/4, columns 32*db + 16*(g%2) + 4*(L%4) .. +3. After the transpose,
-  // lane L holds column 32*db + L%32 of keys 16*cc + 8*hi + 4*(L/32) + 0..3,
-  // which pairs with P's registers 8*(cc%2) + 4*hi + 0..3 of the half tile.
-  int v_off[2][D / 32];
-  {
-    const int g = lane >> 4;
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi) {
-      const int r = 8 * hi + 4 * hf + ((lane & 15) >> 2);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int byte = 64 * db + 32 * (g & 1) + 8 * (lane & 3);
-        v_off[hi][db] = r * T::kRowBytes + (((byte >> 4) ^ swz<D>(r)) << 4) + (byte & 15);
-      }
-    }
-  }
-
   f32x16 o_acc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o_acc[db] = (f32x16){};
   float m_run = -INFINITY;   // running max of S*c for this lane's row (same in lane ^ 32)
-  float msub = 0.f;          // subtrahend of the exponent: m_run, or 0 while m_run = -inf
   float l_run = 0.f;         // partial running sum over this lane's half of the keys
-  float alpha = 1.f;         // pending rescale of o_acc
-  bool o_stale = false;      // some lane of the wave has alpha != 1 pending
+  f32x16 s = {};             // S^T of the current half tile (one query row per lane)
+  bf16x8 pb[2] = {};         // P of the previous half tile, the B operand of P V
 
-  // The pipeline runs over 32-key half tiles h (keys 32h .. 32h+31).
-  // S^T of a half tile = K_h Q^T: one 32x32 block, 32 keys x 32 rows; kb
-  // points at the half tile's first K row in LDS.
-  auto qk = [&](const char* kb, f32x16& s) __attribute__((always_inline)) {
-    s = (f32x16){};
-#pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) {
-      const u32x4 a = *(const lds_u32x4*)(kb + k_off[kc]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qreg[kc], s, 0, 0, 0);
-    }
-  };
   // Key j is allowed for this lane's row iff j <= klim (klim folds the valid
   // length, the causal limit and the masked leading rows into one bound).
   const int klim = my_row < qs ? -1 : min(kv - 1, causal ? my_row : 0x7fffffff);
@@ -304,157 +293,169 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const int k0 = h * 32;
     return (k0 + 31 >= kv) || (causal && k0 + 31 > row_lo) || (row_lo < qs);
   };
-  auto mask = [&](int h, f32x16& s) __attribute__((always_inline)) {
-    const int lim = klim - h * 32 - 4 * hf;   // key offset within the half tile must be <= lim
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3)) <= lim ? s[r] : -INFINITY;
+
+  // K tile t holds keys 64t .. 64t+63 (K halves 2t, 2t+1); V tile t holds keys
+  // 64t-32 .. 64t+31 (V halves 2t-1, 2t). Both live in stage t % kStages.
+  // K half h: stage (h/2) % kStages, row 32*(h%2); V half h: stage
+  // ((h+1)/2) % kStages, row 32*(1 - h%2). Callers pass h modulo 2*kStages as
+  // a compile-time constant, so every LDS address is a per-lane offset plus an
+  // immediate.
+  auto k_half = [&](auto hm) __attribute__((always_inline)) {
+    constexpr int h = decltype(hm)::value;
+    return kst((h >> 1) % kStages) + (h & 1) * 32 * T::kRowBytes;
   };
-  // row max, running-max update, and S <- S*c - m (in place)
-  auto rowmax_shift = [&](f32x16& s, bool live) __attribute__((always_inline)) {
+  auto v_half = [&](auto hm) __attribute__((always_inline)) {
+    constexpr int h = decltype(hm)::value;
+    return vst(((h + 1) >> 1) % kStages) + (~h & 1) * 32 * T::kRowBytes;
+  };
+
+  // Cluster C_h (MFMA): S of half h (into s) and O += P V of half h-1 (P from
+  // the previous softmax cluster; zero before the first). All 24 operand reads
+  // are issued first; the QK MFMAs hide the transposing V reads' latency.
+  auto cluster_c = [&](auto hm) __attribute__((always_inline)) {
+    constexpr int h = decltype(hm)::value;   // half index modulo 2*kStages
+    const char* kb = k_half(std::integral_constant<int, h>{});
+    const char* vb = v_half(std::integral_constant<int, (h + 2 * kStages - 1) % (2 * kStages)>{});
+    // (re-derive the offsets here instead of keeping 16 of them live)
+    int ko = k_off0, vo = v_off0;
+    asm volatile("" : "+v"(ko), "+v"(vo));
+    u32x4 ka[D / 16];
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) ka[kc] = *(const lds_u32x4*)(kb + (ko ^ (32 * kc)));
+    bf16x8 va[2][D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int off_lo = vo ^ (64 * db);
+      const int off_hi = off_lo ^ (8 * T::kRowBytes + 16);
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const char* p0 = vb + 16 * cc * T::kRowBytes;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + off_lo));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + off_hi));
+        va[cc][db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    }
+    s = (f32x16){};
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[kc]), qreg[kc], s, 0, 0, 0);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cc][db], pb[cc], o_acc[db], 0, 0, 0);
+    // order: the K reads, then all V reads, then the QK MFMAs, then the PV MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);      // DS read: K
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * D / 16, 0);  // DS read: V
+    __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);      // MFMA: QK
+    __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);      // MFMA: PV
+  };
+
+  // Cluster S_h (VALU): the online softmax of half h on s.
+  auto cluster_s = [&](int h) __attribute__((always_inline)) {
+    if (need_mask(h)) {
+      const int lim = klim - h * 32 - 4 * hf;   // key offset within the half tile must be <= lim
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3)) <= lim ? s[r] : -INFINITY;
+    }
     const float a0 = fmaxf(fmaxf(s[0], s[1]), s[2]), a1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
     const float a2 = fmaxf(fmaxf(s[6], s[7]), s[8]), a3 = fmaxf(fmaxf(s[9], s[10]), s[11]);
     const float a4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
     const float mx = lane_swap_max(fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), s[15])));
-    const float tmax = live ? mx * c : -INFINITY;   // c > 0, so -inf stays -inf
+    const float tmax = mx * c;   // c > 0, so -inf stays -inf
     const bool grow = tmax > m_run + kTau;
-    const float m_new = grow ? tmax : m_run;
-    const float a = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // m_run = -inf gives 0
-    l_run *= a;
-    alpha *= a;
-    m_run = m_new;
-    msub = (m_run == -INFINITY) ? 0.f : m_run;
-    o_stale = o_stale || __builtin_amdgcn_ballot_w64(grow) != 0;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      // raise the subtrahend; rescale l and O (O holds P V up to half h-1)
+      const float m_new = grow ? tmax : m_run;
+      const float a = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // m_run = -inf gives 0
+      m_run = m_new;
+      l_run *= a;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], c, -msub);
-  };
-  // P = exp2(S*c - m): fp32 into the row sum, bf16 into the PV operand
-  auto expo = [&](const f32x16& s, bf16x8 (&pb)[2]) __attribute__((always_inline)) {
+      for (int db = 0; db < D / 32; ++db) o_acc[db] *= a;
+    }
+    const float msub = (m_run == -INFINITY) ? 0.f : m_run;
     float p[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(s[r]);
+    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -msub));
     l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])) +
              (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const u32x4 w = {pack2(p[8 * h + 0], p[8 * h + 1]), pack2(p[8 * h + 2], p[8 * h + 3]),
-                       pack2(p[8 * h + 4], p[8 * h + 5]), pack2(p[8 * h + 6], p[8 * h + 7])};
-      pb[h] = as_bf16x8(w);
-    }
-  };
-  // O^T += V^T P^T for a half tile whose first V row is at vb: 16-key chunk cc
-  // pairs with P registers 8*cc..
-  auto pv = [&](const char* vb, const bf16x8 (&pb)[2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const char* p0 = vb + 16 * cc * T::kRowBytes;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + v_off[0][db]));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + v_off[1][db]));
-        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc], o_acc[db], 0, 0, 0);
-      }
+    for (int u = 0; u < 2; ++u) {
+      const u32x4 w = {pack2(p[8 * u + 0], p[8 * u + 1]), pack2(p[8 * u + 2], p[8 * u + 3]),
+                       pack2(p[8 * u + 4], p[8 * u + 5]), pack2(p[8 * u + 6], p[8 * u + 7])};
+      pb[u] = as_bf16x8(w);
     }
   };
 
-  // Half tiles: nh_wg for the workgroup, nh (a prefix) for this wave.
-  const int nh_wg = (kv_end + 31) / 32;
-  int nh = wave_live ? nh_wg : 0;
-  if (causal) nh = min(nh, row_hi / 32 + 1);
-
-  // One pipelined half step h: S of half h is in sc (already shifted); S of
-  // half h+1 goes to sn. kb: K rows of half h+1; vb: V rows of half h.
-  // Phase A: S of h+1 on the MFMA unit while the VALU exponentiates h.
-  // Phase B: O += P V of h on the MFMA unit while the VALU takes the row max
-  // of h+1 and forms S*c - m.
-  auto half_step = [&](int h, const char* kb, const char* vb, f32x16& sc, f32x16& sn) __attribute__((always_inline)) {
-    if (h >= nh) return;
-    if (o_stale) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) o_acc[db] *= alpha;
-      alpha = 1.f;
-      o_stale = false;
-    }
-    // Half h+1 may lie past this wave's last half (then its S is computed from
-    // whatever the stage holds and discarded: no branch splits the phase).
-    const bool nxt = h + 1 < nh;
-    bf16x8 pb[2];
-    qk(kb, sn);
-    expo(sc, pb);
-    // keep P and l in this block (the compiler would otherwise sink them
-    // past the mask branch, away from the MFMAs they are meant to overlap)
-    asm volatile("" :: "v"(pb[0]), "v"(pb[1]), "v"(l_run));
-    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // DS read
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 40 / (D / 16), 0);   // VALU
-    }
-    if (nxt && need_mask(h + 1)) mask(h + 1, sn);
-    pv(vb, pb);
-    rowmax_shift(sn, nxt);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-      __builtin_amdgcn_sched_group_barrier(0x002, 32 / (D / 16), 1);
-    }
-  };
-
-  // K tile t holds keys 64t .. 64t+63; V tile t holds keys 64t-32 .. 64t+31,
-  // half a tile earlier, so that step t (half steps 2t+1 and 2t+2, which read
-  // K halves 2t+2, 2t+3 and V halves 2t+1, 2t+2) reads exactly K tile t+1 and
-  // V tile t+1. Tiles live in stage t % kStages. Step t waits for tiles t+1
-  // (tiles t+2, t+3 may still be in flight), then, behind the barrier that
-  // also retires step t-1's reads of stage t % kStages, copies tiles t+4 into
-  // it. Copies are issued for every step, also past the last tile (those
-  // lanes re-read the clamped last valid row), so that the number in flight,
-  // and with it every wait count, is the same in every step. Half step 0 runs
-  // before the loop from tiles 0.
-  constexpr int kC = 2 * T::kCopiesPerWave;   // copies per wave per K+V tile pair
-  constexpr int kHalf = 32 * T::kRowBytes;
+  // Ping-pong: every SIMD holds one wave of each group. In iteration j group 0
+  // runs C_j then S_j, group 1 runs S_{j-1} then C_j, with a workgroup barrier
+  // between the halves, so one wave of each SIMD feeds the MFMA unit while the
+  // other works on the VALU. Tile t is read by the C clusters of iterations
+  // 2t and 2t+1; at the start of iteration 2t the workgroup waits for tile t,
+  // and once every wave has passed that barrier (all reads of tile t-1 are
+  // done) it copies tile t+3 into tile t-1's stage. Copies are issued for
+  // every tile step, also past the last tile (clamped rows), so that the
+  // number in flight, and with it every wait count, is the same each time.
+  constexpr int kC = 2 * T::kCopiesPerWave;   // copies per wave per K+V tile
   auto copy_tiles = [&](int t) __attribute__((always_inline)) {
-    const int st = t % kStages;
+    const int st = t & (kStages - 1);
     copy_tile(kg, t * kBN, kst(st));
     copy_tile(vg, t * kBN - 32, vst(st));
   };
-  f32x16 sa, sb;
-  if (nh_wg > 0) {
-#pragma unroll
-    for (int t = 0; t < kStages; ++t) copy_tiles(t);
-    wait_copies<(kStages - 1) * kC>();
-    __syncthreads();
-    if (nh > 0) {
-      qk(kst(0), sa);
-      if (need_mask(0)) mask(0, sa);
-      rowmax_shift(sa, true);
-    }
-    half_step(0, kst(0) + kHalf, vst(0) + kHalf, sa, sb);
-  }
-  auto step = [&](auto stage, int t) __attribute__((always_inline)) {
-    constexpr int S = decltype(stage)::value;   // == (t + 1) % kStages
-    wait_copies<(kStages - 2) * kC>();
-    __syncthreads();   // tiles t+1 have landed; stage t % kStages is no longer read
-    copy_tiles(t + kStages);
-    half_step(2 * t + 1, kst(S), vst(S), sb, sa);
-    half_step(2 * t + 2, kst(S) + kHalf, vst(S) + kHalf, sa, sb);
+  auto slot_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
-  static_assert(kStages == 4, "the step loop below is unrolled for four stages");
-  for (int t = 0; 2 * t + 1 < nh_wg; t += 4) {
-    step(std::integral_constant<int, 1>{}, t);
-    if (2 * t + 3 >= nh_wg) break;
-    step(std::integral_constant<int, 2>{}, t + 1);
-    if (2 * t + 5 >= nh_wg) break;
-    step(std::integral_constant<int, 3>{}, t + 2);
-    if (2 * t + 7 >= nh_wg) break;
-    step(std::integral_constant<int, 0>{}, t + 3);
-  }
-  wait_copies<0>();   // no copy may still be writing LDS when the next tile (or wave) starts
-  if (o_stale) {
+  if (nh_wg > 0) {
+    if (it > 0) __syncthreads();   // every wave is done reading the previous tile's stages
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) o_acc[db] *= alpha;
+    for (int t = 0; t < kStages - 1; ++t) copy_tiles(t);
+    // One loop per group (the group decides the order of the clusters); both
+    // pass the same barriers in the same order.
+    auto run = [&](auto gm) __attribute__((always_inline)) {
+      constexpr int G = decltype(gm)::value;
+      auto iter = [&](auto jm, int j) __attribute__((always_inline)) {
+        constexpr int J = decltype(jm)::value;   // j % (2 * kStages)
+        if constexpr ((J & 1) == 0) {
+          wait_copies<(kStages - 2) * kC>();
+          __syncthreads();   // tile j/2 has landed; stage of tile j/2 - 1 is no longer read
+          copy_tiles(j / 2 + kStages - 1);
+        } else {
+          slot_barrier();
+        }
+        if constexpr (G == 0) {
+          if (j <= nh) cluster_c(jm);
+          slot_barrier();
+          if (j < nh) cluster_s(j);
+        } else {
+          if (j >= 1 && j - 1 < nh) cluster_s(j - 1);
+          slot_barrier();
+          if (j <= nh) cluster_c(jm);
+        }
+      };
+      static_assert(kStages == 4, "the loop below is unrolled over 2 * kStages half tiles");
+      for (int j0 = 0; j0 <= nh_wg; j0 += 8) {
+        iter(std::integral_constant<int, 0>{}, j0);
+        if (j0 + 1 > nh_wg) break;
+        iter(std::integral_constant<int, 1>{}, j0 + 1);
+        if (j0 + 2 > nh_wg) break;
+        iter(std::integral_constant<int, 2>{}, j0 + 2);
+        if (j0 + 3 > nh_wg) break;
+        iter(std::integral_constant<int, 3>{}, j0 + 3);
+        if (j0 + 4 > nh_wg) break;
+        iter(std::integral_constant<int, 4>{}, j0 + 4);
+        if (j0 + 5 > nh_wg) break;
+        iter(std::integral_constant<int, 5>{}, j0 + 5);
+        if (j0 + 6 > nh_wg) break;
+        iter(std::integral_constant<int, 6>{}, j0 + 6);
+        if (j0 + 7 > nh_wg) break;
+        iter(std::integral_constant<int, 7>{}, j0 + 7);
+      }
+    };
+    if (grp == 0) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{});
+    wait_copies<0>();   // no copy may still be writing LDS when the next tile (or wave) starts
   }
 
   // ---- epilogue: O / l, LSE, bf16 store ----
