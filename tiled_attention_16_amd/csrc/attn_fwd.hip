@@ -309,20 +309,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     return vst(((h + 1) >> 1) % kStages) + (~h & 1) * 32 * T::kRowBytes;
   };
 
-  // Cluster C_h (MFMA): S of half h (into s) and O += P V of half h-1 (P from
-  // the previous softmax cluster; zero before the first). All 24 operand reads
-  // are issued first; the QK MFMAs hide the transposing V reads' latency.
-  auto cluster_c = [&](auto hm) __attribute__((always_inline)) {
+  // Operands of cluster C_h: K of half h (A operand of S^T = K Q^T) and V of
+  // half h-1 (A operand of O^T += V^T P^T). They are read from LDS one cluster
+  // ahead, during the softmax cluster of the same wave, so the MFMA cluster
+  // itself never waits on LDS and the reads of one group overlap the other
+  // group's MFMAs.
+  u32x4 ka[D / 16];
+  bf16x8 va[2][D / 32];
+  auto load_ops = [&](auto hm) __attribute__((always_inline)) {
     constexpr int h = decltype(hm)::value;   // half index modulo 2*kStages
     const char* kb = k_half(std::integral_constant<int, h>{});
     const char* vb = v_half(std::integral_constant<int, (h + 2 * kStages - 1) % (2 * kStages)>{});
     // (re-derive the offsets here instead of keeping 16 of them live)
     int ko = k_off0, vo = v_off0;
     asm volatile("" : "+v"(ko), "+v"(vo));
-    u32x4 ka[D / 16];
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) ka[kc] = *(const lds_u32x4*)(kb + (ko ^ (32 * kc)));
-    bf16x8 va[2][D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int off_lo = vo ^ (64 * db);
@@ -335,6 +337,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
         va[cc][db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     }
+  };
+  // Cluster C_h (MFMA): S of half h (into s) and O += P V of half h-1 (P from
+  // the previous softmax cluster; zero before the first).
+  auto cluster_c = [&]() __attribute__((always_inline)) {
     s = (f32x16){};
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc)
@@ -344,11 +350,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
         o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cc][db], pb[cc], o_acc[db], 0, 0, 0);
-    // order: the K reads, then all V reads, then the QK MFMAs, then the PV MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);      // DS read: K
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * D / 16, 0);  // DS read: V
-    __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);      // MFMA: QK
-    __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);      // MFMA: PV
   };
 
   // Cluster S_h (VALU): the online softmax of half h on s.
@@ -389,13 +390,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
 
   // Ping-pong: every SIMD holds one wave of each group. In iteration j group 0
   // runs C_j then S_j, group 1 runs S_{j-1} then C_j, with a workgroup barrier
-  // between the halves, so one wave of each SIMD feeds the MFMA unit while the
-  // other works on the VALU. Tile t is read by the C clusters of iterations
-  // 2t and 2t+1; at the start of iteration 2t the workgroup waits for tile t,
-  // and once every wave has passed that barrier (all reads of tile t-1 are
-  // done) it copies tile t+3 into tile t-1's stage. Copies are issued for
-  // every tile step, also past the last tile (clamped rows), so that the
-  // number in flight, and with it every wait count, is the same each time.
+  // between the halves ("slots" 2j and 2j+1), so one wave of each SIMD feeds
+  // the MFMA unit while the other works on the VALU and reads the operands of
+  // its next MFMA cluster from LDS. Tile t (K halves 2t, 2t+1; V halves 2t-1,
+  // 2t) is read in slots 4t-1 .. 4t+2, so the workgroup waits for tile t at the
+  // barrier before slot 4t-1 and, once every wave has passed that barrier
+  // (the last reads of tile t-1 were in slot 4t-2), copies tile t+3 into tile
+  // t-1's stage. Copies are issued for every tile step, also past the last
+  // tile (clamped rows), so that the number in flight, and with it every wait
+  // count, is the same each time.
   constexpr int kC = 2 * T::kCopiesPerWave;   // copies per wave per K+V tile
   auto copy_tiles = [&](int t) __attribute__((always_inline)) {
     const int st = t & (kStages - 1);
@@ -411,29 +414,41 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     if (it > 0) __syncthreads();   // every wave is done reading the previous tile's stages
 #pragma unroll
     for (int t = 0; t < kStages - 1; ++t) copy_tiles(t);
+    wait_copies<(kStages - 2) * kC>();
+    __syncthreads();   // tile 0 has landed
+    copy_tiles(kStages - 1);
     // One loop per group (the group decides the order of the clusters); both
     // pass the same barriers in the same order.
     auto run = [&](auto gm) __attribute__((always_inline)) {
       constexpr int G = decltype(gm)::value;
+      // The operand reads of the next MFMA cluster are issued unconditionally
+      // (always inside LDS) at the start of the wave's softmax slot, so the LDS
+      // works while the VALU does the softmax.
       auto iter = [&](auto jm, int j) __attribute__((always_inline)) {
         constexpr int J = decltype(jm)::value;   // j % (2 * kStages)
-        if constexpr ((J & 1) == 0) {
+        constexpr int J1 = (J + 1) % (2 * kStages);
+        slot_barrier();
+        if constexpr (G == 0) {
+          if (j <= nh) cluster_c();
+        } else {
+          load_ops(jm);
+          if (j >= 1 && j - 1 < nh) cluster_s(j - 1);
+        }
+        if constexpr (J & 1) {
           wait_copies<(kStages - 2) * kC>();
-          __syncthreads();   // tile j/2 has landed; stage of tile j/2 - 1 is no longer read
-          copy_tiles(j / 2 + kStages - 1);
+          __syncthreads();   // tile (j+1)/2 has landed; tile (j+1)/2 - 1 is no longer read
+          copy_tiles((j + 1) / 2 + kStages - 1);
         } else {
           slot_barrier();
         }
         if constexpr (G == 0) {
-          if (j <= nh) cluster_c(jm);
-          slot_barrier();
+          load_ops(std::integral_constant<int, J1>{});
           if (j < nh) cluster_s(j);
         } else {
-          if (j >= 1 && j - 1 < nh) cluster_s(j - 1);
-          slot_barrier();
-          if (j <= nh) cluster_c(jm);
+          if (j <= nh) cluster_c();
         }
       };
+      if constexpr (G == 0) load_ops(std::integral_constant<int, 0>{});
       static_assert(kStages == 4, "the loop below is unrolled over 2 * kStages half tiles");
       for (int j0 = 0; j0 <= nh_wg; j0 += 8) {
         iter(std::integral_constant<int, 0>{}, j0);
