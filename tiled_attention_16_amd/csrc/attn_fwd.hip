@@ -75,20 +75,21 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-constexpr int kBN = 64;        // keys per K/V tile
-constexpr int kWaves = 8;      // wave64s per workgroup (two per SIMD), 32 query rows each
-constexpr int kStages = 4;     // LDS ring depth for K and V tiles: three tiles of copy lookahead
-constexpr int kBM = 32 * kWaves;
+constexpr int kSlice = 32;     // keys per K/V slice (one LDS stage, one pipeline step)
+constexpr int kStages = 8;     // LDS ring depth in slices
+constexpr int kWaves = 4;      // wave64s per workgroup, one per SIMD
+constexpr int kRows = 64;      // query rows per wave: two 32-row MFMA blocks
+constexpr int kBM = kRows * kWaves;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 units
 constexpr float kLn2 = 0.69314718055994530942f;
 
 template <int D>
-struct Tile {
+struct Slice {
   static constexpr int kRowBytes = 2 * D;
-  static constexpr int kBytes = kBN * kRowBytes;            // one K or V stage
-  static constexpr int kLds = 2 * kStages * kBytes;         // K stages, then V stages
-  static constexpr int kCopies = kBytes / 1024;             // 1 KB wave copies per stage
+  static constexpr int kBytes = kSlice * kRowBytes;          // one K or V stage
+  static constexpr int kLds = 2 * kStages * kBytes;          // K stages, then V stages
+  static constexpr int kCopies = kBytes / 1024;              // 1 KB wave copies per stage
   static constexpr int kCopiesPerWave = kCopies / kWaves;
   static constexpr int kRowsPerCopy = 1024 / kRowBytes;
   static constexpr int kLanesPerRow = 64 / kRowsPerCopy;
@@ -140,13 +141,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     uint16_t* __restrict__ O, float* __restrict__ LSE, int H, int N_q, int N_k, float c, int neg_scale,
     int causal, const int32_t* __restrict__ seqlens_k, const int32_t* __restrict__ q_start, int n_qt,
     int n_wg) {
-  using T = Tile<D>;
+  using T = Slice<D>;
   __shared__ __attribute__((aligned(1024))) char smem[T::kLds];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
-  const int grp = wave >> 2;   // waves w and w+4 share a SIMD: one of each group
   const int hf = lane >> 5;
 
   // ---- work decomposition: blockIdx -> (batch*head, pair of query tiles) ----
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   int qs = 0;
   if (q_start) qs = min(max(q_start[b], 0), N_q);
 
-  // ---- K/V tile copies: global -> LDS, 1 KB per wave instruction ----
+  // ---- K/V slice copies: global -> LDS, 1 KB per wave instruction ----
   // Copy q of this wave fills LDS bytes [1024*qi, 1024*qi + 1024) of a stage,
   // qi = wave * kCopiesPerWave + q: lane L lands at byte 16*L, which is row
   // qi*kRowsPerCopy + L / kLanesPerRow, chunk position L % kLanesPerRow, so it
@@ -181,13 +181,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const int r = cp_row(q);
     cp_off[q] = r * T::kRowBytes + (((lane % T::kLanesPerRow) ^ swz<D>(r)) << 4);
   }
-  // Copy the 64 rows starting at key k0 of a head's K or V into stage dst.
-  // Rows outside [0, kv) are never read: those lanes fetch a clamped row whose
-  // data the mask ignores (or that is multiplied by a zero probability).
-  auto copy_tile = [&](const char* src, int k0, const char* dst) __attribute__((always_inline)) {
+  // Copy the kSlice rows starting at key k0 of a head's K or V into stage dst.
+  // Rows at or past kv are never read: those lanes fetch the clamped last valid
+  // row, whose data the mask ignores (or multiplies by a zero probability).
+  auto copy_slice = [&](const char* src, int k0, const char* dst) __attribute__((always_inline)) {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)dst +
                           wave * T::kCopiesPerWave * 1024;
-    const bool ragged = k0 < 0 || k0 + kBN > kv;
+    const bool ragged = k0 + kSlice > kv;
     const char* base = ragged ? src : src + (ptrdiff_t)k0 * T::kRowBytes;
     // (readfirstlane returns a signed int: widen through uint32_t so the low
     // half is zero-extended, never sign-extended into the high half)
@@ -198,34 +198,40 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     for (int q = 0; q < T::kCopiesPerWave; ++q) {
       uint32_t voff = (uint32_t)cp_off[q];
       if (ragged) {
-        const int key = min(max(k0 + cp_row(q), 0), kv - 1);
+        const int key = min(k0 + cp_row(q), kv - 1);
         voff += (uint32_t)((key - cp_row(q)) * T::kRowBytes);
       }
       // The copy is issued as inline assembly so that the compiler does not
       // treat it as a pending write to every LDS address (it would then wait
       // for it before each LDS read); completion is awaited explicitly with
-      // wait_copies() before the barrier that publishes the tile.
+      // wait_copies() before the barrier that publishes the slice.
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                    :: "s"(__builtin_amdgcn_readfirstlane(lds0 + q * 1024)), "v"(voff), "s"(sbase)
                    : "memory", "m0");
     }
   };
-  // Stage st: K rows at kst(st), V rows at vst(st).
+  // Slice s lives in stage s % kStages: K rows at kst(st), V rows at vst(st).
   auto kst = [&](int st) __attribute__((always_inline)) { return (const char*)smem + st * T::kBytes; };
   auto vst = [&](int st) __attribute__((always_inline)) { return (const char*)smem + (kStages + st) * T::kBytes; };
+  constexpr int kC = 2 * T::kCopiesPerWave;   // copies per wave per K+V slice
+  auto copy_slices = [&](int s) __attribute__((always_inline)) {
+    const int st = s & (kStages - 1);
+    copy_slice(kg, s * kSlice, kst(st));
+    copy_slice(vg, s * kSlice, vst(st));
+  };
 
   // ---- per-lane LDS offsets of the MFMA operand reads ----
-  // K (A operand of S^T = K Q^T): lane L reads row L%32 of a 32-key half
-  // tile, logical chunk 2*kc + L/32, at byte r*kRowBytes + ((2kc + L/32) ^
-  // swz(r))*16. The swizzle only flips chunk bits, so the offset for chunk
-  // pair kc is k_off0 ^ (32*kc).
+  // K (A operand of S^T = K Q^T): lane L reads row L%32 of a slice, logical
+  // chunk 2*kc + L/32, at byte r*kRowBytes + ((2kc + L/32) ^ swz(r))*16. The
+  // swizzle only flips chunk bits, so the offset for chunk pair kc is
+  // k_off0 ^ (32*kc).
   // V (A operand of O^T += V^T P^T, via the transposing read): 16-key chunk cc,
   // half hi: lane L of group g = L/16 supplies row 16*cc + 8*hi + 4*(L/32) +
   // (L%16)/4, columns 32*db + 16*(g%2) + 4*(L%4) .. +3. After the transpose,
   // lane L holds column 32*db + L%32 of keys 16*cc + 8*hi + 4*(L/32) + 0..3,
-  // which pairs with P's registers 8*(cc%2) + 4*hi + 0..3 of the half tile.
-  // Its offset is v_off0 ^ (hi*(8*kRowBytes + 16)) ^ (64*db) (row +8 flips
-  // swizzle bit 0), plus 16*cc rows as an immediate.
+  // which pairs with P's registers 8*cc + 4*hi + 0..3. Its offset is
+  // v_off0 ^ (hi*(8*kRowBytes + 16)) ^ (64*db) (row +8 flips swizzle bit 0),
+  // plus 16*cc rows as an immediate.
   // Every base these are added to is a multiple of 16 rows, so base + (off ^ x)
   // == (base + off) ^ x and the bases stay immediate offsets.
   int k_off0, v_off0;
@@ -252,79 +258,80 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   if (causal) kv_end = min(kv_end, q_end);
   if (qs >= q_end) kv_end = 0;                     // every row of the tile is masked
 
-  const int row_lo = q0 + 32 * wave;               // this wave's rows: row_lo .. row_lo + 31
-  const int row_hi = min(row_lo + 31, N_q - 1);
+  // This wave's rows: row_lo .. row_lo + 63, as MFMA blocks rb = 0, 1 of 32
+  // rows; lane L holds row row_lo + 32*rb + L%32 of block rb.
+  const int row_lo = q0 + kRows * wave;
+  const int row_hi = min(row_lo + kRows - 1, N_q - 1);
   const bool wave_live = row_lo < N_q && row_hi >= qs;
-  const int my_row = row_lo + (lane & 31);
   const size_t q_base = (size_t)bh * N_q * D;
 
-  // 32-key half tiles h (keys 32h .. 32h+31): nh_wg for the workgroup, nh (a
-  // prefix) for this wave.
-  const int nh_wg = (kv_end + 31) / 32;
+  // slices: nh_wg for the workgroup, nh (a prefix) for this wave
+  const int nh_wg = (kv_end + kSlice - 1) / kSlice;
   int nh = wave_live ? nh_wg : 0;
-  if (causal) nh = min(nh, row_hi / 32 + 1);
+  if (causal) nh = min(nh, row_hi / kSlice + 1);
 
   // ---- Q rows -> VGPRs as the B operand of S^T = K Q^T ----
-  bf16x8 qreg[D / 16];
-  {
+  bf16x8 qreg[2][D / 16];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = row_lo + 32 * rb + (lane & 31);
     const uint32_t flip = neg_scale ? 0x80008000u : 0u;   // negative scale: negate Q exactly
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (my_row < N_q) x = *(const u32x4*)(Q + q_base + (size_t)my_row * D + kc * 16 + hf * 8);
+      if (row < N_q) x = *(const u32x4*)(Q + q_base + (size_t)row * D + kc * 16 + hf * 8);
       x ^= flip;
-      qreg[kc] = as_bf16x8(x);
+      qreg[rb][kc] = as_bf16x8(x);
     }
   }
 
-  f32x16 o_acc[D / 32];
+  f32x16 o_acc[2][D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) o_acc[db] = (f32x16){};
-  float m_run = -INFINITY;   // running max of S*c for this lane's row (same in lane ^ 32)
-  float l_run = 0.f;         // partial running sum over this lane's half of the keys
-  f32x16 s = {};             // S^T of the current half tile (one query row per lane)
-  bf16x8 pb[2] = {};         // P of the previous half tile, the B operand of P V
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o_acc[rb][db] = (f32x16){};
+  float m_run[2] = {-INFINITY, -INFINITY};   // running max of S*c of the lane's row in block rb
+  float l_run[2] = {0.f, 0.f};               // partial running sum over this lane's half of the keys
+  float alpha[2] = {1.f, 1.f};               // pending rescale of o_acc[rb]
+  bool o_stale = false;                      // some lane has alpha != 1 pending
 
-  // Key j is allowed for this lane's row iff j <= klim (klim folds the valid
-  // length, the causal limit and the masked leading rows into one bound).
-  const int klim = my_row < qs ? -1 : min(kv - 1, causal ? my_row : 0x7fffffff);
-  // masking is needed only where the half tile crosses that bound for some row
+  // Key j is allowed for row i iff j <= klim (klim folds the valid length, the
+  // causal limit and the masked leading rows into one bound).
+  int klim[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = row_lo + 32 * rb + (lane & 31);
+    klim[rb] = row < qs ? -1 : min(kv - 1, causal ? row : 0x7fffffff);
+  }
+  // masking is needed only where slice h crosses that bound for some row
   auto need_mask = [&](int h) __attribute__((always_inline)) {
-    const int k0 = h * 32;
-    return (k0 + 31 >= kv) || (causal && k0 + 31 > row_lo) || (row_lo < qs);
+    const int k0 = h * kSlice;
+    return (k0 + kSlice - 1 >= kv) || (causal && k0 + kSlice - 1 > row_lo) || (row_lo < qs);
+  };
+  auto mask = [&](int h, f32x16 (&s)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int lim = klim[rb] - h * kSlice - 4 * hf;   // key offset within the slice must be <= lim
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[rb][r] = (8 * (r >> 2) + (r & 3)) <= lim ? s[rb][r] : -INFINITY;
+    }
   };
 
-  // K tile t holds keys 64t .. 64t+63 (K halves 2t, 2t+1); V tile t holds keys
-  // 64t-32 .. 64t+31 (V halves 2t-1, 2t). Both live in stage t % kStages.
-  // K half h: stage (h/2) % kStages, row 32*(h%2); V half h: stage
-  // ((h+1)/2) % kStages, row 32*(1 - h%2). Callers pass h modulo 2*kStages as
-  // a compile-time constant, so every LDS address is a per-lane offset plus an
-  // immediate.
-  auto k_half = [&](auto hm) __attribute__((always_inline)) {
-    constexpr int h = decltype(hm)::value;
-    return kst((h >> 1) % kStages) + (h & 1) * 32 * T::kRowBytes;
-  };
-  auto v_half = [&](auto hm) __attribute__((always_inline)) {
-    constexpr int h = decltype(hm)::value;
-    return vst(((h + 1) >> 1) % kStages) + (~h & 1) * 32 * T::kRowBytes;
-  };
-
-  // Operands of cluster C_h: K of half h (A operand of S^T = K Q^T) and V of
-  // half h-1 (A operand of O^T += V^T P^T). They are read from LDS one cluster
-  // ahead, during the softmax cluster of the same wave, so the MFMA cluster
-  // itself never waits on LDS and the reads of one group overlap the other
-  // group's MFMAs.
+  // Operand registers: K of the slice the next QK reads, V of the slice the
+  // next PV reads. Each is read from LDS one phase before it is used.
   u32x4 ka[D / 16];
   bf16x8 va[2][D / 32];
-  auto load_ops = [&](auto hm) __attribute__((always_inline)) {
-    constexpr int h = decltype(hm)::value;   // half index modulo 2*kStages
-    const char* kb = k_half(std::integral_constant<int, h>{});
-    const char* vb = v_half(std::integral_constant<int, (h + 2 * kStages - 1) % (2 * kStages)>{});
-    // (re-derive the offsets here instead of keeping 16 of them live)
-    int ko = k_off0, vo = v_off0;
-    asm volatile("" : "+v"(ko), "+v"(vo));
+  auto load_k = [&](auto sm) __attribute__((always_inline)) {
+    const char* kb = kst(decltype(sm)::value);
+    int ko = k_off0;
+    asm volatile("" : "+v"(ko));   // re-derive the offsets here instead of keeping them live
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) ka[kc] = *(const lds_u32x4*)(kb + (ko ^ (32 * kc)));
+  };
+  auto load_v = [&](auto sm) __attribute__((always_inline)) {
+    const char* vb = vst(decltype(sm)::value);
+    int vo = v_off0;
+    asm volatile("" : "+v"(vo));
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int off_lo = vo ^ (64 * db);
@@ -338,157 +345,182 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       }
     }
   };
-  // Cluster C_h (MFMA): S of half h (into s) and O += P V of half h-1 (P from
-  // the previous softmax cluster; zero before the first).
-  auto cluster_c = [&]() __attribute__((always_inline)) {
-    s = (f32x16){};
+  // S^T = K Q^T for both row blocks: each K fragment feeds two MFMAs.
+  auto qk = [&](f32x16 (&s)[2]) __attribute__((always_inline)) {
+    s[0] = (f32x16){};
+    s[1] = (f32x16){};
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[kc]), qreg[kc], s, 0, 0, 0);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[kc]), qreg[rb][kc], s[rb], 0, 0, 0);
+  };
+  // O^T += V^T P^T for both row blocks: each V fragment feeds two MFMAs.
+  auto pv = [&](const bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
-        o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cc][db], pb[cc], o_acc[db], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          o_acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cc][db], pb[rb][cc], o_acc[rb][db], 0, 0, 0);
+  };
+  // row max, running-max update, and S <- S*c - m (in place); a slice that is
+  // not live leaves the running state unchanged
+  auto rowmax_shift = [&](f32x16 (&s)[2], bool live) __attribute__((always_inline)) {
+    bool grow_any = false;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const f32x16& x = s[rb];
+      const float a0 = fmaxf(fmaxf(x[0], x[1]), x[2]), a1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
+      const float a2 = fmaxf(fmaxf(x[6], x[7]), x[8]), a3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
+      const float a4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
+      const float mx = lane_swap_max(fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), x[15])));
+      const float tmax = live ? mx * c : -INFINITY;   // c > 0, so -inf stays -inf
+      const bool grow = tmax > m_run[rb] + kTau;
+      const float m_new = grow ? tmax : m_run[rb];
+      const float a = grow ? __builtin_amdgcn_exp2f(m_run[rb] - m_new) : 1.f;   // m_run = -inf gives 0
+      l_run[rb] *= a;
+      alpha[rb] *= a;
+      m_run[rb] = m_new;
+      grow_any = grow_any || grow;
+      const float msub = (m_new == -INFINITY) ? 0.f : m_new;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[rb][r] = fmaf(s[rb][r], c, -msub);
+    }
+    o_stale = o_stale || __builtin_amdgcn_ballot_w64(grow_any) != 0;
+  };
+  // P = exp2(S*c - m): fp32 into the row sums, bf16 into the PV operand
+  auto expo = [&](const f32x16 (&s)[2], bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(s[rb][r]);
+      l_run[rb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])) +
+                   (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const u32x4 w = {pack2(p[8 * u + 0], p[8 * u + 1]), pack2(p[8 * u + 2], p[8 * u + 3]),
+                         pack2(p[8 * u + 4], p[8 * u + 5]), pack2(p[8 * u + 6], p[8 * u + 7])};
+        pb[rb][u] = as_bf16x8(w);
+      }
+    }
   };
 
-  // Cluster S_h (VALU): the online softmax of half h on s.
-  auto cluster_s = [&](int h) __attribute__((always_inline)) {
-    if (need_mask(h)) {
-      const int lim = klim - h * 32 - 4 * hf;   // key offset within the half tile must be <= lim
+  // Step h (slice h; S of slice h is in sc, already shifted):
+  //   wait for slices <= h+2, barrier, copy slice h+7 into slice h-1's stage;
+  //   phase A: read V(h); QK(h+1) on the MFMA unit (K(h+1) read last phase)
+  //            while the VALU exponentiates slice h;
+  //   phase B: read K(h+2); PV(h) on the MFMA unit while the VALU takes the
+  //            row max of slice h+1 and forms S*c - m.
+  // Slice h+1 may lie past this wave's last slice: its S is then computed from
+  // whatever the stage holds and discarded, so no branch splits a phase.
+  // Slice h-1's stage is free at step h: V(h-1) was read in step h-1 and
+  // K(h-1) in step h-3. Copies are issued for every step, also past the last
+  // slice (clamped rows), so the number in flight, and with it the wait
+  // count, is the same each time: slices h+3 .. h+6 may still be in flight.
+  auto step = [&](auto hm, int h, f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
+    constexpr int Hm = decltype(hm)::value;   // h % kStages
+    wait_copies<4 * kC>();
+    __syncthreads();   // slices <= h+2 have landed; slice h-1's stage is no longer read
+    copy_slices(h + kStages - 1);
+    if (h >= nh) return;
+    if (o_stale) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3)) <= lim ? s[r] : -INFINITY;
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o_acc[rb][db] *= alpha[rb];
+      alpha[0] = alpha[1] = 1.f;
+      o_stale = false;
     }
-    const float a0 = fmaxf(fmaxf(s[0], s[1]), s[2]), a1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
-    const float a2 = fmaxf(fmaxf(s[6], s[7]), s[8]), a3 = fmaxf(fmaxf(s[9], s[10]), s[11]);
-    const float a4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
-    const float mx = lane_swap_max(fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), s[15])));
-    const float tmax = mx * c;   // c > 0, so -inf stays -inf
-    const bool grow = tmax > m_run + kTau;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      // raise the subtrahend; rescale l and O (O holds P V up to half h-1)
-      const float m_new = grow ? tmax : m_run;
-      const float a = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;   // m_run = -inf gives 0
-      m_run = m_new;
-      l_run *= a;
+    const bool nxt = h + 1 < nh;
+    bf16x8 pb[2][2];
+    load_v(std::integral_constant<int, Hm>{});
+    qk(sn);
+    expo(sc, pb);
+    // keep P and l in this block (the compiler would otherwise sink them
+    // past the mask branch, away from the MFMAs they are meant to overlap)
+    asm volatile("" :: "v"(pb[0][0]), "v"(pb[0][1]), "v"(pb[1][0]), "v"(pb[1][1]), "v"(l_run[0]), "v"(l_run[1]));
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * D / 16, 0);   // DS read: V
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) o_acc[db] *= a;
+    for (int i = 0; i < D / 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);            // VALU
     }
-    const float msub = (m_run == -INFINITY) ? 0.f : m_run;
-    float p[16];
+    if (nxt && need_mask(h + 1)) mask(h + 1, sn);
+    load_k(std::integral_constant<int, (Hm + 2) % kStages>{});
+    pv(pb);
+    rowmax_shift(sn, nxt);
+    __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 1);       // DS read: K
 #pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -msub));
-    l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])) +
-             (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const u32x4 w = {pack2(p[8 * u + 0], p[8 * u + 1]), pack2(p[8 * u + 2], p[8 * u + 3]),
-                       pack2(p[8 * u + 4], p[8 * u + 5]), pack2(p[8 * u + 6], p[8 * u + 7])};
-      pb[u] = as_bf16x8(w);
+    for (int i = 0; i < D / 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);            // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);            // VALU
     }
   };
 
-  // Ping-pong: every SIMD holds one wave of each group. In iteration j group 0
-  // runs C_j then S_j, group 1 runs S_{j-1} then C_j, with a workgroup barrier
-  // between the halves ("slots" 2j and 2j+1), so one wave of each SIMD feeds
-  // the MFMA unit while the other works on the VALU and reads the operands of
-  // its next MFMA cluster from LDS. Tile t (K halves 2t, 2t+1; V halves 2t-1,
-  // 2t) is read in slots 4t-1 .. 4t+2, so the workgroup waits for tile t at the
-  // barrier before slot 4t-1 and, once every wave has passed that barrier
-  // (the last reads of tile t-1 were in slot 4t-2), copies tile t+3 into tile
-  // t-1's stage. Copies are issued for every tile step, also past the last
-  // tile (clamped rows), so that the number in flight, and with it every wait
-  // count, is the same each time.
-  constexpr int kC = 2 * T::kCopiesPerWave;   // copies per wave per K+V tile
-  auto copy_tiles = [&](int t) __attribute__((always_inline)) {
-    const int st = t & (kStages - 1);
-    copy_tile(kg, t * kBN, kst(st));
-    copy_tile(vg, t * kBN - 32, vst(st));
-  };
-  auto slot_barrier = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
+  f32x16 sa[2], sb[2];
   if (nh_wg > 0) {
     if (it > 0) __syncthreads();   // every wave is done reading the previous tile's stages
 #pragma unroll
-    for (int t = 0; t < kStages - 1; ++t) copy_tiles(t);
-    wait_copies<(kStages - 2) * kC>();
-    __syncthreads();   // tile 0 has landed
-    copy_tiles(kStages - 1);
-    // One loop per group (the group decides the order of the clusters); both
-    // pass the same barriers in the same order.
-    auto run = [&](auto gm) __attribute__((always_inline)) {
-      constexpr int G = decltype(gm)::value;
-      // The operand reads of the next MFMA cluster are issued unconditionally
-      // (always inside LDS) at the start of the wave's softmax slot, so the LDS
-      // works while the VALU does the softmax.
-      auto iter = [&](auto jm, int j) __attribute__((always_inline)) {
-        constexpr int J = decltype(jm)::value;   // j % (2 * kStages)
-        constexpr int J1 = (J + 1) % (2 * kStages);
-        slot_barrier();
-        if constexpr (G == 0) {
-          if (j <= nh) cluster_c();
-        } else {
-          load_ops(jm);
-          if (j >= 1 && j - 1 < nh) cluster_s(j - 1);
-        }
-        if constexpr (J & 1) {
-          wait_copies<(kStages - 2) * kC>();
-          __syncthreads();   // tile (j+1)/2 has landed; tile (j+1)/2 - 1 is no longer read
-          copy_tiles((j + 1) / 2 + kStages - 1);
-        } else {
-          slot_barrier();
-        }
-        if constexpr (G == 0) {
-          load_ops(std::integral_constant<int, J1>{});
-          if (j < nh) cluster_s(j);
-        } else {
-          if (j <= nh) cluster_c();
-        }
-      };
-      if constexpr (G == 0) load_ops(std::integral_constant<int, 0>{});
-      static_assert(kStages == 4, "the loop below is unrolled over 2 * kStages half tiles");
-      for (int j0 = 0; j0 <= nh_wg; j0 += 8) {
-        iter(std::integral_constant<int, 0>{}, j0);
-        if (j0 + 1 > nh_wg) break;
-        iter(std::integral_constant<int, 1>{}, j0 + 1);
-        if (j0 + 2 > nh_wg) break;
-        iter(std::integral_constant<int, 2>{}, j0 + 2);
-        if (j0 + 3 > nh_wg) break;
-        iter(std::integral_constant<int, 3>{}, j0 + 3);
-        if (j0 + 4 > nh_wg) break;
-        iter(std::integral_constant<int, 4>{}, j0 + 4);
-        if (j0 + 5 > nh_wg) break;
-        iter(std::integral_constant<int, 5>{}, j0 + 5);
-        if (j0 + 6 > nh_wg) break;
-        iter(std::integral_constant<int, 6>{}, j0 + 6);
-        if (j0 + 7 > nh_wg) break;
-        iter(std::integral_constant<int, 7>{}, j0 + 7);
-      }
-    };
-    if (grp == 0) run(std::integral_constant<int, 0>{});
-    else run(std::integral_constant<int, 1>{});
+    for (int s = 0; s < kStages - 1; ++s) copy_slices(s);
+    wait_copies<4 * kC>();
+    __syncthreads();   // slices 0 .. 2 have landed
+    if (nh > 0) {
+      load_k(std::integral_constant<int, 0>{});
+      qk(sa);
+      if (need_mask(0)) mask(0, sa);
+      rowmax_shift(sa, true);
+      load_k(std::integral_constant<int, 1>{});
+    }
+    static_assert(kStages == 8, "the loop below is unrolled over kStages slices");
+    for (int h0 = 0; h0 < nh_wg; h0 += 8) {
+      step(std::integral_constant<int, 0>{}, h0, sa, sb);
+      if (h0 + 1 >= nh_wg) break;
+      step(std::integral_constant<int, 1>{}, h0 + 1, sb, sa);
+      if (h0 + 2 >= nh_wg) break;
+      step(std::integral_constant<int, 2>{}, h0 + 2, sa, sb);
+      if (h0 + 3 >= nh_wg) break;
+      step(std::integral_constant<int, 3>{}, h0 + 3, sb, sa);
+      if (h0 + 4 >= nh_wg) break;
+      step(std::integral_constant<int, 4>{}, h0 + 4, sa, sb);
+      if (h0 + 5 >= nh_wg) break;
+      step(std::integral_constant<int, 5>{}, h0 + 5, sb, sa);
+      if (h0 + 6 >= nh_wg) break;
+      step(std::integral_constant<int, 6>{}, h0 + 6, sa, sb);
+      if (h0 + 7 >= nh_wg) break;
+      step(std::integral_constant<int, 7>{}, h0 + 7, sb, sa);
+    }
     wait_copies<0>();   // no copy may still be writing LDS when the next tile (or wave) starts
+  }
+  if (o_stale) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o_acc[rb][db] *= alpha[rb];
   }
 
   // ---- epilogue: O / l, LSE, bf16 store ----
-  if (my_row < N_q) {
-    const float l_tot = lane_swap_add(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = O + q_base + (size_t)my_row * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = row_lo + 32 * rb + (lane & 31);
+    const float l_tot = lane_swap_add(l_run[rb]);
+    if (row < N_q) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      uint16_t* orow = O + q_base + (size_t)row * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 w = {pack2(o_acc[db][4 * g + 0] * inv, o_acc[db][4 * g + 1] * inv),
-                         pack2(o_acc[db][4 * g + 2] * inv, o_acc[db][4 * g + 3] * inv)};
-        *(u32x2*)(orow + 32 * db + 8 * g + 4 * hf) = w;
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x2 w = {pack2(o_acc[rb][db][4 * g + 0] * inv, o_acc[rb][db][4 * g + 1] * inv),
+                           pack2(o_acc[rb][db][4 * g + 2] * inv, o_acc[rb][db][4 * g + 3] * inv)};
+          *(u32x2*)(orow + 32 * db + 8 * g + 4 * hf) = w;
+        }
       }
+      if (LSE && lane < 32)
+        LSE[(size_t)bh * N_q + row] = l_tot > 0.f ? (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     }
-    if (LSE && lane < 32)
-      LSE[(size_t)bh * N_q + my_row] = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   }
   }   // tiles of the pair
 }
