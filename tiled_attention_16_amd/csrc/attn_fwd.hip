@@ -127,6 +127,30 @@ __device__ __forceinline__ float lane_swap_add(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// MFMA 32x32x16 bf16 -> fp32, issued as inline assembly so that each
+// accumulator's register class is fixed: scores in VGPRs (the VALU reads
+// them), the output accumulator and Q in AGPRs (in the loop only MFMAs touch
+// them).
+// The compiler does not know these are MFMAs, so the code itself places the
+// wait states an MFMA result needs before anything else reads it
+// (mfma_result_wait), and keeps VALU writes of MFMA inputs far from the MFMA.
+// (scores: A from VGPRs, B = Q from AGPRs, where Q stays for the whole tile)
+// Each begins with 3 wait states: the compiler may materialise an operand
+// with a VALU or v_accvgpr_write move right before, and an MFMA must not read
+// a register in the 2 wait states after such a write.
+__device__ __forceinline__ void mfma_v_init(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_a(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// 24 wait states: more than a 32x32 MFMA result needs before another
+// instruction may read it.
+__device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
 // Wait until at most N of this wave's copies are still in flight (copies
 // complete in issue order).
 template <int N>
@@ -213,6 +237,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // Slice s lives in stage s % kStages: K rows at kst(st), V rows at vst(st).
   auto kst = [&](int st) __attribute__((always_inline)) { return (const char*)smem + st * T::kBytes; };
   auto vst = [&](int st) __attribute__((always_inline)) { return (const char*)smem + (kStages + st) * T::kBytes; };
+  // the V stage base relative to the folded-in kVBase (see v_off below)
+  auto vst_rel = [&](int st) __attribute__((always_inline)) { return (const char*)smem + st * T::kBytes; };
   constexpr int kC = 2 * T::kCopiesPerWave;   // copies per wave per K+V slice
   auto copy_slices = [&](int s) __attribute__((always_inline)) {
     const int st = s & (kStages - 1);
@@ -242,6 +268,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const int rv = 4 * hf + ((lane & 15) >> 2);
     const int byte = 32 * (g & 1) + 8 * (lane & 3);
     v_off0 = rv * T::kRowBytes + (((byte >> 4) ^ swz<D>(rv)) << 4) + (byte & 15);
+  }
+  // All operand offsets, kept in registers. The V stages start at
+  // kStages * kBytes (64 KB for d = 128), more than a DS immediate holds, so
+  // that base is folded into the V offsets (it has no bits below 64 KB, so it
+  // commutes with the XORs) and the immediates stay below it.
+  constexpr int kVBase = kStages * T::kBytes;
+  int k_off[D / 16], v_off[2][D / 32];
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) k_off[kc] = k_off0 ^ (32 * kc);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    v_off[0][db] = (v_off0 ^ (64 * db)) + kVBase;
+    v_off[1][db] = (v_off0 ^ (64 * db) ^ (8 * T::kRowBytes + 16)) + kVBase;
   }
 
   // A workgroup owns the pair of query tiles (n_qt-1-pr, pr): under a causal
@@ -323,59 +362,36 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   bf16x8 va[2][D / 32];
   auto load_k = [&](auto sm) __attribute__((always_inline)) {
     const char* kb = kst(decltype(sm)::value);
-    int ko = k_off0;
-    asm volatile("" : "+v"(ko));   // re-derive the offsets here instead of keeping them live
 #pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) ka[kc] = *(const lds_u32x4*)(kb + (ko ^ (32 * kc)));
+    for (int kc = 0; kc < D / 16; ++kc) ka[kc] = *(const lds_u32x4*)(kb + k_off[kc]);
   };
-  auto load_v = [&](auto sm) __attribute__((always_inline)) {
-    const char* vb = vst(decltype(sm)::value);
-    int vo = v_off0;
-    asm volatile("" : "+v"(vo));
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int off_lo = vo ^ (64 * db);
-      const int off_hi = off_lo ^ (8 * T::kRowBytes + 16);
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const char* p0 = vb + 16 * cc * T::kRowBytes;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + off_lo));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + off_hi));
-        va[cc][db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-    }
-  };
-  // S^T = K Q^T for both row blocks: each K fragment feeds two MFMAs.
+  // S^T = K Q^T for both row blocks, not interleaved (prologue only).
   auto qk = [&](f32x16 (&s)[2]) __attribute__((always_inline)) {
-    s[0] = (f32x16){};
-    s[1] = (f32x16){};
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[kc]), qreg[rb][kc], s[rb], 0, 0, 0);
+      for (int rb = 0; rb < 2; ++rb) {
+        if (kc == 0) mfma_v_init(s[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
+        else mfma_v(s[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
+      }
+    mfma_result_wait();
   };
-  // O^T += V^T P^T for both row blocks: each V fragment feeds two MFMAs.
-  auto pv = [&](const bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          o_acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cc][db], pb[rb][cc], o_acc[rb][db], 0, 0, 0);
-  };
-  // row max, running-max update, and S <- S*c - m (in place); a slice that is
-  // not live leaves the running state unchanged
-  auto rowmax_shift = [&](f32x16 (&s)[2], bool live) __attribute__((always_inline)) {
-    bool grow_any = false;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const f32x16& x = s[rb];
+  // Row max of block rb, running-max update, and S <- S*c - m, in four
+  // sub-steps (so they can be spread between MFMAs): partial maxes; the row max
+  // and running-max update; the shift of elements 0..7; of elements 8..15. A slice that is not live
+  // leaves the running state unchanged.
+  float part[2][3];
+  bool grow_any = false;
+  auto rowmax_sub = [&](f32x16 (&s)[2], int rb, int sub, bool live) __attribute__((always_inline)) {
+    f32x16& x = s[rb];
+    if (sub == 0) {   // partial maxes
       const float a0 = fmaxf(fmaxf(x[0], x[1]), x[2]), a1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
       const float a2 = fmaxf(fmaxf(x[6], x[7]), x[8]), a3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
       const float a4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
-      const float mx = lane_swap_max(fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), x[15])));
+      part[rb][0] = fmaxf(fmaxf(a0, a1), a2);
+      part[rb][1] = fmaxf(fmaxf(a3, a4), x[15]);
+    } else if (sub == 1) {   // row max across the lane pair, running-max update
+      const float mx = lane_swap_max(fmaxf(part[rb][0], part[rb][1]));
       const float tmax = live ? mx * c : -INFINITY;   // c > 0, so -inf stays -inf
       const bool grow = tmax > m_run[rb] + kTau;
       const float m_new = grow ? tmax : m_run[rb];
@@ -384,42 +400,54 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       alpha[rb] *= a;
       m_run[rb] = m_new;
       grow_any = grow_any || grow;
-      const float msub = (m_new == -INFINITY) ? 0.f : m_new;
+      part[rb][2] = (m_new == -INFINITY) ? 0.f : -m_new;   // minus the exponent's subtrahend
+    } else {   // S*c - m for elements 0..7 (sub 2) or 8..15 (sub 3)
+      const int r0 = 8 * (sub - 2);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[rb][r] = fmaf(s[rb][r], c, -msub);
+      for (int r = 0; r < 8; ++r) x[r0 + r] = fmaf(x[r0 + r], c, part[rb][2]);
     }
-    o_stale = o_stale || __builtin_amdgcn_ballot_w64(grow_any) != 0;
   };
-  // P = exp2(S*c - m): fp32 into the row sums, bf16 into the PV operand
-  auto expo = [&](const f32x16 (&s)[2], bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
+  // P = exp2(S*c - m) for elements e0 .. e0+n-1 of block rb: fp32 into the
+  // row sum, bf16 pairs into the PV operand words.
+  uint32_t pbw[2][8];
+  float lsum[2];
+  auto expo_part = [&](const f32x16 (&s)[2], int rb, int e0, int n) __attribute__((always_inline)) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(s[rb][r]);
-      l_run[rb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])) +
-                   (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const u32x4 w = {pack2(p[8 * u + 0], p[8 * u + 1]), pack2(p[8 * u + 2], p[8 * u + 3]),
-                         pack2(p[8 * u + 4], p[8 * u + 5]), pack2(p[8 * u + 6], p[8 * u + 7])};
-        pb[rb][u] = as_bf16x8(w);
-      }
+    for (int e = e0; e < e0 + n; e += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(s[rb][e]);
+      const float p1 = __builtin_amdgcn_exp2f(s[rb][e + 1]);
+      lsum[rb] += p0 + p1;
+      pbw[rb][e >> 1] = pack2(p0, p1);
     }
+  };
+  auto pb = [&](int rb, int cc) __attribute__((always_inline)) {
+    const u32x4 w = {pbw[rb][4 * cc], pbw[rb][4 * cc + 1], pbw[rb][4 * cc + 2], pbw[rb][4 * cc + 3]};
+    return as_bf16x8(w);
+  };
+  // one transposing V read pair: va[cc][db] for PV
+  auto load_v_one = [&](const char* vb, int cc, int db) __attribute__((always_inline)) {
+    const char* p0 = vb + 16 * cc * T::kRowBytes;   // vb: vst_rel of the stage
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + v_off[0][db]));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + v_off[1][db]));
+    va[cc][db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
   // Step h (slice h; S of slice h is in sc, already shifted):
   //   wait for slices <= h+2, barrier, copy slice h+7 into slice h-1's stage;
-  //   phase A: read V(h); QK(h+1) on the MFMA unit (K(h+1) read last phase)
-  //            while the VALU exponentiates slice h;
-  //   phase B: read K(h+2); PV(h) on the MFMA unit while the VALU takes the
-  //            row max of slice h+1 and forms S*c - m.
+  //   phase A: QK(h+1) on the MFMA unit (K(h+1) was read last phase) while the
+  //            VALU exponentiates slice h and the LDS reads V(h);
+  //   phase B: PV(h) on the MFMA unit while the VALU takes the row max of
+  //            slice h+1 and forms S*c - m, and the LDS reads K(h+2).
+  // Each phase is written as kG groups of one MFMA, a share of the LDS reads
+  // and a share of the VALU work, fenced so the scheduler keeps that order:
+  // every MFMA overlaps the VALU work that follows it.
   // Slice h+1 may lie past this wave's last slice: its S is then computed from
   // whatever the stage holds and discarded, so no branch splits a phase.
   // Slice h-1's stage is free at step h: V(h-1) was read in step h-1 and
   // K(h-1) in step h-3. Copies are issued for every step, also past the last
   // slice (clamped rows), so the number in flight, and with it the wait
   // count, is the same each time: slices h+3 .. h+6 may still be in flight.
+  constexpr int kG = D / 8;             // MFMAs per phase
   auto step = [&](auto hm, int h, f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
     constexpr int Hm = decltype(hm)::value;   // h % kStages
     wait_copies<4 * kC>();
@@ -427,6 +455,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     copy_slices(h + kStages - 1);
     if (h >= nh) return;
     if (o_stale) {
+      mfma_result_wait();
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -435,28 +464,58 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       o_stale = false;
     }
     const bool nxt = h + 1 < nh;
-    bf16x8 pb[2][2];
-    load_v(std::integral_constant<int, Hm>{});
-    qk(sn);
-    expo(sc, pb);
-    // keep P and l in this block (the compiler would otherwise sink them
-    // past the mask branch, away from the MFMAs they are meant to overlap)
-    asm volatile("" :: "v"(pb[0][0]), "v"(pb[0][1]), "v"(pb[1][0]), "v"(pb[1][1]), "v"(l_run[0]), "v"(l_run[1]));
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * D / 16, 0);   // DS read: V
+    // ---- phase A ----
+    {
+      const char* vb = vst_rel(Hm);
+      lsum[0] = lsum[1] = 0.f;
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < D / 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);            // VALU
+      for (int g = 0; g < kG; ++g) {
+        const int kc = g >> 1, rb = g & 1;
+        if (kc == 0) mfma_v_init(sn[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
+        else mfma_v(sn[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
+        if ((g & 1) == 0) {   // V reads for PV group g/2, (cc, db) in PV order
+          const int pg = g >> 1;
+          load_v_one(vb, pg / (D / 32), pg % (D / 32));
+        }
+        constexpr int kPer = 32 / kG;   // exponentials per group
+        expo_part(sc, (g * kPer) / 16, (g * kPer) % 16, kPer);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // keep P and the sums in this phase (the compiler would otherwise sink
+      // them past the mask branch, away from the MFMAs they overlap)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        asm volatile("" :: "v"(pbw[rb][0]), "v"(pbw[rb][1]), "v"(pbw[rb][2]), "v"(pbw[rb][3]),
+                     "v"(pbw[rb][4]), "v"(pbw[rb][5]), "v"(pbw[rb][6]), "v"(pbw[rb][7]), "v"(lsum[rb]));
+      l_run[0] += lsum[0];
+      l_run[1] += lsum[1];
     }
+    mfma_result_wait();   // S of slice h+1 is read below
     if (nxt && need_mask(h + 1)) mask(h + 1, sn);
-    load_k(std::integral_constant<int, (Hm + 2) % kStages>{});
-    pv(pb);
-    rowmax_shift(sn, nxt);
-    __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 1);       // DS read: K
+    // ---- phase B ----
+    {
+      const char* kb = kst((Hm + 2) % kStages);
+      grow_any = false;
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < D / 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);            // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);            // VALU
+      for (int g = 0; g < kG; ++g) {
+        const int pg = g >> 1, rb = g & 1;
+        const int cc = pg / (D / 32), db = pg % (D / 32);
+        mfma_a(o_acc[rb][db], va[cc][db], pb(rb, cc));
+        if (g < D / 16) ka[g] = *(const lds_u32x4*)(kb + k_off[g]);
+        // the eight row-max sub-steps (4 per block) spread over the groups
+        constexpr int kSubPer = 8 / kG > 0 ? 8 / kG : 1;
+        if (g * kSubPer < 8 || kG > 8) {
+#pragma unroll
+          for (int u = 0; u < kSubPer; ++u) {
+            const int sub = (g * 8) / kG + u;
+            if (kG <= 8 || (g * 8) % kG == 0) rowmax_sub(sn, sub >> 2, sub & 3, nxt);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      o_stale = o_stale || __builtin_amdgcn_ballot_w64(grow_any) != 0;
     }
   };
 
@@ -471,7 +530,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       load_k(std::integral_constant<int, 0>{});
       qk(sa);
       if (need_mask(0)) mask(0, sa);
-      rowmax_shift(sa, true);
+      grow_any = false;
+#pragma unroll
+      for (int sub = 0; sub < 8; ++sub) rowmax_sub(sa, sub >> 2, sub & 3, true);
+      o_stale = o_stale || __builtin_amdgcn_ballot_w64(grow_any) != 0;
       load_k(std::integral_constant<int, 1>{});
     }
     static_assert(kStages == 8, "the loop below is unrolled over kStages slices");
@@ -494,6 +556,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     }
     wait_copies<0>();   // no copy may still be writing LDS when the next tile (or wave) starts
   }
+  mfma_result_wait();   // the last P V MFMAs have written o_acc
   if (o_stale) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
