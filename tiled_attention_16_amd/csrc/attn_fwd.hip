@@ -8,31 +8,33 @@
 // What one launch computes is stated in include/attn.h. How:
 //
 // Work decomposition ([MEMWALL] §2.2, outer loop over query blocks, inner loop
-// over key/value blocks): one workgroup of 4 wave64s owns a 128-row query tile
-// of one (batch, head); each wave owns 32 of those rows for the whole launch.
-// The workgroup walks the 64-key K/V tiles its rows can see; causal tiles above
-// the diagonal and tiles past the batch's valid key length are never visited,
-// and a wave skips the arithmetic of tiles that lie wholly above its own rows.
+// over key/value blocks): one workgroup of 8 wave64s (two per SIMD) owns a
+// pair of 256-row query tiles of one (batch, head), processed one after the
+// other; each wave owns 32 rows of the tile. Under a causal mask the pair is
+// (t, n-1-t), so every workgroup carries the same number of key slices. The
+// workgroup walks the 32-key K/V slices its rows can see; slices above the
+// causal diagonal and past the batch's valid key length are never visited,
+// and a wave stops computing at the last slice its own rows can see.
 //
-// Data movement ([MEMWALL] §4.3 double buffering; [PT2CUDA] step 5): K and V
-// tiles go from global memory straight into LDS with the gfx950 16-byte
-// global_load_lds copy, no register staging. K and V each have two LDS stages;
-// the copies for K tile j+2 and V tile j+1 are in flight while tile j is
-// computed, and one barrier per tile both publishes the landed tiles and frees
-// the stages read in the previous step. Inside a stage, row r's 16-byte chunk c
-// sits at chunk position c ^ swz(r): the MFMA operand reads (ds_read_b128 for K,
-// the transposing ds_read_b64_tr_b16 for V) then touch distinct banks.
+// Data movement ([MEMWALL] §4.3 double buffering, here an 8-deep ring;
+// [PT2CUDA] step 5): K and V slices go from global memory straight into LDS
+// with the gfx950 16-byte global_load_lds copy, no register staging. Each
+// wave issues its share of the copy of slice h+7 at the end of step h, into
+// the stage slice h-1 used; one barrier per step publishes the landed slices
+// and frees that stage. Inside a stage, row r's 16-byte chunk c sits at chunk
+// position c ^ swz(r), so the MFMA operand reads (ds_read_b128 for K, the
+// transposing ds_read_b64_tr_b16 for V) touch distinct banks.
 //
-// Per K/V tile, per wave (the online softmax of [PT2CUDA] step 3.1 and
+// Per K/V slice, per wave (the online softmax of [PT2CUDA] step 3.1 and
 // [MEMWALL] §3.2, in the exp2 domain with c = |scale| * log2(e)):
 //   S^T = K Q^T on MFMA 32x32x16 bf16 -> fp32. Computing the transpose puts one
-//         query row in each lane (32 keys per lane, the other 32 keys of the
-//         tile in lane ^ 32): the row max is an in-register max plus one
+//         query row in each lane (16 keys per lane, the other 16 keys of the
+//         slice in lane ^ 32): the row max is an in-register max plus one
 //         permlane32 swap, and the row sum needs no cross-lane step until the
 //         very end.
-//   mask  only on tiles that cross the causal diagonal, the valid key length or
-//         the masked leading rows: the score becomes -inf.
-//   m     running max of S*c per row. It is raised only when the tile's max
+//   mask  only on slices that cross the causal diagonal, the valid key length
+//         or the masked leading rows: the score becomes -inf.
+//   m     running max of S*c per row. It is raised only when the slice's max
 //         exceeds it by more than kTau; otherwise the stale max stays the
 //         exponent's subtrahend. O / l does not depend on the subtrahend, so
 //         this is the pages' recurrence in exact arithmetic; the exponentials
@@ -44,9 +46,10 @@
 //   O^T  += V^T P^T on MFMA 32x32x16 bf16 -> fp32, V^T read from LDS with the
 //         transposing read.
 // The loop is software pipelined inside each wave: while the MFMA unit
-// computes S for tile j+1, the VALU exponentiates tile j; while it computes
-// O += P V for tile j, the VALU takes the row max of tile j+1 and forms
-// S*c - m. Two such waves share each SIMD.
+// computes S for slice h+1, the VALU exponentiates slice h; while it computes
+// O += P V for slice h, the VALU takes the row max of slice h+1 and forms
+// S*c - m. The two waves of a SIMD interleave on top of that: one wave's VALU
+// work fills the other's MFMA time.
 // Epilogue ([PT2CUDA] step 4.1, one division per row at the end): O = O / l
 // (0 when l = 0), LSE = ln2 * (m + log2 l) (-inf when l = 0), bf16 store.
 //
@@ -77,8 +80,9 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr int kSlice = 32;     // keys per K/V slice (one LDS stage, one pipeline step)
 constexpr int kStages = 8;     // LDS ring depth in slices
-constexpr int kWaves = 4;      // wave64s per workgroup, one per SIMD
-constexpr int kRows = 64;      // query rows per wave: two 32-row MFMA blocks
+constexpr int kRB = 1;         // 32-row MFMA blocks (query rows / 32) per wave
+constexpr int kRows = 32 * kRB;           // query rows per wave
+constexpr int kWaves = 8 / kRB;           // wave64s per workgroup: 256 rows per workgroup
 constexpr int kBM = kRows * kWaves;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 units
@@ -90,10 +94,11 @@ struct Slice {
   static constexpr int kBytes = kSlice * kRowBytes;          // one K or V stage
   static constexpr int kLds = 2 * kStages * kBytes;          // K stages, then V stages
   static constexpr int kCopies = kBytes / 1024;              // 1 KB wave copies per stage
-  static constexpr int kCopiesPerWave = kCopies / kWaves;
+  static constexpr int kCopyWaves = kCopies < kWaves ? kCopies : kWaves;   // waves that copy
+  static constexpr int kCopiesPerWave = kCopies / kCopyWaves;
   static constexpr int kRowsPerCopy = 1024 / kRowBytes;
   static constexpr int kLanesPerRow = 64 / kRowsPerCopy;
-  static_assert(kCopies % kWaves == 0, "copies must split evenly over the waves");
+  static_assert(kCopies % kCopyWaves == 0, "copies must split evenly over the copying waves");
   static_assert(kLds <= 160 * 1024, "the stages must fit the 160 KB LDS of a CU");
 };
 
@@ -218,6 +223,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const uint32_t base_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
     const uint32_t base_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uintptr_t)base >> 32));
     const uint64_t sbase = ((uint64_t)base_hi << 32) | (uint64_t)base_lo;
+    if (wave >= T::kCopyWaves) return;
 #pragma unroll
     for (int q = 0; q < T::kCopiesPerWave; ++q) {
       uint32_t voff = (uint32_t)cp_off[q];
@@ -310,9 +316,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   if (causal) nh = min(nh, row_hi / kSlice + 1);
 
   // ---- Q rows -> VGPRs as the B operand of S^T = K Q^T ----
-  bf16x8 qreg[2][D / 16];
+  bf16x8 qreg[kRB][D / 16];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb) {
     const int row = row_lo + 32 * rb + (lane & 31);
     const uint32_t flip = neg_scale ? 0x80008000u : 0u;   // negative scale: negate Q exactly
 #pragma unroll
@@ -324,21 +330,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     }
   }
 
-  f32x16 o_acc[2][D / 32];
+  f32x16 o_acc[kRB][D / 32];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o_acc[rb][db] = (f32x16){};
-  float m_run[2] = {-INFINITY, -INFINITY};   // running max of S*c of the lane's row in block rb
-  float l_run[2] = {0.f, 0.f};               // partial running sum over this lane's half of the keys
-  float alpha[2] = {1.f, 1.f};               // pending rescale of o_acc[rb]
+  float m_run[kRB], l_run[kRB], alpha[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    m_run[rb] = -INFINITY;   // running max of S*c of the lane's row in block rb
+    l_run[rb] = 0.f;         // partial running sum over this lane's half of the keys
+    alpha[rb] = 1.f;         // pending rescale of o_acc[rb]
+  }
   bool o_stale = false;                      // some lane has alpha != 1 pending
 
   // Key j is allowed for row i iff j <= klim (klim folds the valid length, the
   // causal limit and the masked leading rows into one bound).
-  int klim[2];
+  int klim[kRB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb) {
     const int row = row_lo + 32 * rb + (lane & 31);
     klim[rb] = row < qs ? -1 : min(kv - 1, causal ? row : 0x7fffffff);
   }
@@ -347,9 +357,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const int k0 = h * kSlice;
     return (k0 + kSlice - 1 >= kv) || (causal && k0 + kSlice - 1 > row_lo) || (row_lo < qs);
   };
-  auto mask = [&](int h, f32x16 (&s)[2]) __attribute__((always_inline)) {
+  auto mask = [&](int h, f32x16 (&s)[kRB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
       const int lim = klim[rb] - h * kSlice - 4 * hf;   // key offset within the slice must be <= lim
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[rb][r] = (8 * (r >> 2) + (r & 3)) <= lim ? s[rb][r] : -INFINITY;
@@ -366,11 +376,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     for (int kc = 0; kc < D / 16; ++kc) ka[kc] = *(const lds_u32x4*)(kb + k_off[kc]);
   };
   // S^T = K Q^T for both row blocks, not interleaved (prologue only).
-  auto qk = [&](f32x16 (&s)[2]) __attribute__((always_inline)) {
+  auto qk = [&](f32x16 (&s)[kRB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < kRB; ++rb) {
         if (kc == 0) mfma_v_init(s[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
         else mfma_v(s[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
       }
@@ -380,9 +390,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // sub-steps (so they can be spread between MFMAs): partial maxes; the row max
   // and running-max update; the shift of elements 0..7; of elements 8..15. A slice that is not live
   // leaves the running state unchanged.
-  float part[2][3];
+  float part[kRB][2];
+  float negm[kRB];   // minus the exponent's subtrahend: -m_run, or 0 while m_run = -inf
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) negm[rb] = 0.f;
   bool grow_any = false;
-  auto rowmax_sub = [&](f32x16 (&s)[2], int rb, int sub, bool live) __attribute__((always_inline)) {
+  auto rowmax_sub = [&](f32x16 (&s)[kRB], int rb, int sub, bool live) __attribute__((always_inline)) {
     f32x16& x = s[rb];
     if (sub == 0) {   // partial maxes
       const float a0 = fmaxf(fmaxf(x[0], x[1]), x[2]), a1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
@@ -394,24 +407,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       const float mx = lane_swap_max(fmaxf(part[rb][0], part[rb][1]));
       const float tmax = live ? mx * c : -INFINITY;   // c > 0, so -inf stays -inf
       const bool grow = tmax > m_run[rb] + kTau;
-      const float m_new = grow ? tmax : m_run[rb];
-      const float a = grow ? __builtin_amdgcn_exp2f(m_run[rb] - m_new) : 1.f;   // m_run = -inf gives 0
-      l_run[rb] *= a;
-      alpha[rb] *= a;
-      m_run[rb] = m_new;
-      grow_any = grow_any || grow;
-      part[rb][2] = (m_new == -INFINITY) ? 0.f : -m_new;   // minus the exponent's subtrahend
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // rare once the running max has settled
+        const float m_new = grow ? tmax : m_run[rb];
+        const float a = grow ? __builtin_amdgcn_exp2f(m_run[rb] - m_new) : 1.f;   // m_run = -inf gives 0
+        l_run[rb] *= a;
+        alpha[rb] *= a;
+        m_run[rb] = m_new;
+        grow_any = true;
+        negm[rb] = (m_new == -INFINITY) ? 0.f : -m_new;
+      }
     } else {   // S*c - m for elements 0..7 (sub 2) or 8..15 (sub 3)
       const int r0 = 8 * (sub - 2);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) x[r0 + r] = fmaf(x[r0 + r], c, part[rb][2]);
+      for (int r = 0; r < 8; ++r) x[r0 + r] = fmaf(x[r0 + r], c, negm[rb]);
     }
   };
   // P = exp2(S*c - m) for elements e0 .. e0+n-1 of block rb: fp32 into the
   // row sum, bf16 pairs into the PV operand words.
-  uint32_t pbw[2][8];
-  float lsum[2];
-  auto expo_part = [&](const f32x16 (&s)[2], int rb, int e0, int n) __attribute__((always_inline)) {
+  uint32_t pbw[kRB][8];
+  float lsum[kRB];
+  auto expo_part = [&](const f32x16 (&s)[kRB], int rb, int e0, int n) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = e0; e < e0 + n; e += 2) {
       const float p0 = __builtin_amdgcn_exp2f(s[rb][e]);
@@ -447,49 +462,54 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // K(h-1) in step h-3. Copies are issued for every step, also past the last
   // slice (clamped rows), so the number in flight, and with it the wait
   // count, is the same each time: slices h+3 .. h+6 may still be in flight.
-  constexpr int kG = D / 8;             // MFMAs per phase
-  auto step = [&](auto hm, int h, f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
+  constexpr int kG = kRB * D / 16;      // MFMAs per phase
+  constexpr int kSub = 4 * kRB;         // row-max sub-steps per phase
+  auto step = [&](auto hm, int h, f32x16 (&sc)[kRB], f32x16 (&sn)[kRB]) __attribute__((always_inline)) {
     constexpr int Hm = decltype(hm)::value;   // h % kStages
     wait_copies<4 * kC>();
     __syncthreads();   // slices <= h+2 have landed; slice h-1's stage is no longer read
-    copy_slices(h + kStages - 1);
-    if (h >= nh) return;
+    if (h >= nh) {   // this wave's rows are done; it still copies its share
+      copy_slices(h + kStages - 1);
+      return;
+    }
     if (o_stale) {
       mfma_result_wait();
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o_acc[rb][db] *= alpha[rb];
-      alpha[0] = alpha[1] = 1.f;
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) alpha[rb] = 1.f;
       o_stale = false;
     }
     const bool nxt = h + 1 < nh;
     // ---- phase A ----
     {
       const char* vb = vst_rel(Hm);
-      lsum[0] = lsum[1] = 0.f;
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) lsum[rb] = 0.f;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int g = 0; g < kG; ++g) {
-        const int kc = g >> 1, rb = g & 1;
+        const int kc = g / kRB, rb = g % kRB;
         if (kc == 0) mfma_v_init(sn[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
         else mfma_v(sn[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
-        if ((g & 1) == 0) {   // V reads for PV group g/2, (cc, db) in PV order
-          const int pg = g >> 1;
+        if (g % kRB == 0) {   // V reads for PV group g/kRB, (cc, db) in PV order
+          const int pg = g / kRB;
           load_v_one(vb, pg / (D / 32), pg % (D / 32));
         }
-        constexpr int kPer = 32 / kG;   // exponentials per group
+        constexpr int kPer = 16 * kRB / kG;   // exponentials per group
         expo_part(sc, (g * kPer) / 16, (g * kPer) % 16, kPer);
         __builtin_amdgcn_sched_barrier(0);
       }
       // keep P and the sums in this phase (the compiler would otherwise sink
       // them past the mask branch, away from the MFMAs they overlap)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < kRB; ++rb)
         asm volatile("" :: "v"(pbw[rb][0]), "v"(pbw[rb][1]), "v"(pbw[rb][2]), "v"(pbw[rb][3]),
                      "v"(pbw[rb][4]), "v"(pbw[rb][5]), "v"(pbw[rb][6]), "v"(pbw[rb][7]), "v"(lsum[rb]));
-      l_run[0] += lsum[0];
-      l_run[1] += lsum[1];
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) l_run[rb] += lsum[rb];
     }
     mfma_result_wait();   // S of slice h+1 is read below
     if (nxt && need_mask(h + 1)) mask(h + 1, sn);
@@ -500,26 +520,30 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int g = 0; g < kG; ++g) {
-        const int pg = g >> 1, rb = g & 1;
+        const int pg = g / kRB, rb = g % kRB;
         const int cc = pg / (D / 32), db = pg % (D / 32);
         mfma_a(o_acc[rb][db], va[cc][db], pb(rb, cc));
         if (g < D / 16) ka[g] = *(const lds_u32x4*)(kb + k_off[g]);
-        // the eight row-max sub-steps (4 per block) spread over the groups
-        constexpr int kSubPer = 8 / kG > 0 ? 8 / kG : 1;
-        if (g * kSubPer < 8 || kG > 8) {
+        // the row-max sub-steps (4 per block) spread over the groups
+        constexpr int kSubPer = kSub / kG > 0 ? kSub / kG : 1;
+        if (g * kSubPer < kSub || kG > kSub) {
 #pragma unroll
           for (int u = 0; u < kSubPer; ++u) {
-            const int sub = (g * 8) / kG + u;
-            if (kG <= 8 || (g * 8) % kG == 0) rowmax_sub(sn, sub >> 2, sub & 3, nxt);
+            const int sub = (g * kSub) / kG + u;
+            if (kG <= kSub || (g * kSub) % kG == 0) rowmax_sub(sn, sub >> 2, sub & 3, nxt);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      o_stale = o_stale || __builtin_amdgcn_ballot_w64(grow_any) != 0;
+      o_stale = o_stale || grow_any;
     }
+    // The copies go last: the waves reach this point at different times, so
+    // the workgroup's copies reach the memory pipeline spread out rather than
+    // all at once after the barrier (the stage they fill was freed by it).
+    copy_slices(h + kStages - 1);
   };
 
-  f32x16 sa[2], sb[2];
+  f32x16 sa[kRB], sb[kRB];
   if (nh_wg > 0) {
     if (it > 0) __syncthreads();   // every wave is done reading the previous tile's stages
 #pragma unroll
@@ -532,8 +556,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       if (need_mask(0)) mask(0, sa);
       grow_any = false;
 #pragma unroll
-      for (int sub = 0; sub < 8; ++sub) rowmax_sub(sa, sub >> 2, sub & 3, true);
-      o_stale = o_stale || __builtin_amdgcn_ballot_w64(grow_any) != 0;
+      for (int sub = 0; sub < kSub; ++sub) rowmax_sub(sa, sub >> 2, sub & 3, true);
+      o_stale = o_stale || grow_any;
       load_k(std::integral_constant<int, 1>{});
     }
     static_assert(kStages == 8, "the loop below is unrolled over kStages slices");
@@ -559,14 +583,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   mfma_result_wait();   // the last P V MFMAs have written o_acc
   if (o_stale) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o_acc[rb][db] *= alpha[rb];
   }
 
   // ---- epilogue: O / l, LSE, bf16 store ----
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb) {
     const int row = row_lo + 32 * rb + (lane & 31);
     const float l_tot = lane_swap_add(l_run[rb]);
     if (row < N_q) {
