@@ -403,6 +403,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       const float a4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
       part[rb][0] = fmaxf(fmaxf(a0, a1), a2);
       part[rb][1] = fmaxf(fmaxf(a3, a4), x[15]);
+      // (the empty asm statements keep each piece of VALU work in the MFMA
+      // group it was placed in; the compiler would sink it to its first use)
+      asm volatile("" :: "v"(part[rb][0]), "v"(part[rb][1]));
     } else if (sub == 1) {   // row max across the lane pair, running-max update
       const float mx = lane_swap_max(fmaxf(part[rb][0], part[rb][1]));
       const float tmax = live ? mx * c : -INFINITY;   // c > 0, so -inf stays -inf
@@ -420,6 +423,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       const int r0 = 8 * (sub - 2);
 #pragma unroll
       for (int r = 0; r < 8; ++r) x[r0 + r] = fmaf(x[r0 + r], c, negm[rb]);
+      asm volatile("" :: "v"(x[r0 + 0]), "v"(x[r0 + 1]), "v"(x[r0 + 2]), "v"(x[r0 + 3]),
+                   "v"(x[r0 + 4]), "v"(x[r0 + 5]), "v"(x[r0 + 6]), "v"(x[r0 + 7]));
     }
   };
   // P = exp2(S*c - m) for elements e0 .. e0+n-1 of block rb: fp32 into the
@@ -433,6 +438,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       const float p1 = __builtin_amdgcn_exp2f(s[rb][e + 1]);
       lsum[rb] += p0 + p1;
       pbw[rb][e >> 1] = pack2(p0, p1);
+      asm volatile("" :: "v"(pbw[rb][e >> 1]), "v"(lsum[rb]));
     }
   };
   auto pb = [&](int rb, int cc) __attribute__((always_inline)) {
@@ -448,11 +454,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   };
 
   // Step h (slice h; S of slice h is in sc, already shifted):
-  //   wait for slices <= h+2, barrier, copy slice h+7 into slice h-1's stage;
+  //   wait for slices <= h+2, barrier (slice h-1's stage is now free);
   //   phase A: QK(h+1) on the MFMA unit (K(h+1) was read last phase) while the
   //            VALU exponentiates slice h and the LDS reads V(h);
+  //   copy this wave's share of K(h+7) into slice h-1's stage;
   //   phase B: PV(h) on the MFMA unit while the VALU takes the row max of
-  //            slice h+1 and forms S*c - m, and the LDS reads K(h+2).
+  //            slice h+1 and forms S*c - m, and the LDS reads K(h+2);
+  //   copy this wave's share of V(h+7).
   // Each phase is written as kG groups of one MFMA, a share of the LDS reads
   // and a share of the VALU work, fenced so the scheduler keeps that order:
   // every MFMA overlaps the VALU work that follows it.
@@ -511,6 +519,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) l_run[rb] += lsum[rb];
     }
+    // This wave's share of the K copy of slice h+7, into the stage the barrier
+    // freed. The copies go out between the phases and at the end of the step,
+    // where the waves arrive at different times, so the workgroup's copies
+    // reach the address unit spread out rather than all at once.
+    copy_slice(kg, (h + kStages - 1) * kSlice, kst((Hm + kStages - 1) % kStages));
     mfma_result_wait();   // S of slice h+1 is read below
     if (nxt && need_mask(h + 1)) mask(h + 1, sn);
     // ---- phase B ----
@@ -537,10 +550,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       }
       o_stale = o_stale || grow_any;
     }
-    // The copies go last: the waves reach this point at different times, so
-    // the workgroup's copies reach the memory pipeline spread out rather than
-    // all at once after the barrier (the stage they fill was freed by it).
-    copy_slices(h + kStages - 1);
+    copy_slice(vg, (h + kStages - 1) * kSlice, vst((Hm + kStages - 1) % kStages));   // the V share
   };
 
   f32x16 sa[kRB], sb[kRB];
