@@ -599,25 +599,41 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   }
 
   // ---- epilogue: O / l, LSE, bf16 store ----
+  // In the accumulator layout a lane holds 8-byte pieces of 32 different rows,
+  // so storing straight from it would touch 32 partial cache lines per store
+  // instruction. The wave instead writes its normalised rows into LDS (row
+  // stride 2*D + 16 bytes, which starts the rows of one write on different
+  // banks), reads them back as 16-byte pieces of whole rows, and stores
+  // kLanesPerORow lanes per row: each instruction writes complete rows.
+  constexpr int kORow = 2 * D + 16;
+  constexpr int kChunksPerRow = D / 8;                   // 16-byte pieces per row
+  static_assert(kWaves * kRows * kORow <= T::kLds, "the O staging area must fit in the stages");
+  __syncthreads();   // every wave is done with the K/V stages, which the staging area overlaps
+  char* ost = smem + wave * kRows * kORow;
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
-    const int row = row_lo + 32 * rb + (lane & 31);
+    const int r = 32 * rb + (lane & 31);
+    const int row = row_lo + r;
     const float l_tot = lane_swap_add(l_run[rb]);
-    if (row < N_q) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      uint16_t* orow = O + q_base + (size_t)row * D;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
+    for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const u32x2 w = {pack2(o_acc[rb][db][4 * g + 0] * inv, o_acc[rb][db][4 * g + 1] * inv),
-                           pack2(o_acc[rb][db][4 * g + 2] * inv, o_acc[rb][db][4 * g + 3] * inv)};
-          *(u32x2*)(orow + 32 * db + 8 * g + 4 * hf) = w;
-        }
+      for (int g = 0; g < 4; ++g) {
+        const u32x2 w = {pack2(o_acc[rb][db][4 * g + 0] * inv, o_acc[rb][db][4 * g + 1] * inv),
+                         pack2(o_acc[rb][db][4 * g + 2] * inv, o_acc[rb][db][4 * g + 3] * inv)};
+        *(__attribute__((address_space(3))) u32x2*)(ost + r * kORow + 2 * (32 * db + 8 * g + 4 * hf)) = w;
       }
-      if (LSE && lane < 32)
-        LSE[(size_t)bh * N_q + row] = l_tot > 0.f ? (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     }
+    if (LSE && lane < 32 && row < N_q)
+      LSE[(size_t)bh * N_q + row] = l_tot > 0.f ? (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+  }
+#pragma unroll
+  for (int i = 0; i < kRows * kChunksPerRow / 64; ++i) {
+    const int ci = 64 * i + lane;
+    const int r = ci / kChunksPerRow, ch = ci % kChunksPerRow;
+    const u32x4 x = *(const __attribute__((address_space(3))) u32x4*)(ost + r * kORow + 16 * ch);
+    if (row_lo + r < N_q) *(u32x4*)(O + q_base + (size_t)(row_lo + r) * D + 8 * ch) = x;
   }
   }   // tiles of the pair
 }
