@@ -102,15 +102,23 @@ struct Slice {
   static_assert(kLds <= 160 * 1024, "the stages must fit the 160 KB LDS of a CU");
 };
 
-// Chunk position of 16-byte chunk c of row r is c ^ swz(r). For D = 128 a row
-// is 256 bytes (one sweep of the banks): 16 consecutive rows get 16 distinct
-// swizzles, and 4 consecutive rows x 2 adjacent chunks stay distinct too. For
-// D = 64 two rows share a sweep, so row bit 0 picks the half and bits 1-3 the
-// swizzle.
+// Chunk position of 16-byte chunk c of row r is c ^ swz(r). The banks sweep
+// 256 bytes. Two read patterns must stay conflict-free:
+//   K (ds_read_b128): 16 consecutive rows read the same logical chunk, so the
+//     16 rows must land on 16 distinct chunk positions of a sweep;
+//   V (ds_read_b64_tr_b16): each half-wave reads an aligned 64-byte group
+//     (4 chunks) of 4 consecutive rows 4a..4a+3, so those 4 rows must land on
+//     4 distinct 64-byte groups of a sweep.
+// D = 128 (one row per sweep): swz = (r%4)*4 + (r/4)%4; bits 2-3 separate the
+// 4 rows of a V group, and all 4 bits together separate 16 rows.
+// D = 64 (two rows per sweep, row bit 0 picks the half): swz = bit 2 from
+// row bit 1, bits 0-1 from row bits 2-3; within a half the 8 rows of the
+// same parity get distinct swizzles, and rows 4a, 4a+2 (and 4a+1, 4a+3) differ
+// in bit 2, the 64-byte group bit.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
-  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -262,11 +270,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // (L%16)/4, columns 32*db + 16*(g%2) + 4*(L%4) .. +3. After the transpose,
   // lane L holds column 32*db + L%32 of keys 16*cc + 8*hi + 4*(L/32) + 0..3,
   // which pairs with P's registers 8*cc + 4*hi + 0..3. Its offset is
-  // v_off0 ^ (hi*(8*kRowBytes + 16)) ^ (64*db) (row +8 flips swizzle bit 0),
-  // plus 16*cc rows as an immediate.
+  // v_off0 (hi = 0) or v_off1 (hi = 1, row + 8), XORed with 64*db, plus 16*cc
+  // rows as an immediate (the swizzle repeats every 16 rows).
   // Every base these are added to is a multiple of 16 rows, so base + (off ^ x)
   // == (base + off) ^ x and the bases stay immediate offsets.
-  int k_off0, v_off0;
+  int k_off0, v_off0, v_off1;
   {
     const int r = lane & 31;
     k_off0 = r * T::kRowBytes + ((hf ^ swz<D>(r)) << 4);
@@ -274,6 +282,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const int rv = 4 * hf + ((lane & 15) >> 2);
     const int byte = 32 * (g & 1) + 8 * (lane & 3);
     v_off0 = rv * T::kRowBytes + (((byte >> 4) ^ swz<D>(rv)) << 4) + (byte & 15);
+    v_off1 = (rv + 8) * T::kRowBytes + (((byte >> 4) ^ swz<D>(rv + 8)) << 4) + (byte & 15);
   }
   // All operand offsets, kept in registers. The V stages start at
   // kStages * kBytes (64 KB for d = 128), more than a DS immediate holds, so
@@ -286,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
     v_off[0][db] = (v_off0 ^ (64 * db)) + kVBase;
-    v_off[1][db] = (v_off0 ^ (64 * db) ^ (8 * T::kRowBytes + 16)) + kVBase;
+    v_off[1][db] = (v_off1 ^ (64 * db)) + kVBase;
   }
 
   // A workgroup owns the pair of query tiles (n_qt-1-pr, pr): under a causal
