@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 from oracle import attention, bf16_bits_to_f64, check
-from workloads import WORKLOADS, Workload, make_inputs, make_random
+from workloads import WORKLOADS, Workload, make_inputs, make_random, make_rising
 
 pytestmark = pytest.mark.gpu
 
@@ -131,6 +131,17 @@ def test_large_logits_rescaling():
     q, k, v = make_random(1, 2, 512, 512, 128, seed=17, sigma=(4.0, 1.0, 1.0))
     compare_full(q, k, v, np.float32(128 ** -0.5), True)
     compare_full(q, k, v, np.float32(128 ** -0.5), False)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_running_max_rises_block_after_block(d, causal):
+    # Scores drift linearly along the keys: about half the rows of every wave
+    # find a new maximum, several units above the old one, in nearly every
+    # block of keys, so the running maximum is raised (and l and O rescaled)
+    # many times per row while the other rows keep theirs.
+    q, k, v = make_rising(1, 2, 300, 700, d, seed=29, step=0.5)
+    compare_full(q, k, v, np.float32(d ** -0.5), causal)
 
 
 def test_no_keys():

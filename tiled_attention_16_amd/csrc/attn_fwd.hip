@@ -29,17 +29,21 @@
 // [MEMWALL] §3.2, in the exp2 domain with c = |scale| * log2(e)):
 //   S^T = K Q^T on MFMA 32x32x16 bf16 -> fp32. Computing the transpose puts one
 //         query row in each lane (16 keys per lane, the other 16 keys of the
-//         slice in lane ^ 32): the row max is an in-register max plus one
+//         slice in lane ^ 32): a row max is an in-register max plus one
 //         permlane32 swap, and the row sum needs no cross-lane step until the
 //         very end.
 //   mask  only on slices that cross the causal diagonal, the valid key length
 //         or the masked leading rows: the score becomes -inf.
-//   m     running max of S*c per row. It is raised only when the slice's max
-//         exceeds it by more than kTau; otherwise the stale max stays the
-//         exponent's subtrahend. O / l does not depend on the subtrahend, so
-//         this is the pages' recurrence in exact arithmetic; the exponentials
-//         stay below 2^kTau. When m rises, l and O are scaled by
-//         alpha = exp2(m_old - m_new) (O lazily, before the next P V).
+//   m     the exponent's subtrahend per row. The first slice sets it to that
+//         slice's row max. After that it is a stale running max: it is raised
+//         only when a lane's 16 exponentials of a slice add up to more than
+//         kSumCap (2^8), and then to the slice's row max, with l and O scaled
+//         by exp2(m_old - m_new) and the slice's exponentials redone. The sum
+//         bounds every term, so the exponentials stay below 2^8 without
+//         taking a row max per slice. O / l does not depend on the subtrahend,
+//         so this is the pages' recurrence in exact arithmetic. Key 0 is
+//         allowed for every row that has any allowed key, so a row whose m is
+//         still -inf after the first slice has no allowed key at all.
 //   P     = exp2(S*c - m) in fp32, summed into l in fp32, then rounded to bf16.
 //         Its accumulator layout is already the B operand layout of the next
 //         MFMA, so P never leaves registers.
@@ -47,9 +51,9 @@
 //         transposing read.
 // The loop is software pipelined inside each wave: while the MFMA unit
 // computes S for slice h+1, the VALU exponentiates slice h; while it computes
-// O += P V for slice h, the VALU takes the row max of slice h+1 and forms
-// S*c - m. The two waves of a SIMD interleave on top of that: one wave's VALU
-// work fills the other's MFMA time.
+// O += P V for slice h, the VALU forms S*c - m of slice h+1. The two waves of
+// a SIMD interleave on top of that: one wave's VALU work fills the other's
+// MFMA time.
 // Epilogue ([PT2CUDA] step 4.1, one division per row at the end): O = O / l
 // (0 when l = 0), LSE = ln2 * (m + log2 l) (-inf when l = 0), bf16 store.
 //
@@ -85,7 +89,7 @@ constexpr int kRows = 32 * kRB;           // query rows per wave
 constexpr int kWaves = 8 / kRB;           // wave64s per workgroup: 256 rows per workgroup
 constexpr int kBM = kRows * kWaves;
 constexpr int kThreads = 64 * kWaves;
-constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 units
+constexpr float kSumCap = 256.f;   // bound on a lane's 16 exponentials of one slice (2^8)
 constexpr float kLn2 = 0.69314718055994530942f;
 
 template <int D>
@@ -344,14 +348,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o_acc[rb][db] = (f32x16){};
-  float m_run[kRB], l_run[kRB], alpha[kRB];
+  float m_run[kRB], l_run[kRB];
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
-    m_run[rb] = -INFINITY;   // running max of S*c of the lane's row in block rb
+    m_run[rb] = -INFINITY;   // the exponent's subtrahend for the lane's row in block rb
     l_run[rb] = 0.f;         // partial running sum over this lane's half of the keys
-    alpha[rb] = 1.f;         // pending rescale of o_acc[rb]
   }
-  bool o_stale = false;                      // some lane has alpha != 1 pending
 
   // Key j is allowed for row i iff j <= klim (klim folds the valid length, the
   // causal limit and the masked leading rows into one bound).
@@ -395,45 +397,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       }
     mfma_result_wait();
   };
-  // Row max of block rb, running-max update, and S <- S*c - m, in four
-  // sub-steps (so they can be spread between MFMAs): partial maxes; the row max
-  // and running-max update; the shift of elements 0..7; of elements 8..15. A slice that is not live
-  // leaves the running state unchanged.
-  float part[kRB][2];
   float negm[kRB];   // minus the exponent's subtrahend: -m_run, or 0 while m_run = -inf
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) negm[rb] = 0.f;
-  bool grow_any = false;
-  auto rowmax_sub = [&](f32x16 (&s)[kRB], int rb, int sub, bool live) __attribute__((always_inline)) {
-    f32x16& x = s[rb];
-    if (sub == 0) {   // partial maxes
-      const float a0 = fmaxf(fmaxf(x[0], x[1]), x[2]), a1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
-      const float a2 = fmaxf(fmaxf(x[6], x[7]), x[8]), a3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
-      const float a4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
-      part[rb][0] = fmaxf(fmaxf(a0, a1), a2);
-      part[rb][1] = fmaxf(fmaxf(a3, a4), x[15]);
-      // (the empty asm statements keep each piece of VALU work in the MFMA
-      // group it was placed in; the compiler would sink it to its first use)
-      asm volatile("" :: "v"(part[rb][0]), "v"(part[rb][1]));
-    } else if (sub == 1) {   // row max across the lane pair, running-max update
-      const float mx = lane_swap_max(fmaxf(part[rb][0], part[rb][1]));
-      const float tmax = live ? mx * c : -INFINITY;   // c > 0, so -inf stays -inf
-      const bool grow = tmax > m_run[rb] + kTau;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // rare once the running max has settled
-        const float m_new = grow ? tmax : m_run[rb];
-        const float a = grow ? __builtin_amdgcn_exp2f(m_run[rb] - m_new) : 1.f;   // m_run = -inf gives 0
-        l_run[rb] *= a;
-        alpha[rb] *= a;
-        m_run[rb] = m_new;
-        grow_any = true;
-        negm[rb] = (m_new == -INFINITY) ? 0.f : -m_new;
-      }
-    } else {   // S*c - m for elements 0..7 (sub 2) or 8..15 (sub 3)
-      const int r0 = 8 * (sub - 2);
+  // First slice of a tile: m = the slice's row max of S*c (-inf for a row with
+  // no allowed key in it), then S <- S*c - m.
+  auto first_max = [&](f32x16 (&s)[kRB]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) x[r0 + r] = fmaf(x[r0 + r], c, negm[rb]);
-      asm volatile("" :: "v"(x[r0 + 0]), "v"(x[r0 + 1]), "v"(x[r0 + 2]), "v"(x[r0 + 3]),
-                   "v"(x[r0 + 4]), "v"(x[r0 + 5]), "v"(x[r0 + 6]), "v"(x[r0 + 7]));
+    for (int rb = 0; rb < kRB; ++rb) {
+      f32x16& x = s[rb];
+      float mx = x[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+      const float tmax = lane_swap_max(mx) * c;   // c > 0, so -inf stays -inf
+      m_run[rb] = tmax;
+      negm[rb] = (tmax == -INFINITY) ? 0.f : -tmax;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = fmaf(x[r], c, negm[rb]);
     }
   };
   // P = exp2(S*c - m) for elements e0 .. e0+n-1 of block rb: fp32 into the
@@ -448,6 +428,46 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       lsum[rb] += p0 + p1;
       pbw[rb][e >> 1] = pack2(p0, p1);
       asm volatile("" :: "v"(pbw[rb][e >> 1]), "v"(lsum[rb]));
+    }
+  };
+  // S <- S*c - m for elements e0 .. e0+n-1 of block rb.
+  auto shift_part = [&](f32x16 (&s)[kRB], int rb, int e0, int n) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = e0; e < e0 + n; ++e) s[rb][e] = fmaf(s[rb][e], c, negm[rb]);
+#pragma unroll
+    for (int e = e0; e < e0 + n; e += 2) asm volatile("" :: "v"(s[rb][e]), "v"(s[rb][e + 1]));
+  };
+  // Some lane's exponentials of the slice in s (already shifted by the current
+  // m) add up to more than kSumCap: raise m to the slice's row max where that
+  // max is above m, rescale l and O by exp2(m_old - m_new), and redo the
+  // slice's exponentials. Rows whose max is not above m keep everything
+  // (their shift d is 0). A row with no allowed key so far has m = -inf and
+  // only -inf scores, so its d is 0 as well.
+  auto raise_max = [&](f32x16 (&s)[kRB]) __attribute__((always_inline)) {
+    mfma_result_wait();   // o_acc is rescaled below
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      f32x16& x = s[rb];
+      float mx = x[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+      mx = lane_swap_max(mx);                  // row max of S*c - m over the slice
+      const float d = mx > 0.f ? mx : 0.f;     // 0 for -inf and NaN too
+      const float a = __builtin_amdgcn_exp2f(-d);
+      m_run[rb] += d;
+      negm[rb] = (m_run[rb] == -INFINITY) ? 0.f : -m_run[rb];
+      l_run[rb] *= a;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o_acc[rb][db] *= a;
+      float sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(x[e] - d);
+        const float p1 = __builtin_amdgcn_exp2f(x[e + 1] - d);
+        sum += p0 + p1;
+        pbw[rb][e >> 1] = pack2(p0, p1);
+      }
+      lsum[rb] = sum;
     }
   };
   auto pb = [&](int rb, int cc) __attribute__((always_inline)) {
@@ -467,8 +487,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   //   phase A: QK(h+1) on the MFMA unit (K(h+1) was read last phase) while the
   //            VALU exponentiates slice h and the LDS reads V(h);
   //   copy this wave's share of K(h+7) into slice h-1's stage;
-  //   phase B: PV(h) on the MFMA unit while the VALU takes the row max of
-  //            slice h+1 and forms S*c - m, and the LDS reads K(h+2);
+  //   check the exponential sums of slice h against kSumCap (rarely: raise m);
+  //   phase B: PV(h) on the MFMA unit while the VALU forms S*c - m of slice
+  //            h+1, and the LDS reads K(h+2);
   //   copy this wave's share of V(h+7).
   // Each phase is written as kG groups of one MFMA, a share of the LDS reads
   // and a share of the VALU work, fenced so the scheduler keeps that order:
@@ -480,7 +501,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // slice (clamped rows), so the number in flight, and with it the wait
   // count, is the same each time: slices h+3 .. h+6 may still be in flight.
   constexpr int kG = kRB * D / 16;      // MFMAs per phase
-  constexpr int kSub = 4 * kRB;         // row-max sub-steps per phase
   auto step = [&](auto hm, int h, f32x16 (&sc)[kRB], f32x16 (&sn)[kRB]) __attribute__((always_inline)) {
     constexpr int Hm = decltype(hm)::value;   // h % kStages
     wait_copies<4 * kC>();
@@ -488,16 +508,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     if (h >= nh) {   // this wave's rows are done; it still copies its share
       copy_slices(h + kStages - 1);
       return;
-    }
-    if (o_stale) {
-      mfma_result_wait();
-#pragma unroll
-      for (int rb = 0; rb < kRB; ++rb)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o_acc[rb][db] *= alpha[rb];
-#pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) alpha[rb] = 1.f;
-      o_stale = false;
     }
     const bool nxt = h + 1 < nh;
     // ---- phase A ----
@@ -525,6 +535,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       for (int rb = 0; rb < kRB; ++rb)
         asm volatile("" :: "v"(pbw[rb][0]), "v"(pbw[rb][1]), "v"(pbw[rb][2]), "v"(pbw[rb][3]),
                      "v"(pbw[rb][4]), "v"(pbw[rb][5]), "v"(pbw[rb][6]), "v"(pbw[rb][7]), "v"(lsum[rb]));
+      bool over = false;
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) over = over || !(lsum[rb] <= kSumCap);   // NaN counts as over
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(over) != 0, 0)) raise_max(sc);
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) l_run[rb] += lsum[rb];
     }
@@ -538,7 +552,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     // ---- phase B ----
     {
       const char* kb = kst((Hm + 2) % kStages);
-      grow_any = false;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int g = 0; g < kG; ++g) {
@@ -546,18 +559,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
         const int cc = pg / (D / 32), db = pg % (D / 32);
         mfma_a(o_acc[rb][db], va[cc][db], pb(rb, cc));
         if (g < D / 16) ka[g] = *(const lds_u32x4*)(kb + k_off[g]);
-        // the row-max sub-steps (4 per block) spread over the groups
-        constexpr int kSubPer = kSub / kG > 0 ? kSub / kG : 1;
-        if (g * kSubPer < kSub || kG > kSub) {
-#pragma unroll
-          for (int u = 0; u < kSubPer; ++u) {
-            const int sub = (g * kSub) / kG + u;
-            if (kG <= kSub || (g * kSub) % kG == 0) rowmax_sub(sn, sub >> 2, sub & 3, nxt);
-          }
-        }
+        // the shift S*c - m of slice h+1, 16 elements per block, spread over the groups
+        constexpr int kShPer = 16 * kRB / kG;   // elements per group
+        shift_part(sn, (g * kShPer) / 16, (g * kShPer) % 16, kShPer);
         __builtin_amdgcn_sched_barrier(0);
       }
-      o_stale = o_stale || grow_any;
     }
     copy_slice(vg, (h + kStages - 1) * kSlice, vst((Hm + kStages - 1) % kStages));   // the V share
   };
@@ -573,10 +579,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       load_k(std::integral_constant<int, 0>{});
       qk(sa);
       if (need_mask(0)) mask(0, sa);
-      grow_any = false;
-#pragma unroll
-      for (int sub = 0; sub < kSub; ++sub) rowmax_sub(sa, sub >> 2, sub & 3, true);
-      o_stale = o_stale || grow_any;
+      first_max(sa);
       load_k(std::integral_constant<int, 1>{});
     }
     static_assert(kStages == 8, "the loop below is unrolled over kStages slices");
@@ -600,12 +603,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     wait_copies<0>();   // no copy may still be writing LDS when the next tile (or wave) starts
   }
   mfma_result_wait();   // the last P V MFMAs have written o_acc
-  if (o_stale) {
-#pragma unroll
-    for (int rb = 0; rb < kRB; ++rb)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) o_acc[rb][db] *= alpha[rb];
-  }
 
   // ---- epilogue: O / l, LSE, bf16 store ----
   // In the accumulator layout a lane holds 8-byte pieces of 32 different rows,

@@ -128,3 +128,22 @@ def make_random(B: int, H: int, N_q: int, N_k: int, d: int, seed: int, sigma=(1.
     k = f32_to_bf16_bits(g.standard_normal((B, H, N_k, d), dtype=np.float32) * np.float32(sigma[1]))
     v = f32_to_bf16_bits(g.standard_normal((B, H, N_k, d), dtype=np.float32) * np.float32(sigma[2]))
     return q, k, v
+
+
+def make_rising(B: int, H: int, N_q: int, N_k: int, d: int, seed: int, step: float = 0.5):
+    """Seeded bf16 Q, K, V bits whose scores drift along the key axis.
+
+    K row j is j*step times one fixed unit direction u plus N(0, 1) noise, so the
+    score of query row i against key j grows (or shrinks) linearly in j with slope
+    step * (q_i . u): rows with q_i . u > 0 see a new maximum in nearly every
+    block of keys, the others keep the maximum of their first keys.
+    """
+    g = np.random.Generator(np.random.PCG64(seed))
+    q = g.standard_normal((B, H, N_q, d), dtype=np.float32)
+    u = g.standard_normal(d).astype(np.float32)
+    u /= np.float32(np.linalg.norm(u))
+    ramp = (np.arange(N_k, dtype=np.float32) * np.float32(step))[:, None] * u[None, :]
+    k = g.standard_normal((B, H, N_k, d), dtype=np.float32) + ramp[None, None]
+    v = g.standard_normal((B, H, N_k, d), dtype=np.float32)
+    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
