@@ -222,34 +222,43 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const int r = cp_row(q);
     cp_off[q] = r * T::kRowBytes + (((lane % T::kLanesPerRow) ^ swz<D>(r)) << 4);
   }
-  // Copy the kSlice rows starting at key k0 of a head's K or V into stage dst.
+  // Copy slice sl (keys kSlice*sl ..) of a head's K or V into stage dst.
   // Rows at or past kv are never read: those lanes fetch the clamped last valid
   // row, whose data the mask ignores (or multiplies by a zero probability).
-  auto copy_slice = [&](const char* src, int k0, const char* dst) __attribute__((always_inline)) {
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)dst +
-                          wave * T::kCopiesPerWave * 1024;
-    const bool ragged = k0 + kSlice > kv;
-    const char* base = ragged ? src : src + (ptrdiff_t)k0 * T::kRowBytes;
-    // (readfirstlane returns a signed int: widen through uint32_t so the low
-    // half is zero-extended, never sign-extended into the high half)
-    const uint32_t base_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
-    const uint32_t base_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uintptr_t)base >> 32));
-    const uint64_t sbase = ((uint64_t)base_hi << 32) | (uint64_t)base_lo;
-    if (wave >= T::kCopyWaves) return;
+  // Slices from sl_rag on reach past kv; before it every row is a valid key
+  // and the copy is one scalar address plus the fixed lane offsets.
+  const int sl_rag = kv / kSlice;
+  const uint32_t lds_wave = (uint32_t)(wave * T::kCopiesPerWave * 1024);
+  auto issue_copy = [&](uint64_t sbase, uint32_t voff, uint32_t lds) __attribute__((always_inline)) {
+    // The copy is issued as inline assembly so that the compiler does not
+    // treat it as a pending write to every LDS address (it would then wait
+    // for it before each LDS read); completion is awaited explicitly with
+    // wait_copies() before the barrier that publishes the slice.
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+  };
+  // (readfirstlane returns a signed int: widen through uint32_t so the low
+  // half is zero-extended, never sign-extended into the high half)
+  auto sgpr64 = [&](const char* p) __attribute__((always_inline)) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uintptr_t)p >> 32));
+    return ((uint64_t)hi << 32) | (uint64_t)lo;
+  };
+  auto copy_slice = [&](const char* src, int sl, const char* dst) __attribute__((always_inline)) {
+    if (T::kCopyWaves < kWaves && wave >= T::kCopyWaves) return;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)dst + lds_wave;
+    if (__builtin_expect(sl < sl_rag, 1)) {
+      const uint64_t sbase = sgpr64(src) + (uint64_t)(uint32_t)sl * (uint64_t)T::kBytes;
 #pragma unroll
-    for (int q = 0; q < T::kCopiesPerWave; ++q) {
-      uint32_t voff = (uint32_t)cp_off[q];
-      if (ragged) {
+      for (int q = 0; q < T::kCopiesPerWave; ++q) issue_copy(sbase, (uint32_t)cp_off[q], lds0 + q * 1024);
+    } else {
+      const int k0 = sl * kSlice;
+#pragma unroll
+      for (int q = 0; q < T::kCopiesPerWave; ++q) {
         const int key = min(k0 + cp_row(q), kv - 1);
-        voff += (uint32_t)((key - cp_row(q)) * T::kRowBytes);
+        const uint32_t voff = (uint32_t)cp_off[q] + (uint32_t)((key - cp_row(q)) * T::kRowBytes);
+        issue_copy(sgpr64(src), voff, lds0 + q * 1024);
       }
-      // The copy is issued as inline assembly so that the compiler does not
-      // treat it as a pending write to every LDS address (it would then wait
-      // for it before each LDS read); completion is awaited explicitly with
-      // wait_copies() before the barrier that publishes the slice.
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                   :: "s"(__builtin_amdgcn_readfirstlane(lds0 + q * 1024)), "v"(voff), "s"(sbase)
-                   : "memory", "m0");
     }
   };
   // Slice s lives in stage s % kStages: K rows at kst(st), V rows at vst(st).
@@ -260,8 +269,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   constexpr int kC = 2 * T::kCopiesPerWave;   // copies per wave per K+V slice
   auto copy_slices = [&](int s) __attribute__((always_inline)) {
     const int st = s & (kStages - 1);
-    copy_slice(kg, s * kSlice, kst(st));
-    copy_slice(vg, s * kSlice, vst(st));
+    copy_slice(kg, s, kst(st));
+    copy_slice(vg, s, vst(st));
   };
 
   // ---- per-lane LDS offsets of the MFMA operand reads ----
@@ -363,11 +372,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const int row = row_lo + 32 * rb + (lane & 31);
     klim[rb] = row < qs ? -1 : min(kv - 1, causal ? row : 0x7fffffff);
   }
-  // masking is needed only where slice h crosses that bound for some row
-  auto need_mask = [&](int h) __attribute__((always_inline)) {
-    const int k0 = h * kSlice;
-    return (k0 + kSlice - 1 >= kv) || (causal && k0 + kSlice - 1 > row_lo) || (row_lo < qs);
-  };
+  // Masking is needed only where slice h crosses that bound for some row of
+  // the wave: from the slice holding key kv-1 on (the first h with
+  // kSlice*h + kSlice-1 >= kv), from the slice past the wave's first row's
+  // diagonal on under a causal mask, and everywhere when masked leading rows
+  // are in the wave.
+  int mask_from = kv / kSlice;
+  if (causal) mask_from = min(mask_from, (row_lo + 1) / kSlice);
+  if (row_lo < qs) mask_from = 0;
+  mask_from = __builtin_amdgcn_readfirstlane(mask_from);
+  auto need_mask = [&](int h) __attribute__((always_inline)) { return h >= mask_from; };
   auto mask = [&](int h, f32x16 (&s)[kRB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
@@ -546,7 +560,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     // freed. The copies go out between the phases and at the end of the step,
     // where the waves arrive at different times, so the workgroup's copies
     // reach the address unit spread out rather than all at once.
-    copy_slice(kg, (h + kStages - 1) * kSlice, kst((Hm + kStages - 1) % kStages));
+    copy_slice(kg, h + kStages - 1, kst((Hm + kStages - 1) % kStages));
     mfma_result_wait();   // S of slice h+1 is read below
     if (nxt && need_mask(h + 1)) mask(h + 1, sn);
     // ---- phase B ----
@@ -565,7 +579,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    copy_slice(vg, (h + kStages - 1) * kSlice, vst((Hm + kStages - 1) % kStages));   // the V share
+    copy_slice(vg, h + kStages - 1, vst((Hm + kStages - 1) % kStages));   // the V share
   };
 
   f32x16 sa[kRB], sb[kRB];
