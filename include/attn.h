@@ -66,7 +66,9 @@ typedef enum {
  *              fully masked rows included).
  *   lse        float32 [B, H, N_q] or NULL; when given, written in full.
  *   B, H       batch and head counts (>= 0).
- *   N_q, N_k   query and key sequence lengths (>= 0).
+ *   N_q, N_k   query and key sequence lengths (>= 0); one head's K (or V),
+ *              N_k * d * 2 bytes, must stay below 2^31 bytes (8M keys at
+ *              d = 128), else ATTN_ERR_SHAPE.
  *   d          head dimension: 64 or 128.
  *   scale      multiplier of Q K^T, any finite value (the usual d^-0.5 of
  *              [PT2CUDA] step 1).

@@ -72,6 +72,7 @@ def call(**kw):
     (dict(o=A16 + 16), ta.ATTN_ERR_ALIAS),          # o overlaps q (2*8*64*2 bytes long)
     (dict(lse=A16 * 4 + 64), ta.ATTN_ERR_ALIAS),    # lse inside o
     (dict(B=1 << 20, H=1 << 12, N_q=1 << 12), ta.ATTN_ERR_SHAPE),   # too many workgroups
+    (dict(N_k=1 << 23, d=128), ta.ATTN_ERR_SHAPE),   # one head's K spans 2 GB
 ])
 def test_argument_errors_return_before_any_hip_call(lib, kw, status):
     assert call(**kw) == status

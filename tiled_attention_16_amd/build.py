@@ -25,15 +25,34 @@ HIPCC_FLAGS = [
 
 
 def build_library(verbose: bool = False) -> str:
-    """Build ``libattn.so`` next to this file; return its path. Raises on failure."""
+    """Build ``libattn.so`` next to this file; return its path. Raises on failure.
+
+    The device code is also compiled to assembly with the same flags and
+    checked by ``hazards.check`` (MFMA operand written by a VALU instruction
+    too close before the MFMA); a violation fails the build.
+    """
+    from .hazards import check
+
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(REPO_DIR, "include"), SRC, "-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    if verbose and res.stderr:
-        sys.stderr.write(res.stderr)
+    asm = LIB + ".s.tmp"
+    inc = ["-I", os.path.join(REPO_DIR, "include")]
+    cmd = [hipcc, *HIPCC_FLAGS, *inc, SRC, "-o", tmp]
+    flags_s = [f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
+    cmd_s = [hipcc, *flags_s, *inc, "--cuda-device-only", "-S", SRC, "-o", asm]
+    procs = [subprocess.Popen(c, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True) for c in (cmd, cmd_s)]
+    outs = [p.communicate() for p in procs]
+    for c, p, (out, err) in zip((cmd, cmd_s), procs, outs):
+        if p.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({p.returncode}):\n{' '.join(c)}\n{out}\n{err}")
+    if verbose and outs[0][1]:
+        sys.stderr.write(outs[0][1])
+    with open(asm) as f:
+        problems = check(f.read())
+    os.remove(asm)
+    if problems:
+        os.remove(tmp)
+        raise RuntimeError("MFMA hazard in the compiled kernel:\n" + "\n".join(problems))
     os.replace(tmp, LIB)
     return LIB
 

@@ -78,6 +78,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -145,24 +146,27 @@ __device__ __forceinline__ float lane_swap_add(float x) {
 }
 
 // MFMA 32x32x16 bf16 -> fp32, issued as inline assembly so that each
-// accumulator's register class is fixed: scores in VGPRs (the VALU reads
-// them), the output accumulator and Q in AGPRs (in the loop only MFMAs touch
-// them).
+// operand's register class is fixed: the scores and the output accumulator
+// in VGPRs (the VALU reads them), the K, V and Q operands in AGPRs.
 // The compiler does not know these are MFMAs, so the code itself places the
 // wait states an MFMA result needs before anything else reads it
-// (mfma_result_wait), and keeps VALU writes of MFMA inputs far from the MFMA.
-// (scores: A from VGPRs, B = Q from AGPRs, where Q stays for the whole tile)
-// Each begins with 3 wait states: the compiler may materialise an operand
-// with a VALU or v_accvgpr_write move right before, and an MFMA must not read
-// a register in the 2 wait states after such a write.
+// (mfma_result_wait). An MFMA must also not read a register in the 2 wait
+// states after a VALU write of it: the Pad forms begin with those wait states
+// (used where the compiler materialises operands, in the prologue); in the
+// loop no VALU instruction writes an MFMA operand, which the build verifies
+// on the compiled code (tiled_attention_16_amd/hazards.py).
+template <bool Pad>
 __device__ __forceinline__ void mfma_v_init(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "a"(a), "a"(b));
+  if constexpr (Pad) asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "a"(a), "a"(b));
+  else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "a"(a), "a"(b));
 }
+template <bool Pad>
 __device__ __forceinline__ void mfma_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "a"(a), "a"(b));
+  if constexpr (Pad) asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "a"(a), "a"(b));
+  else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "a"(a), "a"(b));
 }
 __device__ __forceinline__ void mfma_a(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "a"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "a"(a), "v"(b));
 }
 // 24 wait states: more than a 32x32 MFMA result needs before another
 // instruction may read it.
@@ -222,21 +226,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const int r = cp_row(q);
     cp_off[q] = r * T::kRowBytes + (((lane % T::kLanesPerRow) ^ swz<D>(r)) << 4);
   }
-  // Copy slice sl (keys kSlice*sl ..) of a head's K or V into stage dst.
-  // Rows at or past kv are never read: those lanes fetch the clamped last valid
-  // row, whose data the mask ignores (or multiplies by a zero probability).
-  // Slices from sl_rag on reach past kv; before it every row is a valid key
-  // and the copy is one scalar address plus the fixed lane offsets.
-  const int sl_rag = kv / kSlice;
+  // Copy slice sl (keys kSlice*sl ..) of a head's K or V into stage dst, with
+  // buffer_load_dwordx4 ... lds through a raw buffer descriptor that covers
+  // the head's kv valid keys: lanes whose row is at or past kv fall outside
+  // num_records and bring no data (such rows are never used: the mask drops
+  // their scores and their probabilities are 0). The byte offset of a lane is
+  // sl * kBytes + its fixed in-slice offset, so the head's K (or V) must span
+  // less than 2 GB, which the host checks. The copy is issued as inline
+  // assembly so that the compiler does not treat it as a pending write to
+  // every LDS address (it would then wait for it before each LDS read);
+  // completion is awaited explicitly with wait_copies() before the barrier
+  // that publishes the slice.
   const uint32_t lds_wave = (uint32_t)(wave * T::kCopiesPerWave * 1024);
-  auto issue_copy = [&](uint64_t sbase, uint32_t voff, uint32_t lds) __attribute__((always_inline)) {
-    // The copy is issued as inline assembly so that the compiler does not
-    // treat it as a pending write to every LDS address (it would then wait
-    // for it before each LDS read); completion is awaited explicitly with
-    // wait_copies() before the barrier that publishes the slice.
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
-  };
   // (readfirstlane returns a signed int: widen through uint32_t so the low
   // half is zero-extended, never sign-extended into the high half)
   auto sgpr64 = [&](const char* p) __attribute__((always_inline)) {
@@ -244,21 +245,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uintptr_t)p >> 32));
     return ((uint64_t)hi << 32) | (uint64_t)lo;
   };
+  const int kv_bytes = __builtin_amdgcn_readfirstlane(kv * T::kRowBytes);
+  auto rsrc_of = [&](const char* base) __attribute__((always_inline)) {
+    const uint64_t a = sgpr64(base);
+    i32x4 r;
+    r[0] = (int)(uint32_t)a;
+    r[1] = (int)(uint32_t)(a >> 32);   // base bits 32..47; stride 0
+    r[2] = kv_bytes;                    // num_records, in bytes
+    r[3] = 0x00020000;                  // 32-bit data format, no swizzle
+    return r;
+  };
   auto copy_slice = [&](const char* src, int sl, const char* dst) __attribute__((always_inline)) {
     if (T::kCopyWaves < kWaves && wave >= T::kCopyWaves) return;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)dst + lds_wave;
-    if (__builtin_expect(sl < sl_rag, 1)) {
-      const uint64_t sbase = sgpr64(src) + (uint64_t)(uint32_t)sl * (uint64_t)T::kBytes;
+    const i32x4 rs = rsrc_of(src);
 #pragma unroll
-      for (int q = 0; q < T::kCopiesPerWave; ++q) issue_copy(sbase, (uint32_t)cp_off[q], lds0 + q * 1024);
-    } else {
-      const int k0 = sl * kSlice;
-#pragma unroll
-      for (int q = 0; q < T::kCopiesPerWave; ++q) {
-        const int key = min(k0 + cp_row(q), kv - 1);
-        const uint32_t voff = (uint32_t)cp_off[q] + (uint32_t)((key - cp_row(q)) * T::kRowBytes);
-        issue_copy(sgpr64(src), voff, lds0 + q * 1024);
-      }
+    for (int q = 0; q < T::kCopiesPerWave; ++q) {
+      const uint32_t voff = (uint32_t)cp_off[q] + (uint32_t)sl * (uint32_t)T::kBytes;
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :: "s"(lds0 + q * 1024), "v"(voff), "s"(rs) : "memory", "m0");
     }
   };
   // Slice s lives in stage s % kStages: K rows at kst(st), V rows at vst(st).
@@ -316,6 +321,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // workgroups carry equal work and none is left running alone at the end.
   // The tile with more keys goes first.
   const int n_mine = (n_qt - 1 - pr != pr) ? 2 : 1;
+  // Lanes whose key row is past kv fetch nothing, so a stage can keep rows no
+  // copy wrote. Zero the stages once: such rows then hold zeros or keys of an
+  // earlier slice, always finite, and their zero probabilities keep them out.
+  for (int i = tid; i < T::kLds / 16; i += kThreads)
+    *(__attribute__((address_space(3))) u32x4*)(smem + 16 * i) = (u32x4){0u, 0u, 0u, 0u};
+  __syncthreads();
 #pragma nounroll
   for (int it = 0; it < n_mine; ++it) {
   const int qt = it == 0 ? n_qt - 1 - pr : pr;
@@ -336,6 +347,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   const int nh_wg = (kv_end + kSlice - 1) / kSlice;
   int nh = wave_live ? nh_wg : 0;
   if (causal) nh = min(nh, row_hi / kSlice + 1);
+  nh = __builtin_amdgcn_readfirstlane(nh);
 
   // ---- Q rows -> VGPRs as the B operand of S^T = K Q^T ----
   bf16x8 qreg[kRB][D / 16];
@@ -382,6 +394,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   if (row_lo < qs) mask_from = 0;
   mask_from = __builtin_amdgcn_readfirstlane(mask_from);
   auto need_mask = [&](int h) __attribute__((always_inline)) { return h >= mask_from; };
+  // slices mask_from .. nh-1 (this wave's) need the mask: h+1 is one of them
+  // iff (unsigned)(h+1 - mask_from) < mask_span
+  const int mask_span = max(nh, mask_from) - mask_from;
   auto mask = [&](int h, f32x16 (&s)[kRB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
@@ -406,8 +421,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     for (int kc = 0; kc < D / 16; ++kc)
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {
-        if (kc == 0) mfma_v_init(s[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
-        else mfma_v(s[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
+        if (kc == 0) mfma_v_init<true>(s[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
+        else mfma_v<true>(s[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
       }
     mfma_result_wait();
   };
@@ -533,8 +548,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
 #pragma unroll
       for (int g = 0; g < kG; ++g) {
         const int kc = g / kRB, rb = g % kRB;
-        if (kc == 0) mfma_v_init(sn[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
-        else mfma_v(sn[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
+        if (kc == 0) mfma_v_init<false>(sn[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
+        else mfma_v<false>(sn[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
         if (g % kRB == 0) {   // V reads for PV group g/kRB, (cc, db) in PV order
           const int pg = g / kRB;
           load_v_one(vb, pg / (D / 32), pg % (D / 32));
@@ -562,7 +577,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     // reach the address unit spread out rather than all at once.
     copy_slice(kg, h + kStages - 1, kst((Hm + kStages - 1) % kStages));
     mfma_result_wait();   // S of slice h+1 is read below
-    if (nxt && need_mask(h + 1)) mask(h + 1, sn);
+    if ((unsigned)(h + 1 - mask_from) < (unsigned)mask_span) mask(h + 1, sn);
     // ---- phase B ----
     {
       const char* kb = kst((Hm + 2) % kStages);
@@ -679,6 +694,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   const long long n_wg = (long long)B * H * ((n_qt + 1) / 2);   // one workgroup per pair of query tiles
   if (n_wg > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   if ((long long)B * H > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  if ((long long)N_k * d * 2 > 0x7fffffffLL) return ATTN_ERR_SHAPE;   // K/V copy offsets are 32-bit
   const size_t q_bytes = (size_t)B * H * N_q * d * 2;
   const size_t k_bytes = (size_t)B * H * N_k * d * 2;
   const size_t lse_bytes = (size_t)B * H * N_q * 4;
