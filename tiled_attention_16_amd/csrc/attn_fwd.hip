@@ -172,6 +172,13 @@ __device__ __forceinline__ void mfma_a(f32x16& acc, const bf16x8& a, const bf16x
 // instruction may read it.
 __device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
+// Wait until at most N of this wave's LDS reads are in flight (they complete
+// in issue order); the compiler sees this wait and drops the ones it implies.
+template <int N>
+__device__ __forceinline__ void lgkm_wait() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));   // vmcnt, expcnt at their maxima
+}
 // Wait until at most N of this wave's copies are still in flight (copies
 // complete in issue order).
 template <int N>
@@ -454,7 +461,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     for (int e = e0; e < e0 + n; e += 2) {
       const float p0 = __builtin_amdgcn_exp2f(s[rb][e]);
       const float p1 = __builtin_amdgcn_exp2f(s[rb][e + 1]);
-      lsum[rb] += p0 + p1;
+      if (e == 0) lsum[rb] = p0 + p1;   // first pair of the slice
+      else lsum[rb] += p0 + p1;
       pbw[rb][e >> 1] = pack2(p0, p1);
       asm volatile("" :: "v"(pbw[rb][e >> 1]), "v"(lsum[rb]));
     }
@@ -542,8 +550,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     // ---- phase A ----
     {
       const char* vb = vst_rel(Hm);
-#pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) lsum[rb] = 0.f;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int g = 0; g < kG; ++g) {
@@ -586,6 +592,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       for (int g = 0; g < kG; ++g) {
         const int pg = g / kRB, rb = g % kRB;
         const int cc = pg / (D / 32), db = pg % (D / 32);
+        // V pairs were read in phase A in PV order, two reads per pair. Wait
+        // for the first half before group 0 and for the second half before
+        // group kG/2 (by then the K reads issued in between may still be in
+        // flight; LDS reads complete in order), two waits instead of one per
+        // group.
+        static_assert(kRB == 1, "one V pair per group, in group order");
+        if (g == 0) lgkm_wait<kG>();
+        if (g == kG / 2) lgkm_wait<kG / 2>();
         mfma_a(o_acc[rb][db], va[cc][db], pb(rb, cc));
         if (g < D / 16) ka[g] = *(const lds_u32x4*)(kb + k_off[g]);
         // the shift S*c - m of slice h+1, 16 elements per block, spread over the groups
