@@ -18,8 +18,8 @@
 //
 // Data movement ([MEMWALL] §4.3 double buffering, here an 8-deep ring;
 // [PT2CUDA] step 5): K and V slices go from global memory straight into LDS
-// with the gfx950 16-byte global_load_lds copy, no register staging. Each
-// wave issues its share of the copy of slice h+7 at the end of step h, into
+// with 16-byte buffer_load ... lds copies, no register staging. Each wave
+// issues its share of the copy of slice h+7 during step h, into
 // the stage slice h-1 used; one barrier per step publishes the landed slices
 // and frees that stage. Inside a stage, row r's 16-byte chunk c sits at chunk
 // position c ^ swz(r), so the MFMA operand reads (ds_read_b128 for K, the
