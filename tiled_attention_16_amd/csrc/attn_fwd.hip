@@ -262,10 +262,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     r[3] = 0x00020000;                  // 32-bit data format, no swizzle
     return r;
   };
-  auto copy_slice = [&](const char* src, int sl, const char* dst) __attribute__((always_inline)) {
+  // (the empty asm makes the two descriptors opaque, so the compiler keeps
+  // each in its own four SGPRs instead of rebuilding the shared words per copy)
+  i32x4 k_rsrc = rsrc_of(kg), v_rsrc = rsrc_of(vg);
+  asm volatile("" : "+s"(k_rsrc), "+s"(v_rsrc));
+  auto copy_slice = [&](const i32x4& rs, int sl, const char* dst) __attribute__((always_inline)) {
     if (T::kCopyWaves < kWaves && wave >= T::kCopyWaves) return;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)dst + lds_wave;
-    const i32x4 rs = rsrc_of(src);
 #pragma unroll
     for (int q = 0; q < T::kCopiesPerWave; ++q) {
       const uint32_t voff = (uint32_t)cp_off[q] + (uint32_t)sl * (uint32_t)T::kBytes;
@@ -281,8 +284,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   constexpr int kC = 2 * T::kCopiesPerWave;   // copies per wave per K+V slice
   auto copy_slices = [&](int s) __attribute__((always_inline)) {
     const int st = s & (kStages - 1);
-    copy_slice(kg, s, kst(st));
-    copy_slice(vg, s, vst(st));
+    copy_slice(k_rsrc, s, kst(st));
+    copy_slice(v_rsrc, s, vst(st));
   };
 
   // ---- per-lane LDS offsets of the MFMA operand reads ----
@@ -581,7 +584,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     // freed. The copies go out between the phases and at the end of the step,
     // where the waves arrive at different times, so the workgroup's copies
     // reach the address unit spread out rather than all at once.
-    copy_slice(kg, h + kStages - 1, kst((Hm + kStages - 1) % kStages));
+    copy_slice(k_rsrc, h + kStages - 1, kst((Hm + kStages - 1) % kStages));
     mfma_result_wait();   // S of slice h+1 is read below
     if ((unsigned)(h + 1 - mask_from) < (unsigned)mask_span) mask(h + 1, sn);
     // ---- phase B ----
@@ -608,7 +611,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    copy_slice(vg, h + kStages - 1, vst((Hm + kStages - 1) % kStages));   // the V share
+    copy_slice(v_rsrc, h + kStages - 1, vst((Hm + kStages - 1) % kStages));   // the V share
   };
 
   f32x16 sa[kRB], sb[kRB];
