@@ -235,9 +235,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   }
   // Copy slice sl (keys kSlice*sl ..) of a head's K or V into stage dst, with
   // buffer_load_dwordx4 ... lds through a raw buffer descriptor that covers
-  // the head's kv valid keys: lanes whose row is at or past kv fall outside
-  // num_records and bring no data (such rows are never used: the mask drops
-  // their scores and their probabilities are 0). The byte offset of a lane is
+  // the keys the current tile can see (set per tile, below): lanes whose row
+  // is past them fall outside num_records and bring no data (such rows are
+  // never used: the mask drops their scores and their probabilities are 0). The byte offset of a lane is
   // sl * kBytes + its fixed in-slice offset, so the head's K (or V) must span
   // less than 2 GB, which the host checks. The copy is issued as inline
   // assembly so that the compiler does not treat it as a pending write to
@@ -345,6 +345,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   int kv_end = kv;                                 // keys this workgroup can see
   if (causal) kv_end = min(kv_end, q_end);
   if (qs >= q_end) kv_end = 0;                     // every row of the tile is masked
+  // The copies only need the keys the tile can see: keys past kv_end (beyond
+  // the causal limit of the tile's last row) come back as nothing.
+  k_rsrc[2] = v_rsrc[2] = __builtin_amdgcn_readfirstlane(kv_end * T::kRowBytes);
+  asm volatile("" : "+s"(k_rsrc), "+s"(v_rsrc));
 
   // This wave's rows: row_lo .. row_lo + 63, as MFMA blocks rb = 0, 1 of 32
   // rows; lane L holds row row_lo + 32*rb + L%32 of block rb.
