@@ -459,20 +459,64 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       for (int r = 0; r < 16; ++r) x[r] = fmaf(x[r], c, negm[rb]);
     }
   };
-  // P = exp2(S*c - m) for elements e0 .. e0+n-1 of block rb: fp32 into the
-  // row sum, bf16 pairs into the PV operand words.
-  uint32_t pbw[kRB][8];
+  // P = exp2(S*c - m), fp32 into the row sum, bf16 pairs into the PV operand
+  // words. A slice's P is made in two halves: elements 0..7 (keys 0..15 of
+  // the slice, the B operand of the first four PV MFMAs) in the phase before
+  // the one that exponentiates elements 8..15, so that the exponentials are
+  // spread over both phases. The first half is kept per slice parity,
+  // because it is made while the previous slice's first half is still being
+  // consumed.
+  static_assert(kRB == 1, "the P halves below are laid out for one row block per wave");
+  constexpr int kG = kRB * D / 16;      // MFMAs per phase
+  uint32_t pbw_lo[2][4], pbw_hi[4];
+  float lsum_lo[2], lsum_hi;
   float lsum[kRB];
-  auto expo_part = [&](const f32x16 (&s)[kRB], int rb, int e0, int n) __attribute__((always_inline)) {
-#pragma unroll
-    for (int e = e0; e < e0 + n; e += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(s[rb][e]);
-      const float p1 = __builtin_amdgcn_exp2f(s[rb][e + 1]);
-      if (e == 0) lsum[rb] = p0 + p1;   // first pair of the slice
-      else lsum[rb] += p0 + p1;
-      pbw[rb][e >> 1] = pack2(p0, p1);
-      asm volatile("" :: "v"(pbw[rb][e >> 1]), "v"(lsum[rb]));
+  // exponentials of elements e, e+1 of s into word w and running sum acc
+  auto exp_pair = [&](const f32x16& x, int e, uint32_t& w, float& acc, bool first) __attribute__((always_inline)) {
+    const float p0 = __builtin_amdgcn_exp2f(x[e]);
+    const float p1 = __builtin_amdgcn_exp2f(x[e + 1]);
+    if (first) acc = p0 + p1;
+    else acc += p0 + p1;
+    w = pack2(p0, p1);
+    asm volatile("" :: "v"(w), "v"(acc));
+  };
+  // exponential of element j of x; every second one completes a pair: packed
+  // into words[(j % 8) / 2], its sum added to acc (started by the pair with j % 8 = 1)
+  float p_even = 0.f;
+  auto exp_one = [&](const f32x16& x, int j, uint32_t* words, float& acc) __attribute__((always_inline)) {
+    const float p = __builtin_amdgcn_exp2f(x[j]);
+    if ((j & 1) == 0) {
+      p_even = p;
+    } else {
+      if ((j & 7) == 1) acc = p_even + p;
+      else acc += p_even + p;
+      words[(j & 7) >> 1] = pack2(p_even, p);
+      asm volatile("" :: "v"(words[(j & 7) >> 1]), "v"(acc));
     }
+  };
+  // Per-group schedule (kG groups per phase) of the VALU work of the two
+  // phases: phase A exponentiates elements 8..15 of slice h, phase B forms
+  // S*c - m of slice h+1 (all 16 elements) and exponentiates its elements
+  // 0..7, each after its own shift.
+  struct Range { int lo, hi; };
+  auto sched_a = [](int g) constexpr -> Range {   // elements of the second half
+    return kG == 8 ? Range{8 + g, 9 + g} : Range{8 + 2 * g, 10 + 2 * g};
+  };
+  auto sched_b_shift = [](int g) constexpr -> Range {
+    if (kG == 8) {
+      constexpr Range r[8] = {{0, 4}, {4, 8}, {8, 10}, {10, 12}, {12, 14}, {14, 16}, {16, 16}, {16, 16}};
+      return r[g];
+    }
+    constexpr Range r[4] = {{0, 8}, {8, 16}, {16, 16}, {16, 16}};
+    return r[g];
+  };
+  auto sched_b_exp = [](int g) constexpr -> Range {
+    if (kG == 8) {
+      constexpr Range r[8] = {{0, 0}, {0, 1}, {1, 2}, {2, 3}, {3, 4}, {4, 5}, {5, 7}, {7, 8}};
+      return r[g];
+    }
+    constexpr Range r[4] = {{0, 0}, {0, 2}, {2, 6}, {6, 8}};
+    return r[g];
   };
   // S <- S*c - m for elements e0 .. e0+n-1 of block rb.
   auto shift_part = [&](f32x16 (&s)[kRB], int rb, int e0, int n) __attribute__((always_inline)) {
@@ -487,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // slice's exponentials. Rows whose max is not above m keep everything
   // (their shift d is 0). A row with no allowed key so far has m = -inf and
   // only -inf scores, so its d is 0 as well.
-  auto raise_max = [&](f32x16 (&s)[kRB]) __attribute__((always_inline)) {
+  auto raise_max = [&](f32x16 (&s)[kRB], int par) __attribute__((always_inline)) {
     mfma_result_wait();   // o_acc is rescaled below
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
@@ -509,13 +553,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
         const float p0 = __builtin_amdgcn_exp2f(x[e] - d);
         const float p1 = __builtin_amdgcn_exp2f(x[e + 1] - d);
         sum += p0 + p1;
-        pbw[rb][e >> 1] = pack2(p0, p1);
+        if (e < 8) pbw_lo[par][e >> 1] = pack2(p0, p1);
+        else pbw_hi[(e - 8) >> 1] = pack2(p0, p1);
       }
       lsum[rb] = sum;
     }
   };
-  auto pb = [&](int rb, int cc) __attribute__((always_inline)) {
-    const u32x4 w = {pbw[rb][4 * cc], pbw[rb][4 * cc + 1], pbw[rb][4 * cc + 2], pbw[rb][4 * cc + 3]};
+  auto pb = [&](int par, int cc) __attribute__((always_inline)) {
+    const u32x4 w = cc == 0 ? (u32x4){pbw_lo[par][0], pbw_lo[par][1], pbw_lo[par][2], pbw_lo[par][3]}
+                            : (u32x4){pbw_hi[0], pbw_hi[1], pbw_hi[2], pbw_hi[3]};
     return as_bf16x8(w);
   };
   // one transposing V read pair: va[cc][db] for PV
@@ -544,7 +590,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // K(h-1) in step h-3. Copies are issued for every step, also past the last
   // slice (clamped rows), so the number in flight, and with it the wait
   // count, is the same each time: slices h+3 .. h+6 may still be in flight.
-  constexpr int kG = kRB * D / 16;      // MFMAs per phase
   auto step = [&](auto hm, int h, f32x16 (&sc)[kRB], f32x16 (&sn)[kRB]) __attribute__((always_inline)) {
     constexpr int Hm = decltype(hm)::value;   // h % kStages
     wait_copies<4 * kC>();
@@ -561,26 +606,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
 #pragma unroll
       for (int g = 0; g < kG; ++g) {
         const int kc = g / kRB, rb = g % kRB;
-        if (kc == 0) mfma_v_init<false>(sn[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
+        // (for d = 64 the compiler moves the first K operand into AGPRs right
+        // before this MFMA, so it gets the wait states)
+        if (kc == 0) mfma_v_init<D == 64>(sn[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
         else mfma_v<false>(sn[rb], as_bf16x8(ka[kc]), qreg[rb][kc]);
         if (g % kRB == 0) {   // V reads for PV group g/kRB, (cc, db) in PV order
           const int pg = g / kRB;
           load_v_one(vb, pg / (D / 32), pg % (D / 32));
         }
-        constexpr int kPer = 16 * kRB / kG;   // exponentials per group
-        expo_part(sc, (g * kPer) / 16, (g * kPer) % 16, kPer);
+        const Range ra = sched_a(g);   // second half of slice h's exponentials
+#pragma unroll
+        for (int j = ra.lo; j < ra.hi; ++j) exp_one(sc[0], j, pbw_hi, lsum_hi);
         __builtin_amdgcn_sched_barrier(0);
       }
       // keep P and the sums in this phase (the compiler would otherwise sink
       // them past the mask branch, away from the MFMAs they overlap)
-#pragma unroll
-      for (int rb = 0; rb < kRB; ++rb)
-        asm volatile("" :: "v"(pbw[rb][0]), "v"(pbw[rb][1]), "v"(pbw[rb][2]), "v"(pbw[rb][3]),
-                     "v"(pbw[rb][4]), "v"(pbw[rb][5]), "v"(pbw[rb][6]), "v"(pbw[rb][7]), "v"(lsum[rb]));
+      asm volatile("" :: "v"(pbw_hi[0]), "v"(pbw_hi[1]), "v"(pbw_hi[2]), "v"(pbw_hi[3]), "v"(lsum_hi));
+      lsum[0] = lsum_lo[Hm & 1] + lsum_hi;
       bool over = false;
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) over = over || !(lsum[rb] <= kSumCap);   // NaN counts as over
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(over) != 0, 0)) raise_max(sc);
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(over) != 0, 0)) raise_max(sc, Hm & 1);
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) l_run[rb] += lsum[rb];
     }
@@ -607,11 +653,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
         static_assert(kRB == 1, "one V pair per group, in group order");
         if (g == 0) lgkm_wait<kG>();
         if (g == kG / 2) lgkm_wait<kG / 2>();
-        mfma_a(o_acc[rb][db], va[cc][db], pb(rb, cc));
+        mfma_a(o_acc[rb][db], va[cc][db], pb(Hm & 1, cc));
         if (g < D / 16) ka[g] = *(const lds_u32x4*)(kb + k_off[g]);
-        // the shift S*c - m of slice h+1, 16 elements per block, spread over the groups
-        constexpr int kShPer = 16 * kRB / kG;   // elements per group
-        shift_part(sn, (g * kShPer) / 16, (g * kShPer) % 16, kShPer);
+        // the shift S*c - m of slice h+1 and the first half of its exponentials
+        const Range rs = sched_b_shift(g), rx = sched_b_exp(g);
+        if (rs.hi > rs.lo) shift_part(sn, 0, rs.lo, rs.hi - rs.lo);
+#pragma unroll
+        for (int j = rx.lo; j < rx.hi; ++j) exp_one(sn[0], j, pbw_lo[(Hm + 1) & 1], lsum_lo[(Hm + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -630,6 +678,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       qk(sa);
       if (need_mask(0)) mask(0, sa);
       first_max(sa);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) exp_one(sa[0], j, pbw_lo[0], lsum_lo[0]);
       load_k(std::integral_constant<int, 1>{});
     }
     static_assert(kStages == 8, "the loop below is unrolled over kStages slices");
