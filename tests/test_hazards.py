@@ -51,3 +51,19 @@ def test_no_fall_through_after_unconditional_branch():
     asm2 = (HEAD + "\tv_accvgpr_write_b32 a0, v3\n\ts_branch .LBB0_3\n.LBB0_2:\n" + MFMA +
             ".LBB0_3:\n\ts_endpgm\n")
     assert check(asm2) == []
+
+
+def test_mfma_result_read_too_soon():
+    asm = HEAD + MFMA + "\tv_fma_f32 v40, s1, v3, v41\n"
+    assert len(check(asm)) == 1
+    padded = HEAD + MFMA + "\ts_nop 7\n\ts_nop 7\n\ts_nop 3\n\tv_fma_f32 v40, s1, v3, v41\n"
+    assert check(padded) == []
+
+
+def test_mfma_result_read_through_branch_and_chain():
+    # the read sits behind a taken branch: still too close
+    asm = HEAD + MFMA + "\ts_cbranch_scc1 .LBB0_5\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n.LBB0_5:\n\tv_add_f32_e32 v50, v2, v51\n"
+    assert len(check(asm)) == 1
+    # a later MFMA of the same chain takes over: only its own distance counts
+    chain = HEAD + MFMA + MFMA + "\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\tv_add_f32_e32 v50, v2, v51\n"
+    assert check(chain) == []

@@ -635,8 +635,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     // where the waves arrive at different times, so the workgroup's copies
     // reach the address unit spread out rather than all at once.
     copy_slice(k_rsrc, h + kStages - 1, kst((Hm + kStages - 1) % kStages));
-    mfma_result_wait();   // S of slice h+1 is read below
-    if ((unsigned)(h + 1 - mask_from) < (unsigned)mask_span) mask(h + 1, sn);
+    // S of slice h+1 is read below. The mask reads it at once and needs the
+    // wait states; for d = 128 the phase-B shifts come late enough without
+    // them (the build's hazard check verifies that distance), for d = 64 not.
+    const bool msk = (unsigned)(h + 1 - mask_from) < (unsigned)mask_span;
+    if (D == 64 || msk) mfma_result_wait();
+    if (msk) mask(h + 1, sn);
     // ---- phase B ----
     {
       const char* kb = kst((Hm + 2) % kStages);

@@ -1,14 +1,23 @@
-"""Check the compiled kernel for one hazard the hardware does not interlock.
+"""Check the compiled kernel for two hazards the hardware does not interlock.
 
 The MFMAs of ``csrc/attn_fwd.hip`` are inline assembly, so the compiler does
-not know they are MFMAs and does not pad them against the rule that a VALU
-write of a VGPR or AGPR (``v_accvgpr_write``, ``v_mov``, any ``v_*`` result)
-needs at least two wait states before an MFMA reads that register as its A, B
-or C operand (CDNA3/CDNA4 ISA, MFMA dependency table). The kernel code is laid
-out so that no such write comes that close; this module reads the compiler's
-assembly and proves it, instruction by instruction, following fall-through
-and every branch into a block. ``build.py`` runs it on every build and fails
-the build on a violation.
+not know they are MFMAs and pads them against neither rule of the MFMA
+dependency table (CDNA3/CDNA4 ISA):
+  * a VALU write of a VGPR or AGPR (``v_accvgpr_write``, ``v_mov``, any
+    ``v_*`` result) needs at least two wait states before an MFMA reads that
+    register as its A, B or C operand;
+  * an MFMA result needs wait states before a VALU instruction reads it: 11
+    or 12 for an 8-pass 32x32 MFMA, up to 20 for a 16-pass one; the check
+    asks for 20.
+The kernel is laid out so that neither happens; this module reads the
+compiler's assembly and proves it, instruction by instruction, following
+fall-through and every branch, backwards from each MFMA for the first rule and
+forwards for the second. ``build.py`` runs it on every build and fails the
+build on a violation.
+
+(``v_readfirstlane``/``v_readlane`` are left out of the second rule: the
+kernel never reads an MFMA result through them, and the compiler emits dead
+ones that name an accumulator register as a placeholder source.)
 
 Usage: ``python -m tiled_attention_16_amd.hazards kernel.s``
 """
@@ -19,7 +28,8 @@ import sys
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Set, Tuple
 
-WAIT_STATES = 2   # VALU write -> MFMA read of the same register
+WAIT_STATES = 2    # VALU write -> MFMA read of the same register
+RESULT_WAIT = 20   # MFMA write -> VALU read of the same register
 
 _REG = re.compile(r"^([va])(?:(\d+)|\[(\d+):(\d+)\])$")
 
@@ -92,6 +102,26 @@ def _wait_states(ins: Ins) -> int:
     return 1
 
 
+def _reads(ins: Ins) -> Set[Tuple[str, int]]:
+    """Vector registers a VALU instruction reads (its source operands)."""
+    if not ins.op.startswith("v_") or ins.op.startswith("v_mfma"):
+        return set()
+    if ins.op.startswith(("v_readfirstlane", "v_readlane")):
+        return set()
+    srcs = ins.args if ins.op.startswith("v_cmp") else ins.args[1:]
+    out: Set[Tuple[str, int]] = set()
+    for a in srcs:
+        a = a.strip()
+        if a.startswith("-"):
+            a = a[1:]
+        if a.startswith("|") and a.endswith("|"):
+            a = a[1:-1]
+        out |= _regs(a)
+    if "permlane" in ins.op and "swap" in ins.op:
+        out |= _regs(ins.args[0])
+    return out
+
+
 def check(text: str) -> List[str]:
     problems: List[str] = []
     for body in _parse(text):
@@ -131,6 +161,37 @@ def check(text: str) -> List[str]:
                 need -= _wait_states(ins)
                 j -= 1
 
+        def scan_fwd(i: int, need: int, dst: Set[Tuple[str, int]], seen: Set[Tuple[int, int]], where: int):
+            # walk forwards from index i (exclusive) until `need` wait states are covered
+            j = i + 1
+            while need > 0 and j < len(body):
+                ins = body[j]
+                if ins.label:
+                    j += 1
+                    continue
+                if ins.op.startswith("v_mfma"):
+                    if _regs(ins.args[0]) == dst:
+                        return   # the accumulation chain continues; that MFMA is checked itself
+                    need -= 1
+                    j += 1
+                    continue
+                hit = _reads(ins) & dst
+                if hit:
+                    problems.append(f"line {ins.line}: '{ins.op} {', '.join(ins.args)}' reads {sorted(hit)[0]} "
+                                    f"fewer than {RESULT_WAIT} wait states after the MFMA of line {where}")
+                    return
+                if ins.op == "s_endpgm":
+                    return
+                need -= _wait_states(ins)
+                for t in ins.targets:
+                    k = label_at.get(t)
+                    if k is not None and (k, need) not in seen:
+                        seen.add((k, need))
+                        scan_fwd(k, need, dst, seen, where)
+                if ins.op == "s_branch":
+                    return
+                j += 1
+
         for i, ins in enumerate(body):
             if not ins.op.startswith("v_mfma"):
                 continue
@@ -138,6 +199,7 @@ def check(text: str) -> List[str]:
             for a in ins.args[1:4]:
                 reads |= _regs(a)
             scan(i, WAIT_STATES, reads, set(), ins.line)
+            scan_fwd(i, RESULT_WAIT, _regs(ins.args[0]), set(), ins.line)
     return problems
 
 
