@@ -269,11 +269,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   auto copy_slice = [&](const i32x4& rs, int sl, const char* dst) __attribute__((always_inline)) {
     if (T::kCopyWaves < kWaves && wave >= T::kCopyWaves) return;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)dst + lds_wave;
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)sl * (uint32_t)T::kBytes);
 #pragma unroll
     for (int q = 0; q < T::kCopiesPerWave; ++q) {
-      const uint32_t voff = (uint32_t)cp_off[q] + (uint32_t)sl * (uint32_t)T::kBytes;
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                   :: "s"(lds0 + q * 1024), "v"(voff), "s"(rs) : "memory", "m0");
+      // (the lane offset is added after the M0 write: that add is the wait
+      // state the LDS copy needs after M0 changes)
+      uint32_t voff;
+      asm volatile("s_mov_b32 m0, %1\n\tv_add_u32 %0, %2, %3\n\tbuffer_load_dwordx4 %0, %4, 0 offen lds"
+                   : "=&v"(voff) : "s"(lds0 + q * 1024), "s"(soff), "v"(cp_off[q]), "s"(rs) : "memory", "m0");
     }
   };
   // Slice s lives in stage s % kStages: K rows at kst(st), V rows at vst(st).
