@@ -50,10 +50,11 @@
 //   O^T  += V^T P^T on MFMA 32x32x16 bf16 -> fp32, V^T read from LDS with the
 //         transposing read.
 // The loop is software pipelined inside each wave: while the MFMA unit
-// computes S for slice h+1, the VALU exponentiates slice h; while it computes
-// O += P V for slice h, the VALU forms S*c - m of slice h+1. The two waves of
-// a SIMD interleave on top of that: one wave's VALU work fills the other's
-// MFMA time.
+// computes S for slice h+1, the VALU exponentiates the second half of slice h;
+// while it computes O += P V for slice h, the VALU forms S*c - m of slice h+1
+// and exponentiates its first half. The two waves of a SIMD run the same
+// phases at the same time (one barrier per slice keeps them in step) and
+// interleave their MFMAs and VALU work.
 // Epilogue ([PT2CUDA] step 4.1, one division per row at the end): O = O / l
 // (0 when l = 0), LSE = ln2 * (m + log2 l) (-inf when l = 0), bf16 store.
 //
@@ -474,15 +475,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   uint32_t pbw_lo[2][4], pbw_hi[4];
   float lsum_lo[2], lsum_hi;
   float lsum[kRB];
-  // exponentials of elements e, e+1 of s into word w and running sum acc
-  auto exp_pair = [&](const f32x16& x, int e, uint32_t& w, float& acc, bool first) __attribute__((always_inline)) {
-    const float p0 = __builtin_amdgcn_exp2f(x[e]);
-    const float p1 = __builtin_amdgcn_exp2f(x[e + 1]);
-    if (first) acc = p0 + p1;
-    else acc += p0 + p1;
-    w = pack2(p0, p1);
-    asm volatile("" :: "v"(w), "v"(acc));
-  };
   // exponential of element j of x; every second one completes a pair: packed
   // into words[(j % 8) / 2], its sum added to acc (started by the pair with j % 8 = 1)
   float p_even = 0.f;
@@ -578,11 +570,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // Step h (slice h; S of slice h is in sc, already shifted):
   //   wait for slices <= h+2, barrier (slice h-1's stage is now free);
   //   phase A: QK(h+1) on the MFMA unit (K(h+1) was read last phase) while the
-  //            VALU exponentiates slice h and the LDS reads V(h);
-  //   copy this wave's share of K(h+7) into slice h-1's stage;
+  //            VALU exponentiates elements 8..15 of slice h and the LDS reads
+  //            V(h);
   //   check the exponential sums of slice h against kSumCap (rarely: raise m);
+  //   copy this wave's share of K(h+7) into slice h-1's stage;
+  //   mask slice h+1 if it crosses a bound;
   //   phase B: PV(h) on the MFMA unit while the VALU forms S*c - m of slice
-  //            h+1, and the LDS reads K(h+2);
+  //            h+1 and exponentiates its elements 0..7, and the LDS reads
+  //            K(h+2);
   //   copy this wave's share of V(h+7).
   // Each phase is written as kG groups of one MFMA, a share of the LDS reads
   // and a share of the VALU work, fenced so the scheduler keeps that order:
@@ -590,9 +585,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // Slice h+1 may lie past this wave's last slice: its S is then computed from
   // whatever the stage holds and discarded, so no branch splits a phase.
   // Slice h-1's stage is free at step h: V(h-1) was read in step h-1 and
-  // K(h-1) in step h-3. Copies are issued for every step, also past the last
-  // slice (clamped rows), so the number in flight, and with it the wait
-  // count, is the same each time: slices h+3 .. h+6 may still be in flight.
+  // K(h-1) in step h-3. Copies are issued for every step, also past the
+  // tile's last slice (where they fetch nothing), so the number in flight,
+  // and with it the wait count, is the same each time: slices h+3 .. h+6 may
+  // still be in flight.
   auto step = [&](auto hm, int h, f32x16 (&sc)[kRB], f32x16 (&sn)[kRB]) __attribute__((always_inline)) {
     constexpr int Hm = decltype(hm)::value;   // h % kStages
     wait_copies<4 * kC>();
@@ -601,7 +597,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       copy_slices(h + kStages - 1);
       return;
     }
-    const bool nxt = h + 1 < nh;
     // ---- phase A ----
     {
       const char* vb = vst_rel(Hm);
