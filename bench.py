@@ -4,7 +4,13 @@
 
 A step is one call of the C-ABI ``attn_fwd`` over the whole workload (one
 kernel launch: tile schedule, Q/K/V staging, QK^T, mask, online softmax, PV,
-epilogue). Inputs are synthetic seeded bf16 tensors already resident in HBM
+epilogue).
+
+``--workload hbm_causal_n256_d128`` / ``hbm_noncausal_n512_d128`` measure the
+short, bandwidth-bound shapes instead: the line then reports achieved GB/s
+(algorithmic bytes: Q, K, V read once, O and LSE written once) against the
+8 TB/s HBM peak, and successive launches rotate over three copies of the
+inputs at different addresses so that no launch finds its inputs in cache. Inputs are synthetic seeded bf16 tensors already resident in HBM
 when the timed region starts. W untimed warmup steps (enough that the GPU
 clock has settled under load), then exactly K timed steps launched back to
 back and bracketed by a device synchronisation on both sides; the timed
@@ -30,10 +36,14 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import HEADLINE, WORKLOADS, make_inputs  # noqa: E402
+from workloads import HBM_PROBES, HEADLINE, WORKLOADS, make_inputs  # noqa: E402
+
+ALL_WORKLOADS = {**WORKLOADS, **HBM_PROBES}
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, published
 METRIC = "attention fwd TFLOP/s (bf16, causal, N=4096, d=128) + % of MFMA bf16 peak"
+HBM_METRIC = "attention fwd achieved HBM GB/s (bf16, short sequences) + % of HBM peak"
 KERNEL_SRC = os.path.join(ROOT, "tiled_attention_16_amd", "csrc", "attn_fwd.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -102,7 +112,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(ALL_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device copies of MIB MiB each (the reference "
@@ -122,7 +132,8 @@ def main():
     import tiled_attention_16_amd as ta
 
     ta.load_library()
-    w = WORKLOADS[args.workload]
+    w = ALL_WORKLOADS[args.workload]
+    hbm_probe = w.name in HBM_PROBES
     inp = make_inputs(w)
     dev = torch.device("cuda:0")
 
@@ -132,13 +143,18 @@ def main():
     q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
     sl = torch.from_numpy(inp.seqlens_k).to(dev) if inp.seqlens_k is not None else None
     qs = torch.from_numpy(inp.q_start).to(dev) if inp.q_start is not None else None
-    o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.H, w.N_q), dtype=torch.float32, device=dev)
+    sets = [(q, k, v, torch.empty_like(q), torch.empty((w.B, w.H, w.N_q), dtype=torch.float32, device=dev))]
+    if hbm_probe:   # two more input/output sets at other addresses, launched in turn
+        for _ in range(2):
+            sets.append(tuple(t.clone() for t in sets[0][:3]) + (torch.empty_like(q), torch.empty_like(sets[0][4])))
     stream = torch.cuda.current_stream(dev)
+    n_step = [0]
 
     def step():
-        ta.attn_fwd(q, k, v, causal=w.causal, scale=float(inp.scale), seqlens_k=sl, q_start=qs, out=o, lse=lse,
-                    stream=stream)
+        sq, sk, sv, so, slse = sets[n_step[0] % len(sets)]
+        n_step[0] += 1
+        ta.attn_fwd(sq, sk, sv, causal=w.causal, scale=float(inp.scale), seqlens_k=sl, q_start=qs, out=so,
+                    lse=slse, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -160,6 +176,22 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     achieved = tflops
     traffic = measured_traffic(w.name)
+    if hbm_probe:
+        gbs = w.algorithmic_bytes() / (ms_per_step * 1e-3) / 1e9
+        result = {
+            "metric": HBM_METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.N_q, "N_k": w.N_k, "d": w.d,
+                       "causal": w.causal, "varlen": False, "input_sets": len(sets)},
+            "tflops": round(tflops, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+            "launch_ms": {"mean": round(ms_per_step, 5)},
+            "wall_s_timed": round(wall, 4),
+        }
+        print(json.dumps(result), flush=True)
+        return
     result = {
         "metric": METRIC,
         "value": round(tflops, 2),

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 from oracle import attention, bf16_bits_to_f64, check
-from workloads import WORKLOADS, Workload, make_inputs, make_random, make_rising
+from workloads import HBM_PROBES, WORKLOADS, Workload, make_inputs, make_random, make_rising
 
 pytestmark = pytest.mark.gpu
 
@@ -203,7 +203,7 @@ def test_repeatable_bitwise():
 
 # ------------------------------------------------------------------ full-size workloads, sampled rows
 FULL = ["causal_n2048_d128", "causal_n4096_d128", "noncausal_n4096_d128", "varlen_n1024_d64",
-        "causal_n16384_d128_stress"]
+        "causal_n16384_d128_stress", *HBM_PROBES]
 
 
 def sample_rows(n, rng, count=48):
@@ -214,7 +214,7 @@ def sample_rows(n, rng, count=48):
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_workload_sampled(name):
-    w: Workload = WORKLOADS[name]
+    w: Workload = {**WORKLOADS, **HBM_PROBES}[name]
     inp = make_inputs(w)
     o, lse = run(inp.q, inp.k, inp.v, inp.scale, w.causal, inp.seqlens_k, inp.q_start)
     # properties of the whole output

@@ -4,7 +4,7 @@ import hashlib
 import numpy as np
 import pytest
 
-from workloads import WORKLOADS, f32_to_bf16_bits, make_inputs, make_random
+from workloads import HBM_PROBES, WORKLOADS, f32_to_bf16_bits, make_inputs, make_random
 
 
 def test_bf16_rounding_is_nearest_even():
@@ -51,3 +51,10 @@ def test_flops_formula():
     w = WORKLOADS["causal_n4096_d128"]
     assert w.flops() == 4 * 32 * 4096 * 4096 * 128 / 2
     assert WORKLOADS["noncausal_n4096_d128"].flops() == 4 * 32 * 4096 * 4096 * 128
+
+
+def test_hbm_probes_sit_below_the_ridge():
+    # counted flops per algorithmic byte below 2.5 PFLOP/s / 8 TB/s, inputs larger than the 256 MB cache
+    for w in HBM_PROBES.values():
+        assert w.flops() / w.algorithmic_bytes() < 2500.0 / 8.0
+        assert 3 * 2 * w.B * w.H * w.N_k * w.d > 256 << 20

@@ -85,6 +85,18 @@ WORKLOADS = {
                                           causal=True, seed=1005, sigma_q=2.0),
 }
 
+# Short sequences, where the kernel is bound by HBM bandwidth rather than by the
+# matrix cores: for square shapes the counted flops per algorithmic byte are
+# N/4 (causal) and N/2 (non-causal), 64 and 256 here, both below the MI355X
+# ridge of about 312 flop/B (2.5 PFLOP/s over 8 TB/s). Each input set is over
+# 500 MB, more than the 256 MB last-level cache.
+HBM_PROBES = {
+    "hbm_causal_n256_d128": Workload("hbm_causal_n256_d128", B=64, H=32, N_q=256, N_k=256, d=128, causal=True,
+                                     seed=1006),
+    "hbm_noncausal_n512_d128": Workload("hbm_noncausal_n512_d128", B=64, H=32, N_q=512, N_k=512, d=128,
+                                        causal=False, seed=1007),
+}
+
 HEADLINE = "causal_n4096_d128"
 
 
