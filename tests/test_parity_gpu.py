@@ -144,6 +144,29 @@ def test_running_max_rises_block_after_block(d, causal):
     compare_full(q, k, v, np.float32(d ** -0.5), causal)
 
 
+# A workgroup owns two query tiles. When the first tile's slice count is a
+# multiple of the ring depth, its last steps already copy the second tile's
+# first K/V slices and load its Q rows; these shapes take that path (causal
+# N = 1000 and non-causal N = 512 / varlen lengths that are multiples of 256 keys,
+# masked leading rows inside the second tile) next to ones that do not.
+CONT = [
+    # B, H, N, d, causal, seqlens, q_start
+    (1, 2, 1000, 128, True, None, None),
+    (1, 2, 1000, 64, True, None, None),
+    (2, 2, 512, 128, False, None, None),
+    (2, 1, 768, 64, False, [512, 256], [100, 0]),
+    (2, 1, 768, 128, True, [768, 700], [0, 260]),
+]
+
+
+@pytest.mark.parametrize("case", CONT, ids=[f"{c[0]}x{c[1]}x{c[2]}_d{c[3]}_{'c' if c[4] else 'n'}{'_var' if c[5] else ''}" for c in CONT])
+def test_ring_continues_into_second_tile(case):
+    B, H, n, d, causal, sl, qs = case
+    q, k, v = make_random(B, H, n, n, d, seed=n + d + B)
+    compare_full(q, k, v, np.float32(d ** -0.5), causal, None if sl is None else np.array(sl, np.int32),
+                 None if qs is None else np.array(qs, np.int32))
+
+
 def test_no_keys():
     import tiled_attention_16_amd as ta
     q = to_dev(make_random(1, 2, 40, 1, 64, seed=1)[0])
