@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the fused attention forward pass - TEST INFRASTRUCTURE.
+"""fp64 CPU oracle for the attention forward and backward passes - TEST INFRASTRUCTURE.
 
 Only the tests, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
 leg may import this package. The HIP library and its Python binding never do,
@@ -12,6 +12,12 @@ Parity status of each function (what pins it, all in ``tests/test_oracle.py``):
   attention_online  pinned against ``attention`` and the same closed forms.
   allowed_mask      pinned by brute-force loops over i, j.
   checker.check     pinned by planted mistakes (NaN, wrong -inf, out of band).
+  attention_bwd     pinned (tests/test_oracle_bwd.py): central finite
+                    differences of ``attention``, zero-sum of dK over keys,
+                    zero gradients for dO = 0 and for V with equal rows, the
+                    Q = 0 closed form of dV, torch CPU fp64 autograd cross-check.
+  check_grads       pinned by planted mistakes (NaN, out of band).
 """
 from .attention import allowed_mask, attention, attention_online, bf16_bits_to_f64  # noqa: F401
-from .checker import check, CheckResult  # noqa: F401
+from .backward import attention_bwd  # noqa: F401
+from .checker import check, check_grads, CheckResult, GradCheckResult  # noqa: F401

@@ -83,3 +83,55 @@ def check(o_test: np.ndarray, o_ref: np.ndarray, lse_test: Optional[np.ndarray] 
                 if lse_max > LSE_MAX_ABS:
                     reasons.append(f"LSE max abs {lse_max:.3e} > {LSE_MAX_ABS}")
     return CheckResult(not reasons, o_max, o_mean, lse_max, reasons)
+
+
+# Gradients (the backward pass). The benchmark statement fixes no tolerance for
+# them, so the bars follow the forward's, relative to each tensor's size: a
+# bf16 result carries a rounding error of at most 2**-9 of its magnitude, and
+# the bf16 rounding of the recomputed probabilities and score gradients that
+# feed the matrix products adds errors of the same relative size with random
+# signs, which mostly cancel in the sums.
+GRAD_MAX_REL = 2e-2     # max |d| <= GRAD_MAX_REL * max(1, max |ref|)
+GRAD_MEAN_REL = 2e-3    # mean |d| <= GRAD_MEAN_REL * max(1, mean |ref|)
+
+
+@dataclass
+class GradCheckResult:
+    ok: bool
+    stats: dict
+    reasons: list
+
+    def __str__(self) -> str:
+        state = "PASS" if self.ok else "FAIL"
+        parts = [f"{n} max|d|={s[0]:.3e} (bar {s[1]:.2e}) mean|d|={s[2]:.3e} (bar {s[3]:.2e})"
+                 for n, s in self.stats.items()]
+        return f"{state} " + "; ".join(parts) + ("" if self.ok else " :: " + "; ".join(self.reasons))
+
+
+def check_grads(test: dict, ref: dict) -> GradCheckResult:
+    """Compare tested gradients with the oracle's, tensor by tensor.
+
+    ``test`` and ``ref`` map names ("dq", "dk", "dv") to float64 views of
+    equal shape. Any NaN or Inf in a tested tensor fails.
+    """
+    reasons, stats = [], {}
+    for name, r in ref.items():
+        r = np.asarray(r, dtype=np.float64)
+        t = np.asarray(test[name], dtype=np.float64)
+        if t.shape != r.shape:
+            reasons.append(f"{name} shape {t.shape} != {r.shape}")
+            continue
+        if not np.all(np.isfinite(t)):
+            reasons.append(f"{name} has {int(np.sum(~np.isfinite(t)))} non-finite values")
+        d = np.abs(t - r)
+        d = np.where(np.isfinite(d), d, np.inf)
+        mx = float(d.max()) if d.size else 0.0
+        mn = float(d.mean()) if d.size else 0.0
+        bar_max = GRAD_MAX_REL * max(1.0, float(np.abs(r).max()) if r.size else 0.0)
+        bar_mean = GRAD_MEAN_REL * max(1.0, float(np.abs(r).mean()) if r.size else 0.0)
+        stats[name] = (mx, bar_max, mn, bar_mean)
+        if mx > bar_max:
+            reasons.append(f"{name} max abs {mx:.3e} > {bar_max:.3e}")
+        if mn > bar_mean:
+            reasons.append(f"{name} mean abs {mn:.3e} > {bar_mean:.3e}")
+    return GradCheckResult(not reasons, stats, reasons)

@@ -45,3 +45,49 @@ def test_pins_catch_planted_mistake(tmp_path, desc, old, new):
                           "tests/test_oracle.py", "-k", "not online"],
                          cwd=tmp_path, capture_output=True, text=True, timeout=300)
     assert res.returncode != 0, f"no pin caught the planted mistake '{desc}'"
+
+
+# (description, literal text in oracle/backward.py, replacement)
+BWD_MUTANTS = [
+    ("softmax correction dropped", "ds = pb * (dp - (pb * dp).sum(axis=1, keepdims=True))", "ds = pb * dp"),
+    ("softmax correction sign", "ds = pb * (dp - (pb * dp).sum(axis=1, keepdims=True))",
+     "ds = pb * (dp + (pb * dp).sum(axis=1, keepdims=True))"),
+    ("correction summed over rows", "(pb * dp).sum(axis=1, keepdims=True)", "(pb * dp).sum(axis=0, keepdims=True)"),
+    ("dK without scale", "dk[b, h] = sc * (ds.T @ q[b, h])", "dk[b, h] = ds.T @ q[b, h]"),
+    ("dQ from V", "dq[b, h] = sc * (ds @ k[b, h])", "dq[b, h] = sc * (ds @ v[b, h])"),
+    ("dP from K", "dp = g[b, h] @ v[b, h].T", "dp = g[b, h] @ k[b, h].T"),
+    ("dV keys reversed", "dv[b, h] = pb.T @ g[b, h]", "dv[b, h] = pb.T[::-1] @ g[b, h]"),
+    ("dK from untransposed dS", "dk[b, h] = sc * (ds.T @ q[b, h])", "dk[b, h] = sc * (ds[:, ::-1].T @ q[b, h])"),
+]
+
+
+@pytest.mark.parametrize("desc,old,new", BWD_MUTANTS, ids=[m[0] for m in BWD_MUTANTS])
+def test_backward_pins_catch_planted_mistake(tmp_path, desc, old, new):
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle")
+    src = (tmp_path / "oracle" / "backward.py").read_text(encoding="utf-8")
+    assert old in src, f"mutation site for '{desc}' not found"
+    (tmp_path / "oracle" / "backward.py").write_text(src.replace(old, new, 1), encoding="utf-8")
+    (tmp_path / "tests").mkdir()
+    shutil.copy(os.path.join(HERE, "test_oracle_bwd.py"), tmp_path / "tests")
+    (tmp_path / "tests" / "conftest.py").write_text(
+        "import os, sys\nsys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))\n")
+    res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                          "tests/test_oracle_bwd.py", "-k", "not checker"],
+                         cwd=tmp_path, capture_output=True, text=True, timeout=300)
+    assert res.returncode != 0, f"no pin caught the planted mistake '{desc}'"
+
+
+@pytest.mark.parametrize("module,test_file,select", [("attention.py", "test_oracle.py", "not online"),
+                                                      ("backward.py", "test_oracle_bwd.py", "not checker")])
+def test_unmutated_copy_passes(tmp_path, module, test_file, select):
+    """Control for the two tests above: the same harness passes the oracle as it is."""
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle")
+    (tmp_path / "tests").mkdir()
+    shutil.copy(os.path.join(HERE, test_file), tmp_path / "tests")
+    shutil.copytree(os.path.join(HERE, "golden"), tmp_path / "tests" / "golden")
+    (tmp_path / "tests" / "conftest.py").write_text(
+        "import os, sys\nsys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))\n")
+    res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                          f"tests/{test_file}", "-k", select], cwd=tmp_path, capture_output=True, text=True,
+                         timeout=300)
+    assert res.returncode == 0, res.stdout[-2000:]
