@@ -86,13 +86,18 @@ def check(o_test: np.ndarray, o_ref: np.ndarray, lse_test: Optional[np.ndarray] 
 
 
 # Gradients (the backward pass). The benchmark statement fixes no tolerance for
-# them, so the bars follow the forward's, relative to each tensor's size: a
-# bf16 result carries a rounding error of at most 2**-9 of its magnitude, and
-# the bf16 rounding of the recomputed probabilities and score gradients that
-# feed the matrix products adds errors of the same relative size with random
-# signs, which mostly cancel in the sums.
+# them, so the bars are derived from bf16's 8-bit significand, relative to each
+# tensor's size. A bf16 result carries a rounding error of at most 2**-9 of its
+# magnitude (about 2**-10.5 on average), and the bf16 rounding of the
+# recomputed probabilities and score gradients that feed the matrix products
+# adds errors of the same relative size; in rows where a few keys dominate they
+# do not cancel, so the mean error is a few times 2**-10 of the mean magnitude.
+# Bars: the max against the forward's 2e-2 scaled by the largest magnitude, the
+# mean against 1 % of the mean magnitude (about 3x the expected error; a wrong
+# index, sign or term gives errors of the order of the values themselves).
 GRAD_MAX_REL = 2e-2     # max |d| <= GRAD_MAX_REL * max(1, max |ref|)
-GRAD_MEAN_REL = 2e-3    # mean |d| <= GRAD_MEAN_REL * max(1, mean |ref|)
+GRAD_MEAN_REL = 1e-2    # mean |d| <= GRAD_MEAN_REL * mean |ref| + GRAD_MEAN_FLOOR
+GRAD_MEAN_FLOOR = 1e-6
 
 
 @dataclass
@@ -128,7 +133,7 @@ def check_grads(test: dict, ref: dict) -> GradCheckResult:
         mx = float(d.max()) if d.size else 0.0
         mn = float(d.mean()) if d.size else 0.0
         bar_max = GRAD_MAX_REL * max(1.0, float(np.abs(r).max()) if r.size else 0.0)
-        bar_mean = GRAD_MEAN_REL * max(1.0, float(np.abs(r).mean()) if r.size else 0.0)
+        bar_mean = GRAD_MEAN_REL * (float(np.abs(r).mean()) if r.size else 0.0) + GRAD_MEAN_FLOOR
         stats[name] = (mx, bar_max, mn, bar_mean)
         if mx > bar_max:
             reasons.append(f"{name} max abs {mx:.3e} > {bar_max:.3e}")

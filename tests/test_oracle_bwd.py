@@ -141,7 +141,13 @@ def test_grad_checker_bars():
     bad["dv"][0, 0] += 0.2       # above 2e-2 * 5
     assert not check_grads(bad, r).ok
     bad = {k: v.copy() for k, v in r.items()}
-    bad["dk"][:] = 3e-3          # mean above 2e-3
+    bad["dq"][:] += 0.011        # mean above 1 % of mean |dq| = 1
+    assert not check_grads(bad, r).ok
+    ok = {k: v.copy() for k, v in r.items()}
+    ok["dq"][:] += 0.009
+    assert check_grads(ok, r).ok
+    bad = {k: v.copy() for k, v in r.items()}
+    bad["dk"][0, 0] = 1e-4       # the reference is all zeros: only the 1e-6 floor remains
     assert not check_grads(bad, r).ok
     bad = {k: v.copy() for k, v in r.items()}
     bad["dq"][1, 2] = np.nan
