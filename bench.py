@@ -44,6 +44,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, published
 METRIC = "attention fwd TFLOP/s (bf16, causal, N=4096, d=128) + % of MFMA bf16 peak"
 HBM_METRIC = "attention fwd achieved HBM GB/s (bf16, short sequences) + % of HBM peak"
+BWD_METRIC = "attention bwd TFLOP/s (bf16, dQ dK dV, counted 10*B*H*N_q*N_k*d, halved when causal) + % of MFMA bf16 peak"
 KERNEL_SRC = os.path.join(ROOT, "tiled_attention_16_amd", "csrc", "attn_fwd.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -114,6 +115,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(ALL_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time attn_bwd (dQ, dK, dV; its three launches) instead of the forward; O and LSE come "
+                         "from one attn_fwd call before the timed region")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device copies of MIB MiB each (the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
@@ -149,6 +153,8 @@ def main():
             sets.append(tuple(t.clone() for t in sets[0][:3]) + (torch.empty_like(q), torch.empty_like(sets[0][4])))
     stream = torch.cuda.current_stream(dev)
     n_step = [0]
+    if args.backward:
+        return bench_backward(args, torch, ta, w, inp, sets[0], sl, qs, stream, dev)
 
     def step():
         sq, sk, sv, so, slse = sets[n_step[0] % len(sets)]
@@ -217,6 +223,82 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(result), flush=True)
+
+
+def bench_backward(args, torch, ta, w, inp, tensors, sl, qs, stream, dev):
+    """Time the backward pass: a step is one attn_bwd call (Delta, dQ, dK/dV kernels)."""
+    from workloads import make_dout
+
+    q, k, v, o, lse = tensors
+    g = torch.from_numpy(make_dout((w.B, w.H, w.N_q, w.d), seed=w.seed + 500).view(np.int16)).to(dev).view(
+        torch.bfloat16)
+    ta.attn_fwd(q, k, v, causal=w.causal, scale=float(inp.scale), seqlens_k=sl, q_start=qs, out=o, lse=lse,
+                stream=stream)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((w.B, w.H, w.N_q), dtype=torch.float32, device=dev)
+
+    def step():
+        ta.attn_bwd(q, k, v, o, lse, g, causal=w.causal, scale=float(inp.scale), seqlens_k=sl, q_start=qs, dq=dq,
+                    dk=dk, dv=dv, delta=delta, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    e_end.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ms = e_start.elapsed_time(e_end) / args.steps
+    flops = 2.5 * w.flops()   # five N_q x N_k x d products (S, dP, dV, dK, dQ) against the forward's two
+    tflops = flops / (ms * 1e-3) / 1e12
+    result = {
+        "metric": BWD_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.N_q, "N_k": w.N_k, "d": w.d, "causal": w.causal,
+                   "varlen": inp.seqlens_k is not None, "pass": "backward"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "launch_ms": {"mean": round(ms, 5)},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_backward(w, inp)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_backward(w, inp, budget_s: float = 12.0):
+    """Time the fp64 backward oracle on whole heads of the workload until the budget is spent."""
+    import threadpoolctl
+
+    from oracle import attention_bwd, bf16_bits_to_f64
+    from workloads import make_dout
+
+    g = make_dout((w.B, w.H, w.N_q, w.d), seed=w.seed + 500)
+    heads_done = 0
+    t0 = time.perf_counter()
+    b = 0
+    for h in range(w.H):
+        sl = None if inp.seqlens_k is None else inp.seqlens_k[b:b + 1]
+        qs = None if inp.q_start is None else inp.q_start[b:b + 1]
+        attention_bwd(bf16_bits_to_f64(inp.q[b:b + 1, h:h + 1]), bf16_bits_to_f64(inp.k[b:b + 1, h:h + 1]),
+                      bf16_bits_to_f64(inp.v[b:b + 1, h:h + 1]), bf16_bits_to_f64(g[b:b + 1, h:h + 1]),
+                      float(inp.scale), w.causal, seqlens_k=sl, q_start=qs)
+        heads_done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 2.5 * w.flops() / (w.B * w.H) * heads_done
+    blas = [d.get("num_threads", 1) for d in threadpoolctl.threadpool_info() if d.get("user_api") == "blas"]
+    cores = max(blas) if blas else 1
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 backward oracle on {heads_done} of {w.B * w.H} (batch, head) pairs of {w.name}, "
+                      f"{dt:.1f} s wall; {len(os.sched_getaffinity(0))} host cores visible",
+            "seconds": dt}
 
 
 if __name__ == "__main__":

@@ -1,5 +1,5 @@
 /*
- * attn.h - C ABI of the MI355X (gfx950) fused attention forward library.
+ * attn.h - C ABI of the MI355X (gfx950) fused attention library (forward and backward).
  *
  * Pages cited:
  *   [PT2CUDA]  aiknowledge.cn, "4.5 注意力优化实战：从PyTorch到CUDA的完整流程".
@@ -42,15 +42,15 @@
 extern "C" {
 #endif
 
-/* Status codes returned by attn_fwd. */
+/* Status codes returned by attn_fwd and attn_bwd. */
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,      /* a required pointer is NULL                          */
   ATTN_ERR_SHAPE = 2,     /* a size is negative or the problem is too large      */
   ATTN_ERR_HEAD_DIM = 3,  /* d is not 64 or 128                                  */
   ATTN_ERR_SCALE = 4,     /* scale is NaN or infinite                            */
-  ATTN_ERR_ALIGN = 5,     /* q, k, v or o not 16-byte aligned, lse not 4-byte    */
-  ATTN_ERR_ALIAS = 6,     /* o or lse overlaps an input or each other            */
+  ATTN_ERR_ALIGN = 5,     /* a bf16 tensor not 16-byte aligned, lse/delta 4-byte */
+  ATTN_ERR_ALIAS = 6,     /* an output overlaps an input or another output       */
   ATTN_ERR_LAUNCH = 7     /* the kernel launch failed (hipGetLastError)          */
 } attn_status;
 
@@ -87,6 +87,41 @@ typedef enum {
  * q_start are never read on the host.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int N_q, int N_k, int d, float scale, int causal,
+             const int32_t* seqlens_k, const int32_t* q_start, hipStream_t stream);
+
+/*
+ * attn_bwd - gradients of attn_fwd: dQ, dK, dV (bf16) from dO (bf16).
+ *
+ * The backward kernel of [PT2CUDA] step 4.2: dQ sweeps every K/V block, dK and
+ * dV sweep every Q block, and the probabilities are recomputed from the
+ * forward's log-sum-exp instead of being stored. With S, P and the mask of
+ * attn_fwd (same q, k, v, scale, causal, seqlens_k, q_start):
+ *   P  = exp(S - LSE) on allowed entries, 0 elsewhere;
+ *   dV = P^T dO;   dP = dO V^T;   Delta_i = sum_d dO_id O_id;
+ *   dS = P * (dP - Delta);   dQ = scale * dS K;   dK = scale * dS^T Q.
+ * A row with no allowed key (LSE = -inf) contributes nothing; its dQ row is 0.
+ * Keys at or beyond kv_len[b] get dK = dV = 0. Three kernel launches on
+ * `stream` (Delta, then dQ, then dK and dV).
+ *
+ * Arguments (device memory owned by the caller; nothing is allocated, freed,
+ * synchronised or kept):
+ *   q, k, v     the forward's inputs (layouts as in attn_fwd), read only.
+ *   o, lse      the forward's outputs for exactly these inputs and mask: bf16
+ *               [B, H, N_q, d] and float32 [B, H, N_q], read only.
+ *   dout        bf16 [B, H, N_q, d], the gradient of the loss with respect to o.
+ *   dq          bf16 [B, H, N_q, d], written in full.
+ *   dk, dv      bf16 [B, H, N_k, d], written in full.
+ *   delta       float32 [B, H, N_q] workspace, overwritten (Delta above).
+ *   B .. q_start, stream  as in attn_fwd.
+ * q, o, dout, lse, dq and delta may be NULL iff N_q == 0; k, v, dk and dv iff
+ * N_k == 0. Alignment: the bf16 tensors 16 bytes, lse and delta 4 bytes.
+ * No output (dq, dk, dv, delta) may overlap an input or another output.
+ * Errors as in attn_fwd: argument errors return before any HIP call; when
+ * B*H == 0 or N_q == N_k == 0 the call returns ATTN_OK without launching.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, float* delta,
              int B, int H, int N_q, int N_k, int d, float scale, int causal,
              const int32_t* seqlens_k, const int32_t* q_start, hipStream_t stream);
 

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert ta.attn_version() == 100
+    assert ta.attn_version() == 10100
     for code in range(8):
         s = ta.attn_status_str(code)
         assert s and s != "unknown status"
@@ -96,3 +96,35 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(ta, "_LIB_PATH", "/nonexistent/libattn.so")
     with pytest.raises(RuntimeError):
         ta.load_library()
+
+
+def call_bwd(**kw):
+    args = dict(q=A16, k=A16 * 2, v=A16 * 3, o=A16 * 4, dout=A16 * 5, lse=A16 * 6, dq=A16 * 7, dk=A16 * 8,
+                dv=A16 * 9, delta=A16 * 10, B=1, H=2, N_q=8, N_k=8, d=64, scale=0.125, causal=False, seqlens_k=0,
+                q_start=0, stream=0)
+    args.update(kw)
+    return ta.attn_bwd_raw(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=-1), ta.ATTN_ERR_SHAPE),
+    (dict(d=32), ta.ATTN_ERR_HEAD_DIM),
+    (dict(scale=float("-inf")), ta.ATTN_ERR_SCALE),
+    (dict(dout=0), ta.ATTN_ERR_NULL),
+    (dict(lse=0), ta.ATTN_ERR_NULL),
+    (dict(delta=0), ta.ATTN_ERR_NULL),
+    (dict(dk=0), ta.ATTN_ERR_NULL),
+    (dict(dq=A16 * 7 + 8), ta.ATTN_ERR_ALIGN),
+    (dict(dout=A16 * 5 + 4), ta.ATTN_ERR_ALIGN),
+    (dict(delta=A16 * 10 + 2), ta.ATTN_ERR_ALIGN),
+    (dict(dq=A16 * 5 + 16), ta.ATTN_ERR_ALIAS),       # dq overlaps dout
+    (dict(dv=A16 * 8 + 32), ta.ATTN_ERR_ALIAS),       # dv overlaps dk
+    (dict(delta=A16 * 6), ta.ATTN_ERR_ALIAS),         # delta is lse
+])
+def test_bwd_argument_errors_return_before_any_hip_call(lib, kw, status):
+    assert call_bwd(**kw) == status
+
+
+def test_bwd_empty_problem_is_a_noop(lib):
+    assert call_bwd(B=0, q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0, delta=0) == ta.ATTN_OK
+    assert call_bwd(N_q=0, N_k=0, q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0, delta=0) == ta.ATTN_OK

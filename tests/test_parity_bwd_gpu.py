@@ -1,0 +1,157 @@
+"""Parity of the HIP attention backward (attn_bwd) with the fp64 CPU oracle (needs the GPU).
+
+The forward (attn_fwd) runs on the GPU to give O and LSE, as in training; the
+oracle computes dQ, dK, dV from the bf16 inputs alone (it takes neither O nor
+LSE from the GPU). Bars (oracle/checker.py): per gradient, max |d| <= 2e-2 *
+max(1, max |ref|) and mean |d| <= 1e-2 * mean |ref| + 1e-6.
+"""
+import numpy as np
+import pytest
+
+from oracle import attention_bwd, bf16_bits_to_f64, check_grads
+from workloads import WORKLOADS, make_dout, make_inputs, make_random
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tiled_attention_16_amd as ta
+    ta.load_library()
+    return ta
+
+
+def to_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def f64(t):
+    return bf16_bits_to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+def run_bwd(q, k, v, g, scale, causal, seqlens=None, qstart=None):
+    import tiled_attention_16_amd as ta
+    print(f"  bwd B,H,Nq,Nk,d={q.shape[0]},{q.shape[1]},{q.shape[2]},{k.shape[2]},{q.shape[3]} causal={causal} "
+          f"seqlens={seqlens is not None} q_start={qstart is not None}", flush=True)
+    sl = torch.from_numpy(np.asarray(seqlens, np.int32)).cuda() if seqlens is not None else None
+    qs = torch.from_numpy(np.asarray(qstart, np.int32)).cuda() if qstart is not None else None
+    tq, tk, tv, tg = to_dev(q), to_dev(k), to_dev(v), to_dev(g)
+    o, lse = ta.attn_fwd(tq, tk, tv, causal=causal, scale=float(scale), seqlens_k=sl, q_start=qs)
+    dq, dk, dv = ta.attn_bwd(tq, tk, tv, o, lse, tg, causal=causal, scale=float(scale), seqlens_k=sl, q_start=qs)
+    torch.cuda.synchronize()
+    return f64(dq), f64(dk), f64(dv)
+
+
+def compare(q, k, v, g, scale, causal, seqlens=None, qstart=None):
+    dq, dk, dv = run_bwd(q, k, v, g, scale, causal, seqlens, qstart)
+    rq, rk, rv = attention_bwd(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), bf16_bits_to_f64(g),
+                               float(scale), causal, seqlens_k=seqlens, q_start=qstart)
+    r = check_grads({"dq": dq, "dk": dk, "dv": dv}, {"dq": rq, "dk": rk, "dv": rv})
+    print("  ", r, flush=True)
+    assert r.ok, str(r)
+    return dq, dk, dv
+
+
+SHAPES = [
+    # B, H, N_q, N_k, d, causal
+    (1, 1, 1, 1, 64, False),
+    (1, 2, 64, 64, 64, True),
+    (1, 2, 200, 200, 128, False),     # ragged tails
+    (2, 1, 129, 65, 128, False),      # one row / one key past a block
+    (1, 1, 100, 300, 64, True),       # N_q < N_k
+    (1, 1, 300, 77, 128, True),       # N_q > N_k
+    (1, 2, 256, 256, 128, True),      # whole tiles
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{s[0]}x{s[1]}x{s[2]}x{s[3]}_d{s[4]}_{'c' if s[5] else 'n'}" for s in SHAPES])
+def test_bwd_shapes(shape):
+    B, H, nq, nk, d, causal = shape
+    q, k, v = make_random(B, H, nq, nk, d, seed=3 * nq + nk + d)
+    g = make_dout((B, H, nq, d), seed=nq + 5 * nk)
+    compare(q, k, v, g, np.float32(d ** -0.5), causal)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_varlen_and_masked_rows(d, causal):
+    B, H, n = 4, 2, 200
+    q, k, v = make_random(B, H, n, n, d, seed=200 + d)
+    g = make_dout((B, H, n, d), seed=300 + d)
+    seqlens = np.array([0, 63, 150, 200], np.int32)
+    qstart = np.array([0, 64, 10, 200], np.int32)
+    dq, dk, dv = compare(q, k, v, g, np.float32(d ** -0.5), causal, seqlens, qstart)
+    assert np.all(dq[0] == 0) and np.all(dk[0] == 0) and np.all(dv[0] == 0)   # no keys
+    assert np.all(dq[3] == 0) and np.all(dk[3] == 0) and np.all(dv[3] == 0)   # every row masked
+    assert np.all(dq[1, :, :64] == 0)                                         # masked leading rows
+    assert np.all(dk[2, :, 150:] == 0) and np.all(dv[2, :, 150:] == 0)        # keys past the valid length
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.3])
+def test_bwd_scale_values(scale):
+    q, k, v = make_random(1, 2, 130, 130, 128, seed=41)
+    g = make_dout((1, 2, 130, 128), seed=42)
+    compare(q, k, v, g, np.float32(scale), True)
+
+
+def test_bwd_large_logits():
+    q, k, v = make_random(1, 2, 300, 300, 128, seed=43, sigma=(4.0, 1.0, 1.0))
+    g = make_dout((1, 2, 300, 128), seed=44)
+    compare(q, k, v, g, np.float32(128 ** -0.5), True)
+
+
+def test_bwd_every_element_written():
+    import tiled_attention_16_amd as ta
+    B, H, n, d = 2, 2, 150, 64
+    q, k, v = make_random(B, H, n, n, d, seed=45)
+    tq, tk, tv, tg = to_dev(q), to_dev(k), to_dev(v), to_dev(make_dout((B, H, n, d), seed=46))
+    sl = torch.tensor([90, 150], dtype=torch.int32, device="cuda")
+    o, lse = ta.attn_fwd(tq, tk, tv, causal=True, seqlens_k=sl)
+    nan = lambda t: torch.full_like(t, float("nan"))  # noqa: E731
+    dq, dk, dv = ta.attn_bwd(tq, tk, tv, o, lse, tg, causal=True, seqlens_k=sl, dq=nan(tq), dk=nan(tk), dv=nan(tv))
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert not torch.isnan(t).any().item()
+
+
+def test_bwd_repeatable_bitwise():
+    q, k, v = make_random(1, 2, 500, 500, 128, seed=47)
+    g = make_dout((1, 2, 500, 128), seed=48)
+    a = run_bwd(q, k, v, g, np.float32(128 ** -0.5), True)
+    b = run_bwd(q, k, v, g, np.float32(128 ** -0.5), True)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("name", ["causal_n4096_d128", "varlen_n1024_d64"])
+def test_bwd_full_size_heads(name):
+    """The workload at full size, launched as the benchmark launches it; the
+    oracle checks two whole (batch, head) slices."""
+    import tiled_attention_16_amd as ta
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    g = make_dout((w.B, w.H, w.N_q, w.d), seed=w.seed + 500)
+    sl = torch.from_numpy(inp.seqlens_k).cuda() if inp.seqlens_k is not None else None
+    qs = torch.from_numpy(inp.q_start).cuda() if inp.q_start is not None else None
+    tq, tk, tv, tg = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), to_dev(g)
+    o, lse = ta.attn_fwd(tq, tk, tv, causal=w.causal, scale=float(inp.scale), seqlens_k=sl, q_start=qs)
+    dq, dk, dv = ta.attn_bwd(tq, tk, tv, o, lse, tg, causal=w.causal, scale=float(inp.scale), seqlens_k=sl,
+                             q_start=qs)
+    torch.cuda.synchronize()
+    dq, dk, dv = f64(dq), f64(dk), f64(dv)
+    for t in (dq, dk, dv):
+        assert np.all(np.isfinite(t))
+    for b, h in [(0, 0), (w.B - 1, w.H - 1)]:
+        sb = None if inp.seqlens_k is None else inp.seqlens_k[b:b + 1]
+        qb = None if inp.q_start is None else inp.q_start[b:b + 1]
+        rq, rk, rv = attention_bwd(bf16_bits_to_f64(inp.q[b:b + 1, h:h + 1]), bf16_bits_to_f64(inp.k[b:b + 1, h:h + 1]),
+                                   bf16_bits_to_f64(inp.v[b:b + 1, h:h + 1]), bf16_bits_to_f64(g[b:b + 1, h:h + 1]),
+                                   float(inp.scale), w.causal, seqlens_k=sb, q_start=qb)
+        r = check_grads({"dq": dq[b:b + 1, h:h + 1], "dk": dk[b:b + 1, h:h + 1], "dv": dv[b:b + 1, h:h + 1]},
+                        {"dq": rq, "dk": rk, "dv": rv})
+        print(f"  {name} b={b} h={h}: {r}", flush=True)
+        assert r.ok, f"{name} b={b} h={h}: {r}"

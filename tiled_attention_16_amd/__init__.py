@@ -1,7 +1,7 @@
-"""Python binding of the MI355X fused attention forward library (``libattn.so``).
+"""Python binding of the MI355X fused attention library (``libattn.so``).
 
 Argument marshalling only: every step of the computation runs in the HIP
-kernel behind ``attn_fwd`` in ``include/attn.h``. PyTorch supplies device
+kernels behind ``attn_fwd`` and ``attn_bwd`` in ``include/attn.h``. PyTorch supplies device
 memory and the current stream. There is no fallback: if the library is
 missing or the tensors are not on a GPU, the call raises.
 """
@@ -24,7 +24,7 @@ ATTN_ERR_ALIAS = 6
 ATTN_ERR_LAUNCH = 7
 
 # every symbol include/attn.h declares
-EXPORTS = ("attn_fwd", "attn_status_str", "attn_version")
+EXPORTS = ("attn_bwd", "attn_fwd", "attn_status_str", "attn_version")
 
 _lib = None
 
@@ -43,6 +43,9 @@ def load_library() -> ctypes.CDLL:
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
     ]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int] + \
+        [ctypes.c_void_p] * 3
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_version.restype = ctypes.c_int
@@ -60,8 +63,8 @@ def attn_version() -> int:
 
 
 class AttnError(RuntimeError):
-    def __init__(self, status: int):
-        super().__init__(f"attn_fwd failed: {attn_status_str(status)} (status {status})")
+    def __init__(self, status: int, name: str = "attn_fwd"):
+        super().__init__(f"{name} failed: {attn_status_str(status)} (status {status})")
         self.status = status
 
 
@@ -117,3 +120,65 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None, se
     if status != ATTN_OK:
         raise AttnError(status)
     return out, (lse if return_lse else None)
+
+
+def attn_bwd_raw(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int, delta: int,
+                 B: int, H: int, N_q: int, N_k: int, d: int, scale: float, causal: bool, seqlens_k: int,
+                 q_start: int, stream: int) -> int:
+    """The C entry point ``attn_bwd`` with plain integers for pointers; returns the status code."""
+    p = [x or None for x in (q, k, v, o, dout, lse, dq, dk, dv, delta)]
+    return int(load_library().attn_bwd(*p, int(B), int(H), int(N_q), int(N_k), int(d), ctypes.c_float(scale),
+                                       1 if causal else 0, seqlens_k or None, q_start or None, stream or None))
+
+
+def attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] = None, seqlens_k=None,
+             q_start=None, dq=None, dk=None, dv=None, delta=None, stream=None):
+    """Gradients ``(dq, dk, dv)`` of ``attn_fwd`` for upstream gradient ``dout``.
+
+    ``o`` and ``lse`` are ``attn_fwd``'s outputs for the same inputs, mask and
+    scale. All tensors are contiguous GPU tensors: q, o, dout bf16
+    ``[B, H, N_q, d]``; k, v bf16 ``[B, H, N_k, d]``; lse float32 ``[B, H, N_q]``.
+    ``delta`` (float32 ``[B, H, N_q]``) is the kernels' workspace; it is
+    allocated here when not given.
+    """
+    import torch
+
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise ValueError(f"{name} must be a bfloat16 GPU tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+    B, H, N_q, d = q.shape
+    if k.shape[:2] != (B, H) or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must be shaped like q")
+    N_k = k.shape[2]
+    if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or not lse.is_cuda or \
+            lse.shape != (B, H, N_q) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N_q] GPU tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    for name, t in (("seqlens_k", seqlens_k), ("q_start", q_start)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_cuda or t.numel() != B or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 GPU tensor of {B} elements")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 tensor shaped like {name[1:]}")
+    if delta is None:
+        delta = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
+    elif delta.shape != (B, H, N_q) or delta.dtype != torch.float32 or not delta.is_contiguous():
+        raise ValueError("delta must be a contiguous float32 [B, H, N_q] tensor")
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    ptr = lambda t: t.data_ptr() or None  # noqa: E731
+    status = lib.attn_bwd(ptr(q), ptr(k), ptr(v), ptr(o), ptr(dout), ptr(lse), ptr(dq), ptr(dk), ptr(dv),
+                          ptr(delta), B, H, N_q, N_k, d, ctypes.c_float(scale), 1 if causal else 0,
+                          seqlens_k.data_ptr() if seqlens_k is not None else None,
+                          q_start.data_ptr() if q_start is not None else None, ctypes.c_void_p(st.cuda_stream))
+    if status != ATTN_OK:
+        raise AttnError(status, "attn_bwd")
+    return dq, dk, dv

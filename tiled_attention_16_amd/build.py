@@ -1,4 +1,4 @@
-"""Compile the HIP library ``libattn.so`` for gfx950 in-tree.
+"""Compile the HIP library ``libattn.so`` (forward and backward kernels) for gfx950 in-tree.
 
 Usage: ``python -m tiled_attention_16_amd.build`` (or ``build_library()``).
 """
@@ -10,7 +10,7 @@ import sys
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 REPO_DIR = os.path.dirname(PKG_DIR)
-SRC = os.path.join(PKG_DIR, "csrc", "attn_fwd.hip")
+SRCS = [os.path.join(PKG_DIR, "csrc", "attn_fwd.hip"), os.path.join(PKG_DIR, "csrc", "attn_bwd.hip")]
 LIB = os.path.join(PKG_DIR, "libattn.so")
 
 HIPCC_FLAGS = [
@@ -37,9 +37,10 @@ def build_library(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     asm = LIB + ".s.tmp"
     inc = ["-I", os.path.join(REPO_DIR, "include")]
-    cmd = [hipcc, *HIPCC_FLAGS, *inc, SRC, "-o", tmp]
+    cmd = [hipcc, *HIPCC_FLAGS, *inc, *SRCS, "-o", tmp]
     flags_s = [f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
-    cmd_s = [hipcc, *flags_s, *inc, "--cuda-device-only", "-S", SRC, "-o", asm]
+    # the forward kernel's hand-placed MFMAs are the ones the hazard check is for
+    cmd_s = [hipcc, *flags_s, *inc, "--cuda-device-only", "-S", SRCS[0], "-o", asm]
     procs = [subprocess.Popen(c, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True) for c in (cmd, cmd_s)]
     outs = [p.communicate() for p in procs]
     for c, p, (out, err) in zip((cmd, cmd_s), procs, outs):

@@ -807,11 +807,11 @@ extern "C" const char* attn_status_str(int status) {
     case ATTN_ERR_SHAPE: return "invalid or too large shape";
     case ATTN_ERR_HEAD_DIM: return "head dim must be 64 or 128";
     case ATTN_ERR_SCALE: return "scale must be finite";
-    case ATTN_ERR_ALIGN: return "misaligned pointer (q, k, v, o need 16 bytes, lse 4)";
+    case ATTN_ERR_ALIGN: return "misaligned pointer (bf16 tensors need 16 bytes, lse and delta 4)";
     case ATTN_ERR_ALIAS: return "output overlaps an input or the other output";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
   }
 }
 
-extern "C" int attn_version(void) { return 100; }
+extern "C" int attn_version(void) { return 10100; }

@@ -159,3 +159,10 @@ def make_rising(B: int, H: int, N_q: int, N_k: int, d: int, seed: int, step: flo
     v = g.standard_normal((B, H, N_k, d), dtype=np.float32)
     return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
 
+
+
+def make_dout(shape, seed: int, sigma: float = 1.0):
+    """Seeded bf16 bits of an upstream gradient dO of the given shape (the
+    backward pass's extra input): iid N(0, sigma^2), drawn after nothing else."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    return f32_to_bf16_bits(g.standard_normal(tuple(shape), dtype=np.float32) * np.float32(sigma))
