@@ -6,11 +6,12 @@
 // forward kept (its row statistics; here the log-sum-exp).
 //
 // What one call computes is stated in include/attn.h. Three launches:
-//   delta  D_i = sum_d dO_id * O_id (fp32), the row sum of P * dP that the
-//          softmax Jacobian needs (sum_j P_ij dP_ij = dO_i . O_i).
+//   delta  per row (LSE * log2 e, D_i) with D_i = sum_d dO_id * O_id (fp32), the
+//          row sum of P * dP that the softmax Jacobian needs
+//          (sum_j P_ij dP_ij = dO_i . O_i).
 //   dq     one workgroup of 4 wave64s per 128 query rows; each wave keeps its
 //          32 rows of Q and dO in registers and walks the 32-key blocks its
-//          rows can see (K and V through double-buffered LDS):
+//          rows can see (K and V copied straight into a 4-deep LDS ring):
 //            S^T  = K Q^T          (MFMA, lane = query row, 16 keys per lane)
 //            dP^T = V dO^T         (MFMA, same layout)
 //            P    = exp2(S c - LSE log2 e), 0 where masked
@@ -18,7 +19,7 @@
 //            dQ^T += K^T dS^T      (MFMA, K^T by the transposing LDS read)
 //   dkdv   one workgroup of 4 wave64s per 128 keys; each wave keeps its 32
 //          keys of K and V in registers and walks the 32-row Q blocks that
-//          can see them (Q, dO, LSE, D through double-buffered LDS):
+//          can see them (Q, dO and the rows' (LSE, D) through the LDS ring):
 //            S  = Q K^T, dP = dO V^T   (lane = key, 16 query rows per lane)
 //            P, dS as above
 //            dV^T += dO^T P,  dK^T += Q^T dS   (dO^T, Q^T by the transposing read)
@@ -108,38 +109,76 @@ __device__ __forceinline__ bf16x8 read_row(const char* blk, const Offs<D>& o, in
   return __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(blk + (o.row0 ^ (32 * kc))));
 }
 
-// Stage rows [r0, r0 + 32) of a [N, D] bf16 matrix (rows >= lim read as 0)
-// into registers: thread t holds chunks t and t + kThreads of the block.
+// ---- the LDS ring: blocks copied from global memory straight into LDS ----
+// A block is 32 rows of a [N, D] bf16 matrix (one head). Copy number ci of a
+// block moves 1 KB: lane L brings the 16 bytes that belong at byte 16*L of
+// that KB, i.e. row ci*kRowsPerKB + L/kLanesPerRow, chunk position
+// L%kLanesPerRow, which holds logical chunk (position ^ swz(row)).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr int kDepth = 4;   // ring depth in blocks: copies run three blocks ahead
+
 template <int D>
-struct Stage {
-  static constexpr int kChunks = kBlk * D / 8;
-  static constexpr int kPer = kChunks / kThreads;
-  u32x4 x[kPer];
-  __device__ void load(const uint16_t* base, int r0, int lim, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int id = tid + i * kThreads;
-      const int r = id / (D / 8), c = id % (D / 8);
-      x[i] = (u32x4){0u, 0u, 0u, 0u};
-      if (r0 + r < lim) x[i] = *(const u32x4*)(base + (size_t)(r0 + r) * D + c * 8);
-    }
-  }
-  __device__ void store(char* blk, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int id = tid + i * kThreads;
-      const int r = id / (D / 8), c = id % (D / 8);
-      *(lds_u32x4*)(blk + r * 2 * D + ((c ^ swz<D>(r)) << 4)) = x[i];
-    }
-  }
+struct Ring {
+  static constexpr int kBlkBytes = kBlk * 2 * D;
+  static constexpr int kKB = kBlkBytes / 1024;        // copies per matrix block
+  static constexpr int kRowsPerKB = 1024 / (2 * D);
+  static constexpr int kLanesPerRow = 64 / kRowsPerKB;
+  static constexpr int kCpw = 2 * kKB / kWaves;       // copies per wave per block (two matrices)
+  static_assert((2 * kKB) % kWaves == 0, "copies must split evenly over the waves");
 };
 
+// Raw buffer descriptor over [base, base + bytes): lanes whose offset is at
+// or past `bytes` fetch nothing.
+__device__ __forceinline__ i32x4 rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));   // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);                 // num_records
+  r[3] = 0x00020000;                                                 // 32-bit data format
+  return r;
+}
+
+// One 1 KB global -> LDS copy: 16 bytes per lane from rs at byte offset
+// off + soff, written to LDS byte lds + 16*lane. Completion is awaited with
+// wait_copies; the compiler does not see the LDS write (inline assembly), so
+// every read of a copied block follows an explicit wait and a barrier.
+__device__ __forceinline__ void copy_kb(const i32x4& rs, uint32_t soff, uint32_t off, uint32_t lds) {
+  uint32_t v;
+  // (the add after the M0 write is the wait state the LDS copy needs)
+  asm volatile("s_mov_b32 m0, %1\n\tv_add_u32 %0, %2, %3\n\tbuffer_load_dwordx4 %0, %4, 0 offen lds"
+               : "=&v"(v) : "s"(lds), "s"(soff), "v"(off), "s"(rs) : "memory", "m0");
+}
+
+// vmcnt(0) as a builtin the compiler sees: the register loads issued before
+// the ring starts are complete, so it places no wait of its own (which would
+// also drain the ring) inside the loop.
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Lane offset of copy ci (0 .. 2*kKB-1) of a block pair: matrix ci / kKB,
+// KB ci % kKB; returned relative to that matrix's block start.
+template <int D>
+__device__ __forceinline__ int copy_lane_off(int ci, int lane) {
+  using R = Ring<D>;
+  const int r = (ci % R::kKB) * R::kRowsPerKB + lane / R::kLanesPerRow;
+  return r * 2 * D + (((lane % R::kLanesPerRow) ^ swz<D>(r)) << 4);
+}
+
 // ---------------------------------------------------------------- delta
-// D_i = sum_d dO_id O_id for every row of [rows, D]; D/8 lanes per row.
+// Per row: stats = (LSE * log2 e, D) with D = sum_d dO_id O_id, and +inf in
+// place of LSE * log2 e for a row with no allowed key (LSE = -inf), so that
+// exp2(S c - stats.x) is 0 there. D/8 lanes per row.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const uint16_t* __restrict__ O,
                                                              const uint16_t* __restrict__ dO,
-                                                             float* __restrict__ delta, long long rows) {
+                                                             const float* __restrict__ LSE,
+                                                             f32x2* __restrict__ stats, long long rows) {
   constexpr int kL = D / 8;
   const long long row = (long long)blockIdx.x * (256 / kL) + threadIdx.x / kL;
   const int c = threadIdx.x % kL;
@@ -155,21 +194,31 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const uint16_t* __r
   }
 #pragma unroll
   for (int m = kL / 2; m > 0; m >>= 1) s += __shfl_xor(s, m, kL);
-  if (row < rows && c == 0) delta[row] = s;
+  if (row < rows && c == 0) {
+    const float l = LSE[row];
+    stats[row] = (f32x2){l == -INFINITY ? INFINITY : l * kLog2e, s};
+  }
 }
 
 // ---------------------------------------------------------------- dq
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
-    uint16_t* __restrict__ dQ, int H, int N_q, int N_k, float c, float scale, int causal,
-    const int32_t* __restrict__ seqlens_k, const int32_t* __restrict__ q_start, int n_qt) {
-  constexpr int kBlkBytes = kBlk * 2 * D;
-  __shared__ __attribute__((aligned(1024))) char smem[2][2][kBlkBytes];   // [buffer][K, V]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5;
-  const int bh = blockIdx.x / n_qt;
-  const int qt = n_qt - 1 - (int)(blockIdx.x % n_qt);   // tiles with more keys first
+    const uint16_t* __restrict__ dO, const f32x2* __restrict__ stats, uint16_t* __restrict__ dQ, int H, int N_q,
+    int N_k, float c, float scale, int causal, const int32_t* __restrict__ seqlens_k,
+    const int32_t* __restrict__ q_start, int n_qt) {
+  using R = Ring<D>;
+  constexpr int kStage = 2 * R::kBlkBytes;   // [K block][V block]
+  __shared__ __attribute__((aligned(1024))) char smem[kDepth * kStage];
+  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  // Under a causal mask a tile's work grows with its index: launch the tiles
+  // heaviest first across all heads (tile-major), so that the light ones fill
+  // in at the end. Without it, head-major order keeps a head's tiles together
+  // (they read the same K and V).
+  const int n_bh = (int)(gridDim.x / n_qt);
+  const int bh = causal ? (int)(blockIdx.x % n_bh) : (int)(blockIdx.x / n_qt);
+  const int qt = causal ? n_qt - 1 - (int)(blockIdx.x / n_bh) : (int)(blockIdx.x % n_qt);
   const int b = bh / H;
   int kv = N_k;
   if (seqlens_k) kv = min(max(seqlens_k[b], 0), N_k);
@@ -199,39 +248,61 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
   }
   float lse2 = INFINITY, dl = 0.f;   // +inf: a row with no allowed key gets P = 0
   if (row_ok) {
-    const float l = LSE[(size_t)bh * N_q + row];
-    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
-    dl = delta[(size_t)bh * N_q + row];
+    const f32x2 st = stats[(size_t)bh * N_q + row];
+    lse2 = st[0];
+    dl = st[1];
   }
   // key j is allowed for this row iff j <= klim
   const int klim = (!row_ok || row < qs) ? -1 : min(kv - 1, causal ? row : 0x7fffffff);
+
+  wait_loads();
+  // Keys past kv_end fetch nothing, so a stage keeps rows no copy wrote: zero
+  // the ring once, then such rows hold zeros or keys of an earlier block, all
+  // finite, and their probabilities are 0.
+  for (int i = tid; i < kDepth * kStage / 16; i += kThreads) *(lds_u32x4*)(smem + 16 * i) = (u32x4){0u, 0u, 0u, 0u};
+  __syncthreads();
+  const i32x4 k_rs = rsrc(K + k_base, (uint32_t)kv_end * 2 * D), v_rs = rsrc(V + k_base, (uint32_t)kv_end * 2 * D);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  int coff[R::kCpw];
+#pragma unroll
+  for (int i = 0; i < R::kCpw; ++i) coff[i] = copy_lane_off<D>(wave * R::kCpw + i, lane);
+  auto issue = [&](int n) {   // block n into stage n % kDepth
+    const uint32_t st = lds0 + (uint32_t)(n % kDepth) * kStage;
+    const uint32_t soff = (uint32_t)n * R::kBlkBytes;
+#pragma unroll
+    for (int i = 0; i < R::kCpw; ++i) {
+      const int ci = wave * R::kCpw + i;
+      const bool is_v = ci >= R::kKB;
+      copy_kb(is_v ? v_rs : k_rs, soff, coff[i], st + (uint32_t)ci * 1024);
+    }
+  };
 
   const Offs<D> off(lane);
   f32x16 acc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = (f32x16){};
-
-  Stage<D> sk, sv;
-  if (nblk > 0) {
-    sk.load(K + k_base, 0, kv_end, tid);
-    sv.load(V + k_base, 0, kv_end, tid);
-    sk.store(smem[0][0], tid);
-    sv.store(smem[0][1], tid);
-  }
-  __syncthreads();
-  for (int n = 0; n < nblk; ++n) {
-    const int cur = n & 1;
-    if (n + 1 < nblk) {   // next block into registers while this one is used
-      sk.load(K + k_base, (n + 1) * kBlk, kv_end, tid);
-      sv.load(V + k_base, (n + 1) * kBlk, kv_end, tid);
-    }
-    const char* kb = smem[cur][0];
-    const char* vb = smem[cur][1];
-    f32x16 s = {}, dp = {};
 #pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) {
-      s = mfma(read_row<D>(kb, off, kc), qr[kc], s);
-      dp = mfma(read_row<D>(vb, off, kc), gr[kc], dp);
+  for (int n = 0; n < kDepth - 1; ++n) issue(n);
+  for (int n = 0; n < nblk; ++n) {
+    wait_copies<(kDepth - 2) * R::kCpw>();   // block n has landed (this wave's copies)
+    __syncthreads();                          // everyone's copies; block n-1's stage is free
+    issue(n + kDepth - 1);
+    const char* kb = smem + (n % kDepth) * kStage;
+    const char* vb = kb + R::kBlkBytes;
+    f32x16 s = {}, dp = {};
+    {
+      bf16x8 ka[2], va[2];   // operands read one step ahead of their MFMAs
+      ka[0] = read_row<D>(kb, off, 0);
+      va[0] = read_row<D>(vb, off, 0);
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) {
+        if (kc + 1 < D / 16) {
+          ka[(kc + 1) & 1] = read_row<D>(kb, off, kc + 1);
+          va[(kc + 1) & 1] = read_row<D>(vb, off, kc + 1);
+        }
+        s = mfma(ka[kc & 1], qr[kc], s);
+        dp = mfma(va[kc & 1], gr[kc], dp);
+      }
     }
     // P and dS; register r holds key n*32 + 8*(r/4) + 4*hf + r%4
     const int lim = klim - n * kBlk - 4 * hf;
@@ -239,24 +310,23 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       const int j0 = 8 * (r >> 2) + (r & 3);
-      const float p0 = j0 <= lim ? __builtin_amdgcn_exp2f(s[r] * c - lse2) : 0.f;
-      const float p1 = j0 + 1 <= lim ? __builtin_amdgcn_exp2f(s[r + 1] * c - lse2) : 0.f;
-      w[r >> 1] = pack2(p0 * (dp[r] - dl), p1 * (dp[r + 1] - dl));
+      const float d0 = j0 <= lim ? __builtin_amdgcn_exp2f(s[r] * c - lse2) * (dp[r] - dl) : 0.f;
+      const float d1 = j0 + 1 <= lim ? __builtin_amdgcn_exp2f(s[r + 1] * c - lse2) * (dp[r + 1] - dl) : 0.f;
+      w[r >> 1] = pack2(d0, d1);
     }
+    {
+      bf16x8 ta[2];
+      ta[0] = read_tr<D>(kb, off, 0, 0);
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const bf16x8 bw = __builtin_bit_cast(bf16x8, (u32x4){w[4 * cc], w[4 * cc + 1], w[4 * cc + 2], w[4 * cc + 3]});
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[db] = mfma(read_tr<D>(kb, off, cc, db), bw, acc[db]);
+      for (int i = 0; i < 2 * (D / 32); ++i) {   // i = cc * (D/32) + db
+        const int cc = i / (D / 32), db = i % (D / 32);
+        if (i + 1 < 2 * (D / 32)) ta[(i + 1) & 1] = read_tr<D>(kb, off, (i + 1) / (D / 32), (i + 1) % (D / 32));
+        const bf16x8 bw = __builtin_bit_cast(bf16x8, (u32x4){w[4 * cc], w[4 * cc + 1], w[4 * cc + 2], w[4 * cc + 3]});
+        acc[db] = mfma(ta[i & 1], bw, acc[db]);
+      }
     }
-    // The other buffer was last read in the previous iteration, before its
-    // barrier: it can be refilled now, and one barrier publishes it.
-    if (n + 1 < nblk) {
-      sk.store(smem[cur ^ 1][0], tid);
-      sv.store(smem[cur ^ 1][1], tid);
-    }
-    __syncthreads();
   }
+  wait_copies<0>();   // no copy may still be writing LDS when the workgroup ends
   // dQ = scale * dQ^T: register r of block db holds d = 32*db + 8*(r/4) + 4*hf + r%4
   if (row_ok) {
 #pragma unroll
@@ -274,15 +344,19 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int H, int N_q, int N_k, float c, float scale,
-    int causal, const int32_t* __restrict__ seqlens_k, const int32_t* __restrict__ q_start, int n_kt) {
-  constexpr int kBlkBytes = kBlk * 2 * D;
-  __shared__ __attribute__((aligned(1024))) char smem[2][2][kBlkBytes];   // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) float sstat[2][2][kBlk];         // [buffer][LSE*log2e, D]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5;
-  const int bh = blockIdx.x / n_kt;
-  const int kt = (int)(blockIdx.x % n_kt);   // under a causal mask, early keys have the most rows
+    const uint16_t* __restrict__ dO, const f32x2* __restrict__ stats, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, int H, int N_q, int N_k, float c, float scale, int causal,
+    const int32_t* __restrict__ seqlens_k, const int32_t* __restrict__ q_start, int n_kt) {
+  using R = Ring<D>;
+  constexpr int kStage = 2 * R::kBlkBytes + 1024;   // [Q block][dO block][stats of the 32 rows]
+  __shared__ __attribute__((aligned(1024))) char smem[kDepth * kStage];
+  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  // Under a causal mask early key tiles have the most rows: tile-major order,
+  // heaviest first across all heads (see the dq kernel).
+  const int n_bh = (int)(gridDim.x / n_kt);
+  const int bh = causal ? (int)(blockIdx.x % n_bh) : (int)(blockIdx.x / n_kt);
+  const int kt = causal ? (int)(blockIdx.x / n_bh) : (int)(blockIdx.x % n_kt);
   const int b = bh / H;
   int kv = N_k;
   if (seqlens_k) kv = min(max(seqlens_k[b], 0), N_k);
@@ -297,107 +371,118 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
   const int nblk = r_begin < N_q ? (N_q + kBlk - 1) / kBlk - blk0 : 0;
 
   const int key = k0 + kBlk * wave + (lane & 31);
-  const bool key_ok = key < N_k;
-  bf16x8 kr[D / 16], vr[D / 16];   // this key's K and V as B operands
+  const bool key_ok = key < N_k, key_live = key < kv;
+  bf16x8 kr[D / 16], vr[D / 16];   // this key's K and V as B operands (zeros past the valid length)
 #pragma unroll
   for (int kc = 0; kc < D / 16; ++kc) {
     u32x4 a = {0u, 0u, 0u, 0u}, g = {0u, 0u, 0u, 0u};
-    if (key_ok) {
+    if (key_live) {
       a = *(const u32x4*)(K + k_base + (size_t)key * D + kc * 16 + hf * 8);
       g = *(const u32x4*)(V + k_base + (size_t)key * D + kc * 16 + hf * 8);
     }
     kr[kc] = __builtin_bit_cast(bf16x8, a);
     vr[kc] = __builtin_bit_cast(bf16x8, g);
   }
-  const bool key_live = key < kv;
+
+  wait_loads();
+  // Rows past N_q fetch nothing: zero the ring once, so such rows hold zeros
+  // or rows of an earlier block (finite) and are masked out below.
+  for (int i = tid; i < kDepth * kStage / 16; i += kThreads) *(lds_u32x4*)(smem + 16 * i) = (u32x4){0u, 0u, 0u, 0u};
+  __syncthreads();
+  const uint32_t rows_bytes = (uint32_t)N_q * 2 * D;
+  const i32x4 q_rs = rsrc(Q + q_base, rows_bytes), g_rs = rsrc(dO + q_base, rows_bytes);
+  const i32x4 s_rs = rsrc(stats + (size_t)bh * N_q, (uint32_t)N_q * 8);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  int coff[R::kCpw];
+#pragma unroll
+  for (int i = 0; i < R::kCpw; ++i) coff[i] = copy_lane_off<D>(wave * R::kCpw + i, lane);
+  // the stats copy (wave 0): lanes 0..15 bring the 256 bytes of the block's 32 rows
+  const int soff_lane = lane < 16 ? 16 * lane : 0x40000000;
+  auto issue = [&](int n) {   // block n (rows (blk0 + n)*32 ..) into stage n % kDepth
+    const uint32_t st = lds0 + (uint32_t)(n % kDepth) * kStage;
+    const uint32_t r0 = (uint32_t)(blk0 + n) * kBlk;
+#pragma unroll
+    for (int i = 0; i < R::kCpw; ++i) {
+      const int ci = wave * R::kCpw + i;
+      const bool is_g = ci >= R::kKB;
+      copy_kb(is_g ? g_rs : q_rs, r0 * 2 * D, coff[i], st + (uint32_t)ci * 1024);
+    }
+    if (wave == 0) copy_kb(s_rs, r0 * 8, soff_lane, st + 2 * R::kBlkBytes);
+  };
 
   const Offs<D> off(lane);
   f32x16 adk[D / 32], adv[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) adk[db] = adv[db] = (f32x16){};
-
-  Stage<D> sq, sg;
-  float st = 0.f;   // thread t < 64 stages one LSE or D value
-  auto load_stat = [&](int r0) {
-    if (tid < 2 * kBlk) {
-      const int r = r0 + (tid & (kBlk - 1));
-      if (tid < kBlk) {
-        st = INFINITY;
-        if (r < N_q) {
-          const float l = LSE[(size_t)bh * N_q + r];
-          st = l == -INFINITY ? INFINITY : l * kLog2e;
-        }
-      } else {
-        st = r < N_q ? delta[(size_t)bh * N_q + r] : 0.f;
-      }
-    }
-  };
-  auto store_stat = [&](int buf) {
-    if (tid < 2 * kBlk) sstat[buf][tid / kBlk][tid & (kBlk - 1)] = st;
-  };
-  if (nblk > 0) {
-    const int r0 = blk0 * kBlk;
-    sq.load(Q + q_base, r0, N_q, tid);
-    sg.load(dO + q_base, r0, N_q, tid);
-    load_stat(r0);
-    sq.store(smem[0][0], tid);
-    sg.store(smem[0][1], tid);
-    store_stat(0);
-  }
-  __syncthreads();
-  for (int n = 0; n < nblk; ++n) {
-    const int cur = n & 1;
-    const int r0 = (blk0 + n) * kBlk;
-    if (n + 1 < nblk) {
-      sq.load(Q + q_base, r0 + kBlk, N_q, tid);
-      sg.load(dO + q_base, r0 + kBlk, N_q, tid);
-      load_stat(r0 + kBlk);
-    }
-    const char* qb = smem[cur][0];
-    const char* gb = smem[cur][1];
-    f32x16 s = {}, dp = {};
 #pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) {
-      s = mfma(read_row<D>(qb, off, kc), kr[kc], s);
-      dp = mfma(read_row<D>(gb, off, kc), vr[kc], dp);
+  for (int n = 0; n < kDepth - 1; ++n) issue(n);
+  for (int n = 0; n < nblk; ++n) {
+    // block n has landed (this wave's copies; wave 0 has one more per block)
+    if (wave == 0) wait_copies<(kDepth - 2) * (R::kCpw + 1)>();
+    else wait_copies<(kDepth - 2) * R::kCpw>();
+    __syncthreads();
+    issue(n + kDepth - 1);
+    const int r0 = (blk0 + n) * kBlk;
+    const char* qb = smem + (n % kDepth) * kStage;
+    const char* gb = qb + R::kBlkBytes;
+    const char* sb = qb + 2 * R::kBlkBytes;
+    f32x16 s = {}, dp = {};
+    {
+      bf16x8 qa[2], ga[2];   // operands read one step ahead of their MFMAs
+      qa[0] = read_row<D>(qb, off, 0);
+      ga[0] = read_row<D>(gb, off, 0);
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) {
+        if (kc + 1 < D / 16) {
+          qa[(kc + 1) & 1] = read_row<D>(qb, off, kc + 1);
+          ga[(kc + 1) & 1] = read_row<D>(gb, off, kc + 1);
+        }
+        s = mfma(qa[kc & 1], kr[kc], s);
+        dp = mfma(ga[kc & 1], vr[kc], dp);
+      }
     }
     // register r holds query row r0 + 8*(r/4) + 4*hf + r%4 of this lane's key
     uint32_t wp[8], wd[8];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const f32x4 l2 = *(const lds_f32x4*)&sstat[cur][0][8 * g + 4 * hf];
-      const f32x4 dd = *(const lds_f32x4*)&sstat[cur][1][8 * g + 4 * hf];
+      // stats of rows 8g + 4hf .. +3: (lse2, D) pairs, 32 bytes
+      const f32x4 s01 = *(const lds_f32x4*)(sb + 8 * (8 * g + 4 * hf));
+      const f32x4 s23 = *(const lds_f32x4*)(sb + 8 * (8 * g + 4 * hf) + 16);
+      const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
+      const float dd[4] = {s01[1], s01[3], s23[1], s23[3]};
       float p[4], ds[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * g + e;
         const int qrow = r0 + 8 * g + 4 * hf + e;
-        const bool ok = key_live && qrow >= qs && (!causal || key <= qrow);
+        const bool ok = key_live && qrow < N_q && qrow >= qs && (!causal || key <= qrow);
         p[e] = ok ? __builtin_amdgcn_exp2f(s[r] * c - l2[e]) : 0.f;
-        ds[e] = p[e] * (dp[r] - dd[e]);
+        ds[e] = ok ? p[e] * (dp[r] - dd[e]) : 0.f;
       }
       wp[2 * g] = pack2(p[0], p[1]);
       wp[2 * g + 1] = pack2(p[2], p[3]);
       wd[2 * g] = pack2(ds[0], ds[1]);
       wd[2 * g + 1] = pack2(ds[2], ds[3]);
     }
+    {
+      bf16x8 ga[2], qa[2];
+      ga[0] = read_tr<D>(gb, off, 0, 0);
+      qa[0] = read_tr<D>(qb, off, 0, 0);
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const bf16x8 bp = __builtin_bit_cast(bf16x8, (u32x4){wp[4 * cc], wp[4 * cc + 1], wp[4 * cc + 2], wp[4 * cc + 3]});
-      const bf16x8 bd = __builtin_bit_cast(bf16x8, (u32x4){wd[4 * cc], wd[4 * cc + 1], wd[4 * cc + 2], wd[4 * cc + 3]});
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        adv[db] = mfma(read_tr<D>(gb, off, cc, db), bp, adv[db]);
-        adk[db] = mfma(read_tr<D>(qb, off, cc, db), bd, adk[db]);
+      for (int i = 0; i < 2 * (D / 32); ++i) {   // i = cc * (D/32) + db
+        const int cc = i / (D / 32), db = i % (D / 32);
+        if (i + 1 < 2 * (D / 32)) {
+          ga[(i + 1) & 1] = read_tr<D>(gb, off, (i + 1) / (D / 32), (i + 1) % (D / 32));
+          qa[(i + 1) & 1] = read_tr<D>(qb, off, (i + 1) / (D / 32), (i + 1) % (D / 32));
+        }
+        const bf16x8 bp = __builtin_bit_cast(bf16x8, (u32x4){wp[4 * cc], wp[4 * cc + 1], wp[4 * cc + 2], wp[4 * cc + 3]});
+        const bf16x8 bd = __builtin_bit_cast(bf16x8, (u32x4){wd[4 * cc], wd[4 * cc + 1], wd[4 * cc + 2], wd[4 * cc + 3]});
+        adv[db] = mfma(ga[i & 1], bp, adv[db]);
+        adk[db] = mfma(qa[i & 1], bd, adk[db]);
       }
     }
-    if (n + 1 < nblk) {   // the other buffer was last read before the previous barrier
-      sq.store(smem[cur ^ 1][0], tid);
-      sg.store(smem[cur ^ 1][1], tid);
-      store_stat(cur ^ 1);
-    }
-    __syncthreads();
   }
+  wait_copies<0>();   // no copy may still be writing LDS when the workgroup ends
   // register r of block db holds d = 32*db + 8*(r/4) + 4*hf + r%4 of this lane's key
   if (key_ok) {
 #pragma unroll
@@ -437,14 +522,17 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   if (bh > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   const long long n_qt = (N_q + kTile - 1) / kTile, n_kt = (N_k + kTile - 1) / kTile;
   if (bh * n_qt > 0x7fffffffLL || bh * n_kt > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  // per-head byte offsets of the copies are 32-bit
+  if ((long long)(N_q + kTile) * d * 2 > 0x7fffffffLL || (long long)(N_k + kTile) * d * 2 > 0x7fffffffLL)
+    return ATTN_ERR_SHAPE;
   const size_t qb = (size_t)bh * N_q * d * 2, kb = (size_t)bh * N_k * d * 2, rb = (size_t)bh * N_q * 4;
   if (((uintptr_t)q | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq) & 15) return ATTN_ERR_ALIGN;
   if (((uintptr_t)k | (uintptr_t)v | (uintptr_t)dk | (uintptr_t)dv) & 15) return ATTN_ERR_ALIGN;
-  if (((uintptr_t)lse | (uintptr_t)delta) & 3) return ATTN_ERR_ALIGN;
+  if (((uintptr_t)lse & 3) || ((uintptr_t)delta & 7)) return ATTN_ERR_ALIGN;
   const void* ins[] = {q, k, v, o, dout, lse};
   const size_t in_n[] = {qb, kb, kb, qb, qb, rb};
   void* outs[] = {dq, dk, dv, delta};
-  const size_t out_n[] = {qb, kb, kb, rb};
+  const size_t out_n[] = {qb, kb, kb, 2 * rb};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlaps(outs[i], out_n[i], ins[j], in_n[j])) return ATTN_ERR_ALIAS;
@@ -458,28 +546,29 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   const uint16_t *qp = (const uint16_t*)q, *kp = (const uint16_t*)k, *vp = (const uint16_t*)v,
                  *op = (const uint16_t*)o, *gp = (const uint16_t*)dout;
   uint16_t *dqp = (uint16_t*)dq, *dkp = (uint16_t*)dk, *dvp = (uint16_t*)dv;
+  f32x2* stp = (f32x2*)delta;
   hipError_t e = hipSuccess;
   if (has_q) {
     long long rows = bh * N_q;
     const long long per = 256 / (d / 8);
     const long long nb = (rows + per - 1) / per;
     if (nb > 0x7fffffffLL) return ATTN_ERR_SHAPE;
-    void* a0[] = {(void*)&op, (void*)&gp, (void*)&delta, (void*)&rows};
+    void* a0[] = {(void*)&op, (void*)&gp, (void*)&lse, (void*)&stp, (void*)&rows};
     const void* f0 = d == 128 ? (const void*)attn_bwd_delta_kernel<128> : (const void*)attn_bwd_delta_kernel<64>;
     e = hipLaunchKernel(f0, dim3((unsigned)nb), dim3(256), a0, 0, stream);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
     int nqt = (int)n_qt;
-    void* a1[] = {(void*)&qp, (void*)&kp, (void*)&vp, (void*)&gp, (void*)&lse, (void*)&delta, (void*)&dqp,
-                  (void*)&Hi, (void*)&Nq, (void*)&Nk, (void*)&cc, (void*)&sc, (void*)&causal01,
-                  (void*)&seqlens_k, (void*)&q_start, (void*)&nqt};
+    void* a1[] = {(void*)&qp, (void*)&kp, (void*)&vp, (void*)&gp, (void*)&stp, (void*)&dqp, (void*)&Hi,
+                  (void*)&Nq, (void*)&Nk, (void*)&cc, (void*)&sc, (void*)&causal01, (void*)&seqlens_k,
+                  (void*)&q_start, (void*)&nqt};
     const void* f1 = d == 128 ? (const void*)attn_bwd_dq_kernel<128> : (const void*)attn_bwd_dq_kernel<64>;
     e = hipLaunchKernel(f1, dim3((unsigned)(bh * n_qt)), dim3(kThreads), a1, 0, stream);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
   }
   if (has_k) {
     int nkt = (int)n_kt;
-    void* a2[] = {(void*)&qp, (void*)&kp, (void*)&vp, (void*)&gp, (void*)&lse, (void*)&delta, (void*)&dkp,
-                  (void*)&dvp, (void*)&Hi, (void*)&Nq, (void*)&Nk, (void*)&cc, (void*)&sc, (void*)&causal01,
+    void* a2[] = {(void*)&qp, (void*)&kp, (void*)&vp, (void*)&gp, (void*)&stp, (void*)&dkp, (void*)&dvp,
+                  (void*)&Hi, (void*)&Nq, (void*)&Nk, (void*)&cc, (void*)&sc, (void*)&causal01,
                   (void*)&seqlens_k, (void*)&q_start, (void*)&nkt};
     const void* f2 = d == 128 ? (const void*)attn_bwd_dkdv_kernel<128> : (const void*)attn_bwd_dkdv_kernel<64>;
     e = hipLaunchKernel(f2, dim3((unsigned)(bh * n_kt)), dim3(kThreads), a2, 0, stream);
