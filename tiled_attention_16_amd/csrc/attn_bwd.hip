@@ -254,6 +254,13 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
   }
   // key j is allowed for this row iff j <= klim
   const int klim = (!row_ok || row < qs) ? -1 : min(kv - 1, causal ? row : 0x7fffffff);
+  // Blocks n < full_below need no mask for any row of this wave: all its rows
+  // exist and are past q_start, and every key of the block is below kv and
+  // (causal) at or below the wave's first row.
+  const int wrow0 = q0 + kBlk * wave;
+  int full_below = 0;
+  if (wrow0 + kBlk <= N_q && wrow0 >= qs) full_below = min(kv, causal ? wrow0 + 1 : kv) / kBlk;
+  full_below = __builtin_amdgcn_readfirstlane(full_below);
 
   wait_loads();
   // Keys past kv_end fetch nothing, so a stage keeps rows no copy wrote: zero
@@ -305,14 +312,21 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
       }
     }
     // P and dS; register r holds key n*32 + 8*(r/4) + 4*hf + r%4
-    const int lim = klim - n * kBlk - 4 * hf;
     uint32_t w[8];
+    if (n < full_below) {   // every key of the block is allowed for every row of the wave
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const int j0 = 8 * (r >> 2) + (r & 3);
-      const float d0 = j0 <= lim ? __builtin_amdgcn_exp2f(s[r] * c - lse2) * (dp[r] - dl) : 0.f;
-      const float d1 = j0 + 1 <= lim ? __builtin_amdgcn_exp2f(s[r + 1] * c - lse2) * (dp[r + 1] - dl) : 0.f;
-      w[r >> 1] = pack2(d0, d1);
+      for (int r = 0; r < 16; r += 2)
+        w[r >> 1] = pack2(__builtin_amdgcn_exp2f(s[r] * c - lse2) * (dp[r] - dl),
+                          __builtin_amdgcn_exp2f(s[r + 1] * c - lse2) * (dp[r + 1] - dl));
+    } else {
+      const int lim = klim - n * kBlk - 4 * hf;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const int j0 = 8 * (r >> 2) + (r & 3);
+        const float d0 = j0 <= lim ? __builtin_amdgcn_exp2f(s[r] * c - lse2) * (dp[r] - dl) : 0.f;
+        const float d1 = j0 + 1 <= lim ? __builtin_amdgcn_exp2f(s[r + 1] * c - lse2) * (dp[r + 1] - dl) : 0.f;
+        w[r >> 1] = pack2(d0, d1);
+      }
     }
     {
       bf16x8 ta[2];
@@ -370,8 +384,10 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
   const int blk0 = r_begin / kBlk;
   const int nblk = r_begin < N_q ? (N_q + kBlk - 1) / kBlk - blk0 : 0;
 
-  const int key = k0 + kBlk * wave + (lane & 31);
+  const int wkey0 = k0 + kBlk * wave;   // this wave's first key
+  const int key = wkey0 + (lane & 31);
   const bool key_ok = key < N_k, key_live = key < kv;
+  const bool wkey_live = wkey0 + kBlk <= kv;   // all 32 keys of the wave are valid
   bf16x8 kr[D / 16], vr[D / 16];   // this key's K and V as B operands (zeros past the valid length)
 #pragma unroll
   for (int kc = 0; kc < D / 16; ++kc) {
@@ -423,6 +439,10 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
     __syncthreads();
     issue(n + kDepth - 1);
     const int r0 = (blk0 + n) * kBlk;
+    // no mask anywhere in this block for this wave: all its keys are valid,
+    // all rows exist and are past q_start, and (causal) the block starts at
+    // or after the wave's last key
+    const bool full = wkey_live && r0 + kBlk <= N_q && r0 >= qs && (!causal || r0 >= wkey0 + kBlk - 1);
     const char* qb = smem + (n % kDepth) * kStage;
     const char* gb = qb + R::kBlkBytes;
     const char* sb = qb + 2 * R::kBlkBytes;
@@ -451,13 +471,21 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
       const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
       const float dd[4] = {s01[1], s01[3], s23[1], s23[3]};
       float p[4], ds[4];
+      if (full) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g + e;
-        const int qrow = r0 + 8 * g + 4 * hf + e;
-        const bool ok = key_live && qrow < N_q && qrow >= qs && (!causal || key <= qrow);
-        p[e] = ok ? __builtin_amdgcn_exp2f(s[r] * c - l2[e]) : 0.f;
-        ds[e] = ok ? p[e] * (dp[r] - dd[e]) : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(s[4 * g + e] * c - l2[e]);
+          ds[e] = p[e] * (dp[4 * g + e] - dd[e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const int qrow = r0 + 8 * g + 4 * hf + e;
+          const bool ok = key_live && qrow < N_q && qrow >= qs && (!causal || key <= qrow);
+          p[e] = ok ? __builtin_amdgcn_exp2f(s[r] * c - l2[e]) : 0.f;
+          ds[e] = ok ? p[e] * (dp[r] - dd[e]) : 0.f;
+        }
       }
       wp[2 * g] = pack2(p[0], p[1]);
       wp[2 * g + 1] = pack2(p[2], p[3]);
