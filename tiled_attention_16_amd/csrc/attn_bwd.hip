@@ -36,6 +36,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
+#include <type_traits>
 
 #include "attn.h"
 
@@ -363,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
     const int32_t* __restrict__ seqlens_k, const int32_t* __restrict__ q_start, int n_kt) {
   using R = Ring<D>;
   constexpr int kStage = 2 * R::kBlkBytes + 1024;   // [Q block][dO block][stats of the 32 rows]
-  __shared__ __attribute__((aligned(1024))) char smem[kDepth * kStage];
+  __shared__ __attribute__((aligned(1024))) char smem[(kDepth + 1) * kStage];
   const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   // Under a causal mask early key tiles have the most rows: tile-major order,
@@ -403,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
   wait_loads();
   // Rows past N_q fetch nothing: zero the ring once, so such rows hold zeros
   // or rows of an earlier block (finite) and are masked out below.
-  for (int i = tid; i < kDepth * kStage / 16; i += kThreads) *(lds_u32x4*)(smem + 16 * i) = (u32x4){0u, 0u, 0u, 0u};
+  for (int i = tid; i < (kDepth + 1) * kStage / 16; i += kThreads) *(lds_u32x4*)(smem + 16 * i) = (u32x4){0u, 0u, 0u, 0u};
   __syncthreads();
   const uint32_t rows_bytes = (uint32_t)N_q * 2 * D;
   const i32x4 q_rs = rsrc(Q + q_base, rows_bytes), g_rs = rsrc(dO + q_base, rows_bytes);
@@ -414,8 +415,12 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
   for (int i = 0; i < R::kCpw; ++i) coff[i] = copy_lane_off<D>(wave * R::kCpw + i, lane);
   // the stats copy (wave 0): lanes 0..15 bring the 256 bytes of the block's 32 rows
   const int soff_lane = lane < 16 ? 16 * lane : 0x40000000;
-  auto issue = [&](int n) {   // block n (rows (blk0 + n)*32 ..) into stage n % kDepth
-    const uint32_t st = lds0 + (uint32_t)(n % kDepth) * kStage;
+  // Ring of kDepthKV stages: while block n's dV/dK products run, block n+1's
+  // S and dP are already computed, so two stages are being read and up to
+  // three more blocks are in flight.
+  constexpr int kDepthKV = kDepth + 1;
+  auto issue = [&](int n) {   // block n (rows (blk0 + n)*32 ..) into stage n % kDepthKV
+    const uint32_t st = lds0 + (uint32_t)(n % kDepthKV) * kStage;
     const uint32_t r0 = (uint32_t)(blk0 + n) * kBlk;
 #pragma unroll
     for (int i = 0; i < R::kCpw; ++i) {
@@ -425,44 +430,51 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
     }
     if (wave == 0) copy_kb(s_rs, r0 * 8, soff_lane, st + 2 * R::kBlkBytes);
   };
+  // Block n has landed once at most the `ahead` newest blocks' copies of this
+  // wave are in flight (wave 0 issues one copy more per block).
+  auto wait_block = [&](auto ahead) {
+    constexpr int A = decltype(ahead)::value;
+    if (wave == 0) wait_copies<A * (R::kCpw + 1)>();
+    else wait_copies<A * R::kCpw>();
+  };
+  auto stage_of = [&](int n) { return (const char*)smem + (n % kDepthKV) * kStage; };
 
   const Offs<D> off(lane);
   f32x16 adk[D / 32], adv[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) adk[db] = adv[db] = (f32x16){};
-#pragma unroll
-  for (int n = 0; n < kDepth - 1; ++n) issue(n);
-  for (int n = 0; n < nblk; ++n) {
-    // block n has landed (this wave's copies; wave 0 has one more per block)
-    if (wave == 0) wait_copies<(kDepth - 2) * (R::kCpw + 1)>();
-    else wait_copies<(kDepth - 2) * R::kCpw>();
-    __syncthreads();
-    issue(n + kDepth - 1);
-    const int r0 = (blk0 + n) * kBlk;
-    // no mask anywhere in this block for this wave: all its keys are valid,
-    // all rows exist and are past q_start, and (causal) the block starts at
-    // or after the wave's last key
-    const bool full = wkey_live && r0 + kBlk <= N_q && r0 >= qs && (!causal || r0 >= wkey0 + kBlk - 1);
-    const char* qb = smem + (n % kDepth) * kStage;
+  // S = Q K^T and dP = dO V^T of the block in stage qb
+  auto sdp = [&](const char* qb, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
     const char* gb = qb + R::kBlkBytes;
-    const char* sb = qb + 2 * R::kBlkBytes;
-    f32x16 s = {}, dp = {};
-    {
-      bf16x8 qa[2], ga[2];   // operands read one step ahead of their MFMAs
-      qa[0] = read_row<D>(qb, off, 0);
-      ga[0] = read_row<D>(gb, off, 0);
+    s = (f32x16){};
+    dp = (f32x16){};
+    bf16x8 qa[2], ga[2];   // operands read one step ahead of their MFMAs
+    qa[0] = read_row<D>(qb, off, 0);
+    ga[0] = read_row<D>(gb, off, 0);
 #pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc) {
-        if (kc + 1 < D / 16) {
-          qa[(kc + 1) & 1] = read_row<D>(qb, off, kc + 1);
-          ga[(kc + 1) & 1] = read_row<D>(gb, off, kc + 1);
-        }
-        s = mfma(qa[kc & 1], kr[kc], s);
-        dp = mfma(ga[kc & 1], vr[kc], dp);
+    for (int kc = 0; kc < D / 16; ++kc) {
+      if (kc + 1 < D / 16) {
+        qa[(kc + 1) & 1] = read_row<D>(qb, off, kc + 1);
+        ga[(kc + 1) & 1] = read_row<D>(gb, off, kc + 1);
       }
+      s = mfma(qa[kc & 1], kr[kc], s);
+      dp = mfma(ga[kc & 1], vr[kc], dp);
     }
-    // register r holds query row r0 + 8*(r/4) + 4*hf + r%4 of this lane's key
-    uint32_t wp[8], wd[8];
+  };
+  // P and dS of block n from its S and dP, packed as the B operands of the
+  // dV and dK products; register r holds query row r0 + 8*(r/4) + 4*hf + r%4.
+  // no mask anywhere in block n for this wave: all its keys are valid, all
+  // rows exist and are past q_start, and (causal) the block starts at or
+  // after the wave's last key
+  auto block_full = [&](int n) {
+    const int r0 = (blk0 + n) * kBlk;
+    return wkey_live && r0 + kBlk <= N_q && r0 >= qs && (!causal || r0 >= wkey0 + kBlk - 1);
+  };
+  auto softmax_grad = [&](auto full_t, int n, const f32x16& s, const f32x16& dp, uint32_t (&wp)[8],
+                          uint32_t (&wd)[8]) __attribute__((always_inline)) {
+    constexpr bool full = decltype(full_t)::value;
+    const int r0 = (blk0 + n) * kBlk;
+    const char* sb = stage_of(n) + 2 * R::kBlkBytes;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       // stats of rows 8g + 4hf .. +3: (lse2, D) pairs, 32 bytes
@@ -471,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
       const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
       const float dd[4] = {s01[1], s01[3], s23[1], s23[3]};
       float p[4], ds[4];
-      if (full) {
+      if constexpr (full) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           p[e] = __builtin_amdgcn_exp2f(s[4 * g + e] * c - l2[e]);
@@ -492,23 +504,69 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
       wd[2 * g] = pack2(ds[0], ds[1]);
       wd[2 * g + 1] = pack2(ds[2], ds[3]);
     }
-    {
-      bf16x8 ga[2], qa[2];
-      ga[0] = read_tr<D>(gb, off, 0, 0);
-      qa[0] = read_tr<D>(qb, off, 0, 0);
+  };
+  // Interleave the next block's S and dP MFMAs (16) with this block's
+  // softmax VALU work and the LDS reads, one MFMA per group.
+  auto interleave = [&](auto valu_t) __attribute__((always_inline)) {
+    constexpr int kV = decltype(valu_t)::value;
 #pragma unroll
-      for (int i = 0; i < 2 * (D / 32); ++i) {   // i = cc * (D/32) + db
-        const int cc = i / (D / 32), db = i % (D / 32);
-        if (i + 1 < 2 * (D / 32)) {
-          ga[(i + 1) & 1] = read_tr<D>(gb, off, (i + 1) / (D / 32), (i + 1) % (D / 32));
-          qa[(i + 1) & 1] = read_tr<D>(qb, off, (i + 1) / (D / 32), (i + 1) % (D / 32));
-        }
-        const bf16x8 bp = __builtin_bit_cast(bf16x8, (u32x4){wp[4 * cc], wp[4 * cc + 1], wp[4 * cc + 2], wp[4 * cc + 3]});
-        const bf16x8 bd = __builtin_bit_cast(bf16x8, (u32x4){wd[4 * cc], wd[4 * cc + 1], wd[4 * cc + 2], wd[4 * cc + 3]});
-        adv[db] = mfma(ga[i & 1], bp, adv[db]);
-        adk[db] = mfma(qa[i & 1], bd, adk[db]);
-      }
+    for (int i = 0; i < 2 * (D / 16); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);   // VALU
     }
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS for the block in stage qb
+  auto dvdk = [&](const char* qb, const uint32_t (&wp)[8], const uint32_t (&wd)[8]) __attribute__((always_inline)) {
+    const char* gb = qb + R::kBlkBytes;
+    bf16x8 ga[2], qa[2];
+    ga[0] = read_tr<D>(gb, off, 0, 0);
+    qa[0] = read_tr<D>(qb, off, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * (D / 32); ++i) {   // i = cc * (D/32) + db
+      const int cc = i / (D / 32), db = i % (D / 32);
+      if (i + 1 < 2 * (D / 32)) {
+        ga[(i + 1) & 1] = read_tr<D>(gb, off, (i + 1) / (D / 32), (i + 1) % (D / 32));
+        qa[(i + 1) & 1] = read_tr<D>(qb, off, (i + 1) / (D / 32), (i + 1) % (D / 32));
+      }
+      const bf16x8 bp = __builtin_bit_cast(bf16x8, (u32x4){wp[4 * cc], wp[4 * cc + 1], wp[4 * cc + 2], wp[4 * cc + 3]});
+      const bf16x8 bd = __builtin_bit_cast(bf16x8, (u32x4){wd[4 * cc], wd[4 * cc + 1], wd[4 * cc + 2], wd[4 * cc + 3]});
+      adv[db] = mfma(ga[i & 1], bp, adv[db]);
+      adk[db] = mfma(qa[i & 1], bd, adk[db]);
+    }
+  };
+
+  // Software pipeline: step n computes S, dP of block n+1 on the MFMA unit
+  // while the VALU turns block n's S, dP into P and dS, then runs block n's
+  // dV and dK products.
+  f32x16 s_cur, dp_cur;
+  if (nblk > 0) {
+#pragma unroll
+    for (int n = 0; n < kDepthKV - 1; ++n) issue(n);
+    wait_block(std::integral_constant<int, kDepthKV - 2>{});   // block 0
+    __syncthreads();
+    sdp(stage_of(0), s_cur, dp_cur);
+  }
+  for (int n = 0; n < nblk; ++n) {
+    wait_block(std::integral_constant<int, kDepthKV - 3>{});   // block n+1
+    __syncthreads();   // everyone's copies of block n+1; block n-1's stage is free
+    issue(n + kDepthKV - 1);
+    // (past the last block, S and dP come from the stage of a copy that
+    // fetched nothing: finite values, discarded)
+    f32x16 s_nxt, dp_nxt;
+    uint32_t wp[8], wd[8];
+    if (block_full(n)) {
+      sdp(stage_of(n + 1), s_nxt, dp_nxt);
+      softmax_grad(std::true_type{}, n, s_cur, dp_cur, wp, wd);
+      interleave(std::integral_constant<int, 6>{});
+    } else {
+      sdp(stage_of(n + 1), s_nxt, dp_nxt);
+      softmax_grad(std::false_type{}, n, s_cur, dp_cur, wp, wd);
+      interleave(std::integral_constant<int, 10>{});
+    }
+    dvdk(stage_of(n), wp, wd);
+    s_cur = s_nxt;
+    dp_cur = dp_nxt;
   }
   wait_copies<0>();   // no copy may still be writing LDS when the workgroup ends
   // register r of block db holds d = 32*db + 8*(r/4) + 4*hf + r%4 of this lane's key
