@@ -46,12 +46,27 @@ METRIC = "attention fwd TFLOP/s (bf16, causal, N=4096, d=128) + % of MFMA bf16 p
 HBM_METRIC = "attention fwd achieved HBM GB/s (bf16, short sequences) + % of HBM peak"
 BWD_METRIC = "attention bwd TFLOP/s (bf16, dQ dK dV, counted 10*B*H*N_q*N_k*d, halved when causal) + % of MFMA bf16 peak"
 KERNEL_SRC = os.path.join(ROOT, "tiled_attention_16_amd", "csrc", "attn_fwd.hip")
+BWD_SRC = os.path.join(ROOT, "tiled_attention_16_amd", "csrc", "attn_bwd.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_source_hash(path: str = KERNEL_SRC) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_bwd_traffic(workload: str):
+    """HBM bytes per attn_bwd call (its three kernels) from the committed counter
+    summary, or None when it is missing or covers an older kernel source."""
+    path = os.path.join(PROFILES, f"attn_bwd_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path, encoding="utf-8").read()
+    src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not src or src.group(1) != kernel_source_hash(BWD_SRC):
+        return None
+    m = re.search(rf"traffic_bytes_per_call\[{re.escape(workload)}\]:\s*([0-9.eE+]+)", text)
+    return float(m.group(1)) if m else None
 
 
 def measured_traffic(workload: str):
@@ -262,7 +277,7 @@ def bench_backward(args, torch, ta, w, inp, tensors, sl, qs, stream, dev):
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.N_q, "N_k": w.N_k, "d": w.d, "causal": w.causal,
                    "varlen": inp.seqlens_k is not None, "pass": "backward"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_bwd_traffic(w.name)},
         "launch_ms": {"mean": round(ms, 5)},
         "wall_s_timed": round(wall, 4),
     }
