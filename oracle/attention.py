@@ -25,7 +25,9 @@ Readings of the pages taken here (each also listed in the design notes):
   * the scale multiplies the scores before masking ([PT2CUDA] step 1 and
     [PROFILE3] naive module order), so scale = 0 never forms 0 * -inf;
   * causal means key j is visible to query i iff j <= i, the lower-triangular
-    [seq, seq] mask of [PROFILE3] (top-left aligned when N_q != N_k);
+    [seq, seq] mask of [PROFILE3] (top-left aligned when N_q != N_k); causal = 2
+    aligns the triangle bottom-right instead (j <= i + N_k - N_q), the pages'
+    mask when the queries are the last N_q positions of the key sequence;
   * variable-length keys are masked through a per-batch valid length
     ([MEMWALL] §6.2), clamped to [0, N_k]; a per-batch count of leading query
     rows that attend to nothing (``q_start``, clamped to [0, N_q]) lets a
@@ -47,13 +49,25 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
-def allowed_mask(n_q: int, n_k: int, causal: bool, kv_len: Optional[int] = None,
+def causal_offset(n_q: int, n_k: int, causal) -> int:
+    """Diagonal offset of a causal mask: key j is visible to row i iff j <= i + offset.
+
+    causal = 1 (or True): top-left aligned, offset 0 (the lower triangle of
+    [PROFILE3]); causal = 2: bottom-right aligned, offset n_k - n_q, so the
+    last query row sees every key (rows are the last n_q positions of the
+    key sequence, as when new queries attend to a cache of earlier keys).
+    """
+    return n_k - n_q if int(causal) == 2 else 0
+
+
+def allowed_mask(n_q: int, n_k: int, causal, kv_len: Optional[int] = None,
                  q_start: Optional[int] = None, rows: Optional[Sequence[int]] = None) -> np.ndarray:
     """Boolean [R, n_k] matrix, True where query row i may attend to key j.
 
     Built explicitly, entry by entry, from the three rules:
-      causal   -> j <= i, the lower triangle ([PROFILE3], math-backend mask
-                  built with ones -> tril);
+      causal   -> j <= i + causal_offset(...), the lower triangle ([PROFILE3],
+                  math-backend mask built with ones -> tril), top-left
+                  (causal = 1) or bottom-right (causal = 2) aligned;
       kv_len   -> j < kv_len, keys past a sequence's valid length are masked
                   ([MEMWALL] §6.2, masks mark the valid positions);
       q_start  -> i >= q_start, leading rows see no key at all.
@@ -64,7 +78,7 @@ def allowed_mask(n_q: int, n_k: int, causal: bool, kv_len: Optional[int] = None,
     j = np.arange(n_k)
     ok = (j[None, :] < kv) & (i[:, None] >= qs)
     if causal:
-        ok &= j[None, :] <= i[:, None]
+        ok &= j[None, :] <= i[:, None] + causal_offset(n_q, n_k, causal)
     return ok
 
 

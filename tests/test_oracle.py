@@ -260,3 +260,55 @@ def test_torch_sdpa_cpu_fp64_cross_check():
         for h in range(H):
             np.testing.assert_array_equal(got[:, h][~live], 0.0)
             np.testing.assert_array_equal(o[:, h][~live], 0.0)
+
+
+# ---------------------------------------------------------------- bottom-right causal (causal = 2)
+def test_bottom_right_mask_brute_force():
+    for n_q, n_k in [(3, 7), (7, 3), (5, 5), (1, 6)]:
+        ok = allowed_mask(n_q, n_k, 2)
+        for i in range(n_q):
+            for j in range(n_k):
+                assert ok[i, j] == (j - (n_k - n_q) <= i), (n_q, n_k, i, j)
+
+
+def test_bottom_right_single_query_sees_every_key():
+    """One query row at the end of the key sequence (decoding against a cache):
+    bottom-right causal is plain attention over all keys."""
+    q, k, v = rnd((2, 3, 1, 8), 51), rnd((2, 3, 9, 8), 52), rnd((2, 3, 9, 8), 53)
+    o2, l2 = attention(q, k, v, 0.3, 2)
+    o0, l0 = attention(q, k, v, 0.3, False)
+    np.testing.assert_allclose(o2, o0, atol=1e-14)
+    np.testing.assert_allclose(l2, l0, atol=1e-14)
+    o1, _ = attention(q, k, v, 0.3, True)          # top-left: row 0 sees only key 0
+    np.testing.assert_allclose(o1[:, :, 0], v[:, :, 0], atol=1e-14)
+
+
+@pytest.mark.parametrize("n_q,n_k", [(4, 9), (9, 4)])
+def test_bottom_right_prefix_mean_closed_form(n_q, n_k):
+    """Q = 0: row i averages V over keys 0 .. i + n_k - n_q (no key: O = 0, LSE = -inf)."""
+    q = np.zeros((1, 1, n_q, 3))
+    k, v = rnd((1, 1, n_k, 3), 54), rnd((1, 1, n_k, 3), 55)
+    o, lse = attention(q, k, v, 1.0, 2)
+    oo, lo = attention_online(q, k, v, 1.0, 2, block_k=2)
+    for i in range(n_q):
+        last = i + n_k - n_q
+        if last < 0:
+            assert np.all(o[0, 0, i] == 0) and np.isneginf(lse[0, 0, i])
+        else:
+            np.testing.assert_allclose(o[0, 0, i], v[0, 0, :last + 1].mean(axis=0), atol=1e-14)
+            assert abs(lse[0, 0, i] - math.log(last + 1)) < 1e-14
+    np.testing.assert_allclose(oo, o, atol=1e-13)
+
+
+def test_bottom_right_torch_cross_check():
+    torch = pytest.importorskip("torch")
+    try:
+        from torch.nn.attention.bias import causal_lower_right
+    except ImportError:
+        pytest.skip("torch has no bottom-right causal bias")
+    q, k, v = rnd((1, 2, 5, 6), 56), rnd((1, 2, 8, 6), 57), rnd((1, 2, 8, 6), 58)
+    tq, tk, tv = (torch.tensor(x) for x in (q, k, v))
+    want = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=causal_lower_right(5, 8),
+                                                            scale=0.4).numpy()
+    o, _ = attention(q, k, v, 0.4, 2)
+    np.testing.assert_allclose(o, want, atol=1e-12)

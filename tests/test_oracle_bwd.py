@@ -152,3 +152,25 @@ def test_grad_checker_bars():
     bad = {k: v.copy() for k, v in r.items()}
     bad["dq"][1, 2] = np.nan
     assert not check_grads(bad, r).ok
+
+
+def test_finite_differences_bottom_right():
+    n_q, n_k, d = 4, 7, 3
+    q, k, v, g = rnd((1, 1, n_q, d), 61), rnd((1, 1, n_k, d), 62), rnd((1, 1, n_k, d), 63), rnd((1, 1, n_q, d), 64)
+    dq, dk, dv = attention_bwd(q, k, v, g, 0.6, 2)
+    eps = 1e-6
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            args = {"q": q, "k": k, "v": v}
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args[name] = xp
+            lp = loss(args["q"], args["k"], args["v"], g, 0.6, 2, None, None)
+            args[name] = xm
+            lm = loss(args["q"], args["k"], args["v"], g, 0.6, 2, None, None)
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-7, err_msg=f"d{name}")

@@ -24,6 +24,9 @@ MUTANTS = [
     ("log2 in LSE", "m[live] + np.log(l[live])", "m[live] + np.log2(l[live])"),
     ("max not added back to LSE", "m[live] + np.log(l[live])", "np.log(l[live])"),
     ("unnormalised P", "p[live] = e[live] / l[live, None]", "p[live] = e[live]"),
+    ("bottom-right offset reversed", "return n_k - n_q if int(causal) == 2 else 0",
+     "return n_q - n_k if int(causal) == 2 else 0"),
+    ("bottom-right treated as top-left", "return n_k - n_q if int(causal) == 2 else 0", "return 0"),
     ("P times K instead of V", "out[b, h, pos:pos + r] = p[:, :n_valid] @ v[b, h, :n_valid]",
      "out[b, h, pos:pos + r] = p[:, :n_valid] @ k[b, h, :n_valid]"),
 ]
