@@ -22,8 +22,12 @@
  *                    valid length, [MEMWALL] §6.2);
  *   i >= qs[b]       with qs[b] = clamp(q_start[b], 0, N_q), or 0 when q_start
  *                    is NULL (leading query rows that attend to nothing);
- *   j <= i           when causal != 0 (the lower-triangular mask of [PROFILE3];
- *                    top-left aligned when N_q != N_k).
+ *   j <= i           when causal == 1 (the lower-triangular mask of [PROFILE3],
+ *                    top-left aligned when N_q != N_k);
+ *   j <= i + N_k - N_q  when causal == 2 (the same triangle aligned bottom-right:
+ *                    the queries are the last N_q positions of the key
+ *                    sequence, as when new rows attend to cached keys; a row
+ *                    with i + N_k - N_q < 0 sees no key).
  * A row with no allowed key outputs O = +0 and LSE = -inf, never NaN (the
  * NaN-safe softmax of [PROFILE3], math-backend section). Keys at or beyond
  * kv_len[b] are ignored entirely: their K and V contents are never used, so
@@ -51,7 +55,8 @@ typedef enum {
   ATTN_ERR_SCALE = 4,     /* scale is NaN or infinite                            */
   ATTN_ERR_ALIGN = 5,     /* a bf16 tensor not 16-byte aligned, lse/delta 4-byte */
   ATTN_ERR_ALIAS = 6,     /* an output overlaps an input or another output       */
-  ATTN_ERR_LAUNCH = 7     /* the kernel launch failed (hipGetLastError)          */
+  ATTN_ERR_LAUNCH = 7,    /* the kernel launch failed (hipGetLastError)          */
+  ATTN_ERR_MASK = 8       /* causal is not 0, 1 or 2                             */
 } attn_status;
 
 /*
@@ -72,7 +77,9 @@ typedef enum {
  *   d          head dimension: 64 or 128.
  *   scale      multiplier of Q K^T, any finite value (the usual d^-0.5 of
  *              [PT2CUDA] step 1).
- *   causal     nonzero: key j is visible to row i only when j <= i.
+ *   causal     0: no causal mask; 1: key j is visible to row i only when
+ *              j <= i; 2: only when j <= i + N_k - N_q. Other values:
+ *              ATTN_ERR_MASK.
  *   seqlens_k  int32 [B] device array or NULL: valid key count per batch,
  *              clamped to [0, N_k] on the device.
  *   q_start    int32 [B] device array or NULL: rows i < q_start[b] of batch b

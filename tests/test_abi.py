@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert ta.attn_version() == 10100
-    for code in range(8):
+    for code in range(9):
         s = ta.attn_status_str(code)
         assert s and s != "unknown status"
     assert ta.attn_status_str(99) == "unknown status"
@@ -73,6 +73,8 @@ def call(**kw):
     (dict(lse=A16 * 4 + 64), ta.ATTN_ERR_ALIAS),    # lse inside o
     (dict(B=1 << 20, H=1 << 12, N_q=1 << 12), ta.ATTN_ERR_SHAPE),   # too many workgroups
     (dict(N_k=1 << 23, d=128), ta.ATTN_ERR_SHAPE),   # one head's K spans 2 GB
+    (dict(causal=3), ta.ATTN_ERR_MASK),
+    (dict(causal=-1), ta.ATTN_ERR_MASK),
 ])
 def test_argument_errors_return_before_any_hip_call(lib, kw, status):
     assert call(**kw) == status
@@ -120,6 +122,7 @@ def call_bwd(**kw):
     (dict(dq=A16 * 5 + 16), ta.ATTN_ERR_ALIAS),       # dq overlaps dout
     (dict(dv=A16 * 8 + 32), ta.ATTN_ERR_ALIAS),       # dv overlaps dk
     (dict(delta=A16 * 6), ta.ATTN_ERR_ALIAS),         # delta is lse
+    (dict(causal=7), ta.ATTN_ERR_MASK),
 ])
 def test_bwd_argument_errors_return_before_any_hip_call(lib, kw, status):
     assert call_bwd(**kw) == status
@@ -128,3 +131,9 @@ def test_bwd_argument_errors_return_before_any_hip_call(lib, kw, status):
 def test_bwd_empty_problem_is_a_noop(lib):
     assert call_bwd(B=0, q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0, delta=0) == ta.ATTN_OK
     assert call_bwd(N_q=0, N_k=0, q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0, delta=0) == ta.ATTN_OK
+
+
+def test_causal_mode_names():
+    assert [ta.causal_mode(x) for x in (False, True, "none", "top_left", "bottom_right", 2)] == [0, 1, 0, 1, 2, 2]
+    with pytest.raises(ValueError):
+        ta.causal_mode("diagonal")

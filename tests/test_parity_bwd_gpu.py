@@ -155,3 +155,21 @@ def test_bwd_full_size_heads(name):
                         {"dq": rq, "dk": rk, "dv": rv})
         print(f"  {name} b={b} h={h}: {r}", flush=True)
         assert r.ok, f"{name} b={b} h={h}: {r}"
+
+
+BR = [
+    # B, H, N_q, N_k, d, seqlens, q_start
+    (1, 2, 1, 500, 128, None, None),
+    (1, 2, 100, 300, 64, None, None),
+    (1, 1, 300, 77, 128, None, None),
+    (2, 2, 257, 511, 128, [511, 300], [0, 40]),
+]
+
+
+@pytest.mark.parametrize("case", BR, ids=[f"{c[0]}x{c[1]}x{c[2]}x{c[3]}_d{c[4]}{'_var' if c[5] else ''}" for c in BR])
+def test_bwd_bottom_right_causal(case):
+    B, H, nq, nk, d, sl, qs = case
+    q, k, v = make_random(B, H, nq, nk, d, seed=nq + 5 * nk + d)
+    g = make_dout((B, H, nq, d), seed=nq + nk)
+    compare(q, k, v, g, np.float32(d ** -0.5), 2, None if sl is None else np.array(sl, np.int32),
+            None if qs is None else np.array(qs, np.int32))

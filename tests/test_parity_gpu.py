@@ -262,3 +262,25 @@ def test_full_size_workload_sampled(name):
             assert np.all(np.isfinite(lse[b, :, qs:]))
     else:
         assert np.all(np.isfinite(lse))
+
+
+# Bottom-right causal (causal = 2): key j visible to row i iff j <= i + N_k - N_q.
+BR = [
+    # B, H, N_q, N_k, d, seqlens, q_start
+    (1, 2, 1, 1000, 128, None, None),        # one new query against a cache of keys
+    (1, 2, 100, 300, 64, None, None),
+    (1, 1, 300, 77, 128, None, None),        # rows i < 223 see no key
+    (2, 2, 257, 511, 128, [511, 300], [0, 40]),
+    (2, 1, 640, 1200, 64, [1000, 1200], None),
+]
+
+
+@pytest.mark.parametrize("case", BR, ids=[f"{c[0]}x{c[1]}x{c[2]}x{c[3]}_d{c[4]}{'_var' if c[5] else ''}" for c in BR])
+def test_bottom_right_causal(case):
+    B, H, nq, nk, d, sl, qs = case
+    q, k, v = make_random(B, H, nq, nk, d, seed=nq + 3 * nk + d)
+    o, lse = compare_full(q, k, v, np.float32(d ** -0.5), 2, None if sl is None else np.array(sl, np.int32),
+                          None if qs is None else np.array(qs, np.int32))
+    if nq > nk and sl is None:
+        dead = nq - nk
+        assert np.all(o[:, :, :dead] == 0) and np.all(np.isneginf(lse[:, :, :dead]))

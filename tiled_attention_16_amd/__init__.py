@@ -22,6 +22,20 @@ ATTN_ERR_SCALE = 4
 ATTN_ERR_ALIGN = 5
 ATTN_ERR_ALIAS = 6
 ATTN_ERR_LAUNCH = 7
+ATTN_ERR_MASK = 8
+
+# causal modes of the C ABI
+CAUSAL_NONE, CAUSAL_TOP_LEFT, CAUSAL_BOTTOM_RIGHT = 0, 1, 2
+
+
+def causal_mode(causal) -> int:
+    """Map ``False``/``True``/``"top_left"``/``"bottom_right"`` (or 0/1/2) to the ABI's causal mode."""
+    if isinstance(causal, str):
+        modes = {"none": 0, "top_left": 1, "bottom_right": 2}
+        if causal not in modes:
+            raise ValueError(f"causal must be one of {sorted(modes)}, got {causal!r}")
+        return modes[causal]
+    return int(causal)
 
 # every symbol include/attn.h declares
 EXPORTS = ("attn_bwd", "attn_fwd", "attn_status_str", "attn_version")
@@ -73,13 +87,15 @@ def attn_fwd_raw(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N_q: 
     """The C entry point with plain integers for pointers; returns the status code."""
     return int(load_library().attn_fwd(q or None, k or None, v or None, o or None, lse or None,
                                        int(B), int(H), int(N_q), int(N_k), int(d), ctypes.c_float(scale),
-                                       1 if causal else 0, seqlens_k or None, q_start or None, stream or None))
+                                       causal_mode(causal), seqlens_k or None, q_start or None, stream or None))
 
 
 def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None, seqlens_k=None, q_start=None,
              return_lse: bool = True, out=None, lse=None, stream=None) -> Tuple[object, Optional[object]]:
     """Fused attention forward on bf16 ``[B, H, N, d]`` CUDA (HIP) tensors.
 
+    ``causal``: False (none), True or "top_left" (key j visible to row i iff
+    j <= i), "bottom_right" (iff j <= i + N_k - N_q).
     Returns ``(o, lse)``; ``lse`` is None unless ``return_lse``. ``scale``
     defaults to ``d ** -0.5``. ``seqlens_k`` / ``q_start`` are optional int32
     device tensors of shape ``[B]``. The kernel is launched on ``stream`` (a
@@ -113,7 +129,7 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None, se
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     status = lib.attn_fwd(q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None,
                           out.data_ptr() or None, (lse.data_ptr() or None) if lse is not None else None,
-                          B, H, N_q, N_k, d, ctypes.c_float(scale), 1 if causal else 0,
+                          B, H, N_q, N_k, d, ctypes.c_float(scale), causal_mode(causal),
                           seqlens_k.data_ptr() if seqlens_k is not None else None,
                           q_start.data_ptr() if q_start is not None else None,
                           ctypes.c_void_p(st.cuda_stream))
@@ -128,7 +144,7 @@ def attn_bwd_raw(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, d
     """The C entry point ``attn_bwd`` with plain integers for pointers; returns the status code."""
     p = [x or None for x in (q, k, v, o, dout, lse, dq, dk, dv, delta)]
     return int(load_library().attn_bwd(*p, int(B), int(H), int(N_q), int(N_k), int(d), ctypes.c_float(scale),
-                                       1 if causal else 0, seqlens_k or None, q_start or None, stream or None))
+                                       causal_mode(causal), seqlens_k or None, q_start or None, stream or None))
 
 
 def attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] = None, seqlens_k=None,
@@ -176,7 +192,7 @@ def attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[flo
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     ptr = lambda t: t.data_ptr() or None  # noqa: E731
     status = lib.attn_bwd(ptr(q), ptr(k), ptr(v), ptr(o), ptr(dout), ptr(lse), ptr(dq), ptr(dk), ptr(dv),
-                          ptr(delta), B, H, N_q, N_k, d, ctypes.c_float(scale), 1 if causal else 0,
+                          ptr(delta), B, H, N_q, N_k, d, ctypes.c_float(scale), causal_mode(causal),
                           seqlens_k.data_ptr() if seqlens_k is not None else None,
                           q_start.data_ptr() if q_start is not None else None, ctypes.c_void_p(st.cuda_stream))
     if status != ATTN_OK:

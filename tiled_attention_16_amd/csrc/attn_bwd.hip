@@ -206,7 +206,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const f32x2* __restrict__ stats, uint16_t* __restrict__ dQ, int H, int N_q,
-    int N_k, float c, float scale, int causal, const int32_t* __restrict__ seqlens_k,
+    int N_k, float c, float scale, int causal, int coff, const int32_t* __restrict__ seqlens_k,
     const int32_t* __restrict__ q_start, int n_qt) {
   using R = Ring<D>;
   constexpr int kStage = 2 * R::kBlkBytes;   // [K block][V block]
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
   const int q0 = qt * kTile;
   const int q_end = min(q0 + kTile, N_q);
   int kv_end = kv;
-  if (causal) kv_end = min(kv_end, q_end);
+  if (causal) kv_end = min(kv_end, max(q_end + coff, 0));   // row i sees keys <= i + coff
   if (qs >= q_end) kv_end = 0;
   const int nblk = (kv_end + kBlk - 1) / kBlk;
 
@@ -254,13 +254,13 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
     dl = st[1];
   }
   // key j is allowed for this row iff j <= klim
-  const int klim = (!row_ok || row < qs) ? -1 : min(kv - 1, causal ? row : 0x7fffffff);
+  const int klim = (!row_ok || row < qs) ? -1 : min(kv - 1, causal ? row + coff : 0x7fffffff);
   // Blocks n < full_below need no mask for any row of this wave: all its rows
   // exist and are past q_start, and every key of the block is below kv and
   // (causal) at or below the wave's first row.
   const int wrow0 = q0 + kBlk * wave;
   int full_below = 0;
-  if (wrow0 + kBlk <= N_q && wrow0 >= qs) full_below = min(kv, causal ? wrow0 + 1 : kv) / kBlk;
+  if (wrow0 + kBlk <= N_q && wrow0 >= qs) full_below = min(kv, causal ? max(wrow0 + 1 + coff, 0) : kv) / kBlk;
   full_below = __builtin_amdgcn_readfirstlane(full_below);
 
   wait_loads();
@@ -271,9 +271,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
   __syncthreads();
   const i32x4 k_rs = rsrc(K + k_base, (uint32_t)kv_end * 2 * D), v_rs = rsrc(V + k_base, (uint32_t)kv_end * 2 * D);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
-  int coff[R::kCpw];
+  int cpoff[R::kCpw];
 #pragma unroll
-  for (int i = 0; i < R::kCpw; ++i) coff[i] = copy_lane_off<D>(wave * R::kCpw + i, lane);
+  for (int i = 0; i < R::kCpw; ++i) cpoff[i] = copy_lane_off<D>(wave * R::kCpw + i, lane);
   auto issue = [&](int n) {   // block n into stage n % kDepth
     const uint32_t st = lds0 + (uint32_t)(n % kDepth) * kStage;
     const uint32_t soff = (uint32_t)n * R::kBlkBytes;
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
     for (int i = 0; i < R::kCpw; ++i) {
       const int ci = wave * R::kCpw + i;
       const bool is_v = ci >= R::kKB;
-      copy_kb(is_v ? v_rs : k_rs, soff, coff[i], st + (uint32_t)ci * 1024);
+      copy_kb(is_v ? v_rs : k_rs, soff, cpoff[i], st + (uint32_t)ci * 1024);
     }
   };
 
@@ -360,7 +360,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const f32x2* __restrict__ stats, uint16_t* __restrict__ dK,
-    uint16_t* __restrict__ dV, int H, int N_q, int N_k, float c, float scale, int causal,
+    uint16_t* __restrict__ dV, int H, int N_q, int N_k, float c, float scale, int causal, int coff,
     const int32_t* __restrict__ seqlens_k, const int32_t* __restrict__ q_start, int n_kt) {
   using R = Ring<D>;
   constexpr int kStage = 2 * R::kBlkBytes + 1024;   // [Q block][dO block][stats of the 32 rows]
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
   const size_t q_base = (size_t)bh * N_q * D, k_base = (size_t)bh * N_k * D;
   const int k0 = kt * kTile;
   // query rows that can see a key of this tile: [r_begin, N_q)
-  int r_begin = max(qs, causal ? k0 : 0);
+  int r_begin = max(qs, causal ? max(k0 - coff, 0) : 0);   // row i sees keys <= i + coff
   if (k0 >= kv) r_begin = N_q;                  // every key of the tile is masked
   const int blk0 = r_begin / kBlk;
   const int nblk = r_begin < N_q ? (N_q + kBlk - 1) / kBlk - blk0 : 0;
@@ -410,9 +410,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
   const i32x4 q_rs = rsrc(Q + q_base, rows_bytes), g_rs = rsrc(dO + q_base, rows_bytes);
   const i32x4 s_rs = rsrc(stats + (size_t)bh * N_q, (uint32_t)N_q * 8);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
-  int coff[R::kCpw];
+  int cpoff[R::kCpw];
 #pragma unroll
-  for (int i = 0; i < R::kCpw; ++i) coff[i] = copy_lane_off<D>(wave * R::kCpw + i, lane);
+  for (int i = 0; i < R::kCpw; ++i) cpoff[i] = copy_lane_off<D>(wave * R::kCpw + i, lane);
   // the stats copy (wave 0): lanes 0..15 bring the 256 bytes of the block's 32 rows
   const int soff_lane = lane < 16 ? 16 * lane : 0x40000000;
   // Ring of kDepthKV stages: while block n's dV/dK products run, block n+1's
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
     for (int i = 0; i < R::kCpw; ++i) {
       const int ci = wave * R::kCpw + i;
       const bool is_g = ci >= R::kKB;
-      copy_kb(is_g ? g_rs : q_rs, r0 * 2 * D, coff[i], st + (uint32_t)ci * 1024);
+      copy_kb(is_g ? g_rs : q_rs, r0 * 2 * D, cpoff[i], st + (uint32_t)ci * 1024);
     }
     if (wave == 0) copy_kb(s_rs, r0 * 8, soff_lane, st + 2 * R::kBlkBytes);
   };
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
   // after the wave's last key
   auto block_full = [&](int n) {
     const int r0 = (blk0 + n) * kBlk;
-    return wkey_live && r0 + kBlk <= N_q && r0 >= qs && (!causal || r0 >= wkey0 + kBlk - 1);
+    return wkey_live && r0 + kBlk <= N_q && r0 >= qs && (!causal || r0 + coff >= wkey0 + kBlk - 1);
   };
   auto softmax_grad = [&](auto full_t, int n, const f32x16& s, const f32x16& dp, uint32_t (&wp)[8],
                           uint32_t (&wd)[8]) __attribute__((always_inline)) {
@@ -494,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
           const int qrow = r0 + 8 * g + 4 * hf + e;
-          const bool ok = key_live && qrow < N_q && qrow >= qs && (!causal || key <= qrow);
+          const bool ok = key_live && qrow < N_q && qrow >= qs && (!causal || key <= qrow + coff);
           p[e] = ok ? __builtin_amdgcn_exp2f(s[r] * c - l2[e]) : 0.f;
           ds[e] = ok ? p[e] * (dp[r] - dd[e]) : 0.f;
         }
@@ -600,6 +600,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   if (B < 0 || H < 0 || N_q < 0 || N_k < 0) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  if (causal < 0 || causal > 2) return ATTN_ERR_MASK;
   const long long bh = (long long)B * H;
   if (bh == 0 || (N_q == 0 && N_k == 0)) return ATTN_OK;
   const bool has_q = N_q > 0, has_k = N_k > 0;
@@ -627,7 +628,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   }
 
   const float c = scale * kLog2e;
-  int causal01 = causal ? 1 : 0, Hi = H, Nq = N_q, Nk = N_k;
+  int causal01 = causal ? 1 : 0, coff = causal == 2 ? N_k - N_q : 0, Hi = H, Nq = N_q, Nk = N_k;
   float cc = c, sc = scale;
   const uint16_t *qp = (const uint16_t*)q, *kp = (const uint16_t*)k, *vp = (const uint16_t*)v,
                  *op = (const uint16_t*)o, *gp = (const uint16_t*)dout;
@@ -645,8 +646,8 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
     int nqt = (int)n_qt;
     void* a1[] = {(void*)&qp, (void*)&kp, (void*)&vp, (void*)&gp, (void*)&stp, (void*)&dqp, (void*)&Hi,
-                  (void*)&Nq, (void*)&Nk, (void*)&cc, (void*)&sc, (void*)&causal01, (void*)&seqlens_k,
-                  (void*)&q_start, (void*)&nqt};
+                  (void*)&Nq, (void*)&Nk, (void*)&cc, (void*)&sc, (void*)&causal01, (void*)&coff,
+                  (void*)&seqlens_k, (void*)&q_start, (void*)&nqt};
     const void* f1 = d == 128 ? (const void*)attn_bwd_dq_kernel<128> : (const void*)attn_bwd_dq_kernel<64>;
     e = hipLaunchKernel(f1, dim3((unsigned)(bh * n_qt)), dim3(kThreads), a1, 0, stream);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
@@ -654,7 +655,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   if (has_k) {
     int nkt = (int)n_kt;
     void* a2[] = {(void*)&qp, (void*)&kp, (void*)&vp, (void*)&gp, (void*)&stp, (void*)&dkp, (void*)&dvp,
-                  (void*)&Hi, (void*)&Nq, (void*)&Nk, (void*)&cc, (void*)&sc, (void*)&causal01,
+                  (void*)&Hi, (void*)&Nq, (void*)&Nk, (void*)&cc, (void*)&sc, (void*)&causal01, (void*)&coff,
                   (void*)&seqlens_k, (void*)&q_start, (void*)&nkt};
     const void* f2 = d == 128 ? (const void*)attn_bwd_dkdv_kernel<128> : (const void*)attn_bwd_dkdv_kernel<64>;
     e = hipLaunchKernel(f2, dim3((unsigned)(bh * n_kt)), dim3(kThreads), a2, 0, stream);

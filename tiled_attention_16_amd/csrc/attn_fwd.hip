@@ -32,7 +32,8 @@
 //         slice in lane ^ 32): a row max is an in-register max plus one
 //         permlane32 swap, and the row sum needs no cross-lane step until the
 //         very end.
-//   mask  only on slices that cross the causal diagonal, the valid key length
+//   mask  only on slices that cross the causal diagonal (j <= i, or j <= i +
+//         N_k - N_q when aligned bottom-right), the valid key length
 //         or the masked leading rows: the score becomes -inf.
 //   m     the exponent's subtrahend per row. The first slice sets it to that
 //         slice's row max. After that it is a stale running max: it is raised
@@ -192,7 +193,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int H, int N_q, int N_k, float c, int neg_scale,
-    int causal, const int32_t* __restrict__ seqlens_k, const int32_t* __restrict__ q_start, int n_qt,
+    int causal, int coff, const int32_t* __restrict__ seqlens_k, const int32_t* __restrict__ q_start, int n_qt,
     int n_wg) {
   using T = Slice<D>;
   __shared__ __attribute__((aligned(1024))) char smem[T::kLds];
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   const int q0 = qt * kBM;
   const int q_end = min(q0 + kBM, N_q);
   int kv_end = kv;                                 // keys this workgroup can see
-  if (causal) kv_end = min(kv_end, q_end);
+  if (causal) kv_end = min(kv_end, max(q_end + coff, 0));   // row i sees keys <= i + coff
   if (qs >= q_end) kv_end = 0;                     // every row of the tile is masked
   // The copies only need the keys the tile can see: keys past kv_end (beyond
   // the causal limit of the tile's last row) come back as nothing.
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // slices: nh_wg for the workgroup, nh (a prefix) for this wave
   const int nh_wg = (kv_end + kSlice - 1) / kSlice;
   int nh = wave_live ? nh_wg : 0;
-  if (causal) nh = min(nh, row_hi / kSlice + 1);
+  if (causal) nh = min(nh, row_hi + coff < 0 ? 0 : (row_hi + coff) / kSlice + 1);
   nh = __builtin_amdgcn_readfirstlane(nh);
 
   // ---- Q rows -> VGPRs as the B operand of S^T = K Q^T ----
@@ -400,7 +401,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     const int row = row_lo + 32 * rb + (lane & 31);
-    klim[rb] = row < qs ? -1 : min(kv - 1, causal ? row : 0x7fffffff);
+    klim[rb] = row < qs ? -1 : min(kv - 1, causal ? row + coff : 0x7fffffff);
   }
   // Masking is needed only where slice h crosses that bound for some row of
   // the wave: from the slice holding key kv-1 on (the first h with
@@ -408,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // diagonal on under a causal mask, and everywhere when masked leading rows
   // are in the wave.
   int mask_from = kv / kSlice;
-  if (causal) mask_from = min(mask_from, (row_lo + 1) / kSlice);
+  if (causal) mask_from = min(mask_from, max(row_lo + 1 + coff, 0) / kSlice);
   if (row_lo < qs) mask_from = 0;
   mask_from = __builtin_amdgcn_readfirstlane(mask_from);
   auto need_mask = [&](int h) __attribute__((always_inline)) { return h >= mask_from; };
@@ -760,6 +761,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   if (B < 0 || H < 0 || N_q < 0 || N_k < 0) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  if (causal < 0 || causal > 2) return ATTN_ERR_MASK;
   if ((long long)B * H * N_q == 0) return ATTN_OK;
   if (!q || !o) return ATTN_ERR_NULL;
   if (N_k > 0 && (!k || !v)) return ATTN_ERR_NULL;
@@ -791,9 +793,10 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   const uint16_t* kp = (const uint16_t*)k;
   const uint16_t* vp = (const uint16_t*)v;
   uint16_t* op = (uint16_t*)o;
-  int causal01 = causal ? 1 : 0, n_qt_i = (int)n_qt, n_wg_i = (int)n_wg;
+  // causal mode 1: key j visible to row i iff j <= i; mode 2: iff j <= i + N_k - N_q
+  int causal01 = causal ? 1 : 0, coff = causal == 2 ? N_k - N_q : 0, n_qt_i = (int)n_qt, n_wg_i = (int)n_wg;
   void* args[] = {(void*)&qp, (void*)&kp, (void*)&vp, (void*)&op, (void*)&lse, (void*)&H, (void*)&N_q,
-                  (void*)&N_k, (void*)&c, (void*)&neg, (void*)&causal01,
+                  (void*)&N_k, (void*)&c, (void*)&neg, (void*)&causal01, (void*)&coff,
                   (void*)&seqlens_k, (void*)&q_start, (void*)&n_qt_i, (void*)&n_wg_i};
   const void* fn = d == 128 ? (const void*)attn_fwd_kernel<128> : (const void*)attn_fwd_kernel<64>;
   const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)n_wg), dim3(kThreads), args, 0, stream);
@@ -810,6 +813,7 @@ extern "C" const char* attn_status_str(int status) {
     case ATTN_ERR_ALIGN: return "misaligned pointer (bf16 tensors need 16 bytes, lse and delta 4)";
     case ATTN_ERR_ALIAS: return "output overlaps an input or the other output";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    case ATTN_ERR_MASK: return "causal must be 0 (none), 1 (top-left) or 2 (bottom-right)";
     default: return "unknown status";
   }
 }
