@@ -87,9 +87,24 @@ def _rows_blocks(rows: np.ndarray, block: int):
         yield rows[s:s + block]
 
 
+def dense_allowed(attn_mask: Optional[np.ndarray], b: int, h: int, rows: np.ndarray) -> Optional[np.ndarray]:
+    """Rows ``rows`` of the boolean mask for (b, h), or None without a mask.
+
+    ``attn_mask`` is boolean, broadcastable to [B, H, N_q, N_k], True where
+    row i may attend to key j (the SDPA convention for a boolean mask,
+    [PROFILE3]; [PT2CUDA] step 1 writes the same rule as scores where the mask
+    is 0 becoming -inf). It is intersected with the rule masks.
+    """
+    if attn_mask is None:
+        return None
+    m = np.asarray(attn_mask, dtype=bool)
+    return m[b if m.shape[0] > 1 else 0, h if m.shape[1] > 1 else 0][rows]
+
+
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool = False,
               seqlens_k: Optional[np.ndarray] = None, q_start: Optional[np.ndarray] = None,
-              rows: Optional[Sequence[int]] = None, return_probs: bool = False, row_block: int = 1024):
+              rows: Optional[Sequence[int]] = None, return_probs: bool = False, row_block: int = 1024,
+              attn_mask: Optional[np.ndarray] = None):
     """Unfused scaled-dot-product attention in float64.
 
     q: [B, H, N_q, d]; k, v: [B, H, N_k, d] (float64, any values).
@@ -129,6 +144,9 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal:
                 r = blk.shape[0]
                 s = (q[b, h, blk] @ k[b, h].T) * sc
                 ok = allowed_mask(n_q, n_k, causal, kv, qs, rows=blk)
+                dm = dense_allowed(attn_mask, b, h, blk)
+                if dm is not None:
+                    ok = ok & dm
                 s[~ok] = -np.inf
                 m = s.max(axis=1)
                 live = m > -np.inf

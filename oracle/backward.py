@@ -39,11 +39,11 @@ from .attention import attention
 
 def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, scale: float,
                   causal: bool = False, seqlens_k: Optional[np.ndarray] = None,
-                  q_start: Optional[np.ndarray] = None):
+                  q_start: Optional[np.ndarray] = None, attn_mask: Optional[np.ndarray] = None):
     """Gradients (dQ, dK, dV) of attention in float64, shapes of q, k, v.
 
     Rows and keys follow the masking rules of ``oracle.attention``
-    (causal j <= i, keys j < seqlens_k[b], rows i >= q_start[b]).
+    (causal, keys j < seqlens_k[b], rows i >= q_start[b], the boolean attn_mask).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -58,7 +58,8 @@ def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
         return dq, dk, dv
     sc = np.float64(scale)
     # P of the forward definition, every row at once (the oracle's own forward)
-    _, _, p = attention(q, k, v, scale, causal, seqlens_k=seqlens_k, q_start=q_start, return_probs=True)
+    _, _, p = attention(q, k, v, scale, causal, seqlens_k=seqlens_k, q_start=q_start, return_probs=True,
+                        attn_mask=attn_mask)
     for b in range(B):
         for h in range(H):
             pb = p[b, h]                                   # [n_q, n_k]

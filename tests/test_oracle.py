@@ -312,3 +312,65 @@ def test_bottom_right_torch_cross_check():
                                                             scale=0.4).numpy()
     o, _ = attention(q, k, v, 0.4, 2)
     np.testing.assert_allclose(o, want, atol=1e-12)
+
+
+# ---------------------------------------------------------------- boolean attn_mask (True = may attend)
+def softmax_loops(q, k, v, scale, allowed):
+    """Pure-Python loops over one head: the definition written out entry by entry."""
+    n_q, n_k = allowed.shape
+    out = np.zeros((n_q, v.shape[1]))
+    lse = np.full(n_q, -np.inf)
+    for i in range(n_q):
+        sc = [sum(q[i, t] * k[j, t] for t in range(q.shape[1])) * scale for j in range(n_k) if allowed[i, j]]
+        idx = [j for j in range(n_k) if allowed[i, j]]
+        if not idx:
+            continue
+        m = max(sc)
+        e = [math.exp(x - m) for x in sc]
+        tot = sum(e)
+        for w, j in zip(e, idx):
+            out[i] += w / tot * v[j]
+        lse[i] = m + math.log(tot)
+    return out, lse
+
+
+def test_dense_mask_brute_force_loops():
+    rng = np.random.default_rng(71)
+    q, k, v = rnd((2, 2, 6, 3), 72), rnd((2, 2, 7, 3), 73), rnd((2, 2, 7, 3), 74)
+    mask = rng.random((2, 1, 6, 7)) < 0.6          # broadcast over heads
+    mask[1, 0, 2] = False                           # one fully masked row
+    o, lse = attention(q, k, v, 0.5, False, attn_mask=mask)
+    for b in range(2):
+        for h in range(2):
+            wo, wl = softmax_loops(q[b, h], k[b, h], v[b, h], 0.5, mask[b, 0])
+            np.testing.assert_allclose(o[b, h], wo, atol=1e-13)
+            np.testing.assert_allclose(lse[b, h], wl, atol=1e-13)
+    assert np.all(o[1, :, 2] == 0) and np.all(np.isneginf(lse[1, :, 2]))
+
+
+def test_dense_mask_reproduces_the_rule_masks():
+    q, k, v = rnd((2, 2, 9, 4), 75), rnd((2, 2, 9, 4), 76), rnd((2, 2, 9, 4), 77)
+    sl, qs = np.array([9, 5]), np.array([0, 3])
+    want_o, want_l = attention(q, k, v, 0.6, True, seqlens_k=sl, q_start=qs)
+    m = np.zeros((2, 1, 9, 9), bool)
+    for b in range(2):
+        m[b, 0] = allowed_mask(9, 9, True, sl[b], qs[b])
+    o, lse = attention(q, k, v, 0.6, False, attn_mask=m)
+    np.testing.assert_allclose(o, want_o, atol=1e-14)
+    np.testing.assert_array_equal(np.isneginf(lse), np.isneginf(want_l))
+    np.testing.assert_allclose(lse[~np.isneginf(lse)], want_l[~np.isneginf(want_l)], atol=1e-14)
+    # the mask intersects the rules: all-True changes nothing
+    o2, _ = attention(q, k, v, 0.6, True, seqlens_k=sl, q_start=qs, attn_mask=np.ones((1, 1, 9, 9), bool))
+    np.testing.assert_array_equal(o2, want_o)
+
+
+def test_dense_mask_torch_cross_check():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(78)
+    q, k, v = rnd((2, 3, 7, 5), 79), rnd((2, 3, 10, 5), 80), rnd((2, 3, 10, 5), 81)
+    mask = rng.random((2, 3, 7, 10)) < 0.5
+    mask[..., 0] = True                              # no fully masked row (torch gives NaN there)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q), torch.tensor(k), torch.tensor(v), attn_mask=torch.tensor(mask), scale=0.35).numpy()
+    o, _ = attention(q, k, v, 0.35, False, attn_mask=mask)
+    np.testing.assert_allclose(o, want, atol=1e-12)

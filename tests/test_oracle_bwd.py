@@ -174,3 +174,32 @@ def test_finite_differences_bottom_right():
             lm = loss(args["q"], args["k"], args["v"], g, 0.6, 2, None, None)
             num[idx] = (lp - lm) / (2 * eps)
         np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-7, err_msg=f"d{name}")
+
+
+def test_finite_differences_dense_mask():
+    n_q, n_k, d = 5, 6, 3
+    q, k, v, g = rnd((1, 2, n_q, d), 85), rnd((1, 2, n_k, d), 86), rnd((1, 2, n_k, d), 87), rnd((1, 2, n_q, d), 88)
+    mask = np.random.default_rng(89).random((1, 2, n_q, n_k)) < 0.5
+    mask[0, 1, 3] = False
+    dq, dk, dv = attention_bwd(q, k, v, g, 0.6, False, attn_mask=mask)
+
+    def lossm(q_, k_, v_):
+        o, _ = attention(q_, k_, v_, 0.6, False, attn_mask=mask)
+        return float((o * g).sum())
+    eps = 1e-6
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            args = {"q": q, "k": k, "v": v}
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args[name] = xp
+            lp = lossm(args["q"], args["k"], args["v"])
+            args[name] = xm
+            lm = lossm(args["q"], args["k"], args["v"])
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-7, err_msg=f"d{name}")
+    assert np.all(dq[0, 1, 3] == 0)

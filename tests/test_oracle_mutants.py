@@ -27,6 +27,8 @@ MUTANTS = [
     ("bottom-right offset reversed", "return n_k - n_q if int(causal) == 2 else 0",
      "return n_q - n_k if int(causal) == 2 else 0"),
     ("bottom-right treated as top-left", "return n_k - n_q if int(causal) == 2 else 0", "return 0"),
+    ("dense mask ignored", "                    ok = ok & dm", "                    pass"),
+    ("dense mask inverted", "                    ok = ok & dm", "                    ok = ok & ~dm"),
     ("P times K instead of V", "out[b, h, pos:pos + r] = p[:, :n_valid] @ v[b, h, :n_valid]",
      "out[b, h, pos:pos + r] = p[:, :n_valid] @ k[b, h, :n_valid]"),
 ]
