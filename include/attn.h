@@ -56,7 +56,7 @@ typedef enum {
   ATTN_ERR_ALIGN = 5,     /* a bf16 tensor not 16-byte aligned, lse/delta 4-byte */
   ATTN_ERR_ALIAS = 6,     /* an output overlaps an input or another output       */
   ATTN_ERR_LAUNCH = 7,    /* the kernel launch failed (hipGetLastError)          */
-  ATTN_ERR_MASK = 8       /* causal is not 0, 1 or 2                             */
+  ATTN_ERR_MASK = 8       /* causal not 0/1/2, or a bad mask layout              */
 } attn_status;
 
 /*
@@ -96,6 +96,43 @@ typedef enum {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int N_q, int N_k, int d, float scale, int causal,
              const int32_t* seqlens_k, const int32_t* q_start, hipStream_t stream);
+
+/*
+ * attn_fwd_masked - attn_fwd with a general boolean mask intersected with the
+ * rules above (the attn_mask of the pages' interfaces: [PT2CUDA] step 1
+ * masks scores where the mask is 0, [PROFILE3] passes attn_mask to SDPA).
+ *
+ *   mask_bits        uint32 device array, 16-byte aligned, read only: for batch b,
+ *                    head h, row i the words mask_bits[b*mask_stride_b +
+ *                    h*mask_stride_h + i*mask_row_words + w]; bit t of word w
+ *                    set means row i may attend to key 32*w + t. Bits of keys
+ *                    >= N_k are ignored.
+ *   mask_stride_b,   word strides between batches and heads (>= 0; 0 broadcasts
+ *   mask_stride_h    one mask over that dimension).
+ *   mask_row_words   words per row: >= ceil(N_k / 32) and a multiple of 8 (so a
+ *                    row's words for 8 key slices are one aligned 32-byte piece).
+ * Every other argument, and the outputs, as in attn_fwd. A row whose allowed
+ * set is empty outputs O = 0, LSE = -inf. Errors: mask_bits NULL (with work to
+ * do) ATTN_ERR_NULL, misaligned ATTN_ERR_ALIGN, bad row words or strides
+ * ATTN_ERR_MASK, N_q * mask_row_words * 4 >= 2^31 ATTN_ERR_SHAPE.
+ */
+int attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                    const int32_t* seqlens_k, const int32_t* q_start,
+                    const uint32_t* mask_bits, long long mask_stride_b, long long mask_stride_h,
+                    int mask_row_words, hipStream_t stream);
+
+/*
+ * attn_mask_pack - pack a byte mask into the bit layout attn_fwd_masked reads.
+ *   mask       uint8 device array [rows, N_k], row major; nonzero = may attend.
+ *   bits       uint32 device array [rows, row_words], written in full (bits of
+ *              keys >= N_k are 0).
+ *   row_words  >= ceil(N_k / 32) (use a multiple of 8 for attn_fwd_masked).
+ * One kernel launch on `stream`. Errors: bad sizes ATTN_ERR_SHAPE, NULL
+ * pointers ATTN_ERR_NULL, bits not 4-byte aligned ATTN_ERR_ALIGN.
+ */
+int attn_mask_pack(const uint8_t* mask, uint32_t* bits, long long rows, int N_k, int row_words,
+                   hipStream_t stream);
 
 /*
  * attn_bwd - gradients of attn_fwd: dQ, dK, dV (bf16) from dO (bf16).

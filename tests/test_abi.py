@@ -137,3 +137,36 @@ def test_causal_mode_names():
     assert [ta.causal_mode(x) for x in (False, True, "none", "top_left", "bottom_right", 2)] == [0, 1, 0, 1, 2, 2]
     with pytest.raises(ValueError):
         ta.causal_mode("diagonal")
+
+
+def call_masked(**kw):
+    args = dict(q=A16, k=A16 * 2, v=A16 * 3, o=A16 * 4, lse=A16 * 5, B=1, H=2, N_q=8, N_k=300, d=64, scale=0.125,
+                causal=False, seqlens_k=0, q_start=0, mask_bits=A16 * 40, mask_stride_b=0, mask_stride_h=0,
+                mask_row_words=16, stream=0)
+    args.update(kw)
+    return ta.attn_fwd_masked_raw(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mask_bits=0), ta.ATTN_ERR_NULL),
+    (dict(mask_bits=A16 * 40 + 4), ta.ATTN_ERR_ALIGN),
+    (dict(mask_row_words=8), ta.ATTN_ERR_MASK),          # 300 keys need 10 words
+    (dict(mask_row_words=12), ta.ATTN_ERR_MASK),         # not a multiple of 8
+    (dict(mask_stride_h=-1), ta.ATTN_ERR_MASK),
+    (dict(causal=5), ta.ATTN_ERR_MASK),
+    (dict(d=80), ta.ATTN_ERR_HEAD_DIM),
+    (dict(N_q=1 << 22, mask_row_words=1 << 10), ta.ATTN_ERR_SHAPE),
+])
+def test_masked_argument_errors_return_before_any_hip_call(lib, kw, status):
+    assert call_masked(**kw) == status
+
+
+def test_mask_pack_argument_errors(lib):
+    assert lib.attn_mask_pack(A16, A16 * 2, 4, 300, 9, None) == ta.ATTN_ERR_SHAPE    # 300 keys need 10 words
+    assert lib.attn_mask_pack(A16, 0, 4, 300, 16, None) == ta.ATTN_ERR_NULL
+    assert lib.attn_mask_pack(A16, A16 * 2 + 2, 4, 300, 16, None) == ta.ATTN_ERR_ALIGN
+    assert lib.attn_mask_pack(0, 0, 0, 300, 16, None) == ta.ATTN_OK
+
+
+def test_mask_row_words():
+    assert [ta.mask_row_words(n) for n in (1, 256, 257, 4096)] == [8, 8, 16, 128]

@@ -38,7 +38,7 @@ def causal_mode(causal) -> int:
     return int(causal)
 
 # every symbol include/attn.h declares
-EXPORTS = ("attn_bwd", "attn_fwd", "attn_status_str", "attn_version")
+EXPORTS = ("attn_bwd", "attn_fwd", "attn_fwd_masked", "attn_mask_pack", "attn_status_str", "attn_version")
 
 _lib = None
 
@@ -57,6 +57,12 @@ def load_library() -> ctypes.CDLL:
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
     ]
+    lib.attn_fwd_masked.restype = ctypes.c_int
+    lib.attn_fwd_masked.argtypes = lib.attn_fwd.argtypes[:14] + [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_longlong,
+                                                                 ctypes.c_int, ctypes.c_void_p]
+    lib.attn_mask_pack.restype = ctypes.c_int
+    lib.attn_mask_pack.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p]
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int] + \
         [ctypes.c_void_p] * 3
@@ -90,12 +96,48 @@ def attn_fwd_raw(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N_q: 
                                        causal_mode(causal), seqlens_k or None, q_start or None, stream or None))
 
 
+def mask_row_words(N_k: int) -> int:
+    """Words per row of a packed mask: ceil(N_k / 32) rounded up to a multiple of 8."""
+    return max(8, ((N_k + 255) // 256) * 8)
+
+
+def pack_mask(mask, stream=None):
+    """Pack a boolean (or uint8) GPU mask ``[Bm, Hm, N_q, N_k]`` (True = may attend)
+    into the bit layout of ``attn_fwd_masked`` with ``attn_mask_pack``.
+
+    Returns ``(bits, mask_stride_b, mask_stride_h, row_words)``; a size-1
+    batch or head dimension becomes a zero stride (broadcast).
+    """
+    import torch
+
+    lib = load_library()
+    if not isinstance(mask, torch.Tensor) or not mask.is_cuda or mask.dim() != 4 or \
+            mask.dtype not in (torch.bool, torch.uint8):
+        raise ValueError("mask must be a bool or uint8 GPU tensor [B or 1, H or 1, N_q, N_k]")
+    m = mask.contiguous()
+    if m.dtype == torch.bool:
+        m = m.view(torch.uint8)
+    Bm, Hm, N_q, N_k = m.shape
+    rw = mask_row_words(N_k)
+    bits = torch.empty((Bm, Hm, N_q, rw), dtype=torch.int32, device=m.device)
+    st = stream if stream is not None else torch.cuda.current_stream(m.device)
+    status = lib.attn_mask_pack(m.data_ptr() or None, bits.data_ptr() or None, Bm * Hm * N_q, N_k, rw,
+                                ctypes.c_void_p(st.cuda_stream))
+    if status != ATTN_OK:
+        raise AttnError(status, "attn_mask_pack")
+    return bits, (0 if Bm == 1 else Hm * N_q * rw), (0 if Hm == 1 else N_q * rw), rw
+
+
 def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None, seqlens_k=None, q_start=None,
-             return_lse: bool = True, out=None, lse=None, stream=None) -> Tuple[object, Optional[object]]:
+             return_lse: bool = True, out=None, lse=None, stream=None, attn_mask=None,
+             packed_mask=None) -> Tuple[object, Optional[object]]:
     """Fused attention forward on bf16 ``[B, H, N, d]`` CUDA (HIP) tensors.
 
     ``causal``: False (none), True or "top_left" (key j visible to row i iff
-    j <= i), "bottom_right" (iff j <= i + N_k - N_q).
+    j <= i), "bottom_right" (iff j <= i + N_k - N_q). ``attn_mask``: optional
+    bool GPU tensor ``[B or 1, H or 1, N_q, N_k]``, True = may attend,
+    intersected with the other rules (packed by the library on each call;
+    pass ``packed_mask=pack_mask(m)`` to pack once).
     Returns ``(o, lse)``; ``lse`` is None unless ``return_lse``. ``scale``
     defaults to ``d ** -0.5``. ``seqlens_k`` / ``q_start`` are optional int32
     device tensors of shape ``[B]``. The kernel is launched on ``stream`` (a
@@ -127,12 +169,20 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None, se
     if lse is not None and (lse.shape != (B, H, N_q) or lse.dtype != torch.float32 or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous float32 [B, H, N_q] tensor")
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
-    status = lib.attn_fwd(q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None,
-                          out.data_ptr() or None, (lse.data_ptr() or None) if lse is not None else None,
-                          B, H, N_q, N_k, d, ctypes.c_float(scale), causal_mode(causal),
-                          seqlens_k.data_ptr() if seqlens_k is not None else None,
-                          q_start.data_ptr() if q_start is not None else None,
-                          ctypes.c_void_p(st.cuda_stream))
+    if attn_mask is not None and packed_mask is None:
+        if attn_mask.dim() != 4 or attn_mask.shape[2:] != (N_q, N_k) or attn_mask.shape[0] not in (1, B) or \
+                attn_mask.shape[1] not in (1, H):
+            raise ValueError(f"attn_mask must be [1 or {B}, 1 or {H}, {N_q}, {N_k}]")
+        packed_mask = pack_mask(attn_mask, stream=st)
+    args = [q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, out.data_ptr() or None,
+            (lse.data_ptr() or None) if lse is not None else None, B, H, N_q, N_k, d, ctypes.c_float(scale),
+            causal_mode(causal), seqlens_k.data_ptr() if seqlens_k is not None else None,
+            q_start.data_ptr() if q_start is not None else None]
+    if packed_mask is not None:
+        bits, sb, sh, rw = packed_mask
+        status = lib.attn_fwd_masked(*args, bits.data_ptr() or None, sb, sh, rw, ctypes.c_void_p(st.cuda_stream))
+    else:
+        status = lib.attn_fwd(*args, ctypes.c_void_p(st.cuda_stream))
     if status != ATTN_OK:
         raise AttnError(status)
     return out, (lse if return_lse else None)
@@ -198,3 +248,14 @@ def attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[flo
     if status != ATTN_OK:
         raise AttnError(status, "attn_bwd")
     return dq, dk, dv
+
+
+def attn_fwd_masked_raw(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N_q: int, N_k: int, d: int,
+                        scale: float, causal, seqlens_k: int, q_start: int, mask_bits: int, mask_stride_b: int,
+                        mask_stride_h: int, mask_row_words: int, stream: int) -> int:
+    """The C entry point ``attn_fwd_masked`` with plain integers for pointers; returns the status code."""
+    return int(load_library().attn_fwd_masked(q or None, k or None, v or None, o or None, lse or None, int(B), int(H),
+                                              int(N_q), int(N_k), int(d), ctypes.c_float(scale), causal_mode(causal),
+                                              seqlens_k or None, q_start or None, mask_bits or None,
+                                              int(mask_stride_b), int(mask_stride_h), int(mask_row_words),
+                                              stream or None))

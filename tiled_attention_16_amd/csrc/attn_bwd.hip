@@ -39,6 +39,7 @@
 #include <type_traits>
 
 #include "attn.h"
+#include "launch.h"
 
 namespace {
 
@@ -640,25 +641,18 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     const long long per = 256 / (d / 8);
     const long long nb = (rows + per - 1) / per;
     if (nb > 0x7fffffffLL) return ATTN_ERR_SHAPE;
-    void* a0[] = {(void*)&op, (void*)&gp, (void*)&lse, (void*)&stp, (void*)&rows};
-    const void* f0 = d == 128 ? (const void*)attn_bwd_delta_kernel<128> : (const void*)attn_bwd_delta_kernel<64>;
-    e = hipLaunchKernel(f0, dim3((unsigned)nb), dim3(256), a0, 0, stream);
+    e = attn_launch::launch(d == 128 ? attn_bwd_delta_kernel<128> : attn_bwd_delta_kernel<64>, dim3((unsigned)nb),
+                            dim3(256), stream, op, gp, lse, stp, rows);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
-    int nqt = (int)n_qt;
-    void* a1[] = {(void*)&qp, (void*)&kp, (void*)&vp, (void*)&gp, (void*)&stp, (void*)&dqp, (void*)&Hi,
-                  (void*)&Nq, (void*)&Nk, (void*)&cc, (void*)&sc, (void*)&causal01, (void*)&coff,
-                  (void*)&seqlens_k, (void*)&q_start, (void*)&nqt};
-    const void* f1 = d == 128 ? (const void*)attn_bwd_dq_kernel<128> : (const void*)attn_bwd_dq_kernel<64>;
-    e = hipLaunchKernel(f1, dim3((unsigned)(bh * n_qt)), dim3(kThreads), a1, 0, stream);
+    e = attn_launch::launch(d == 128 ? attn_bwd_dq_kernel<128> : attn_bwd_dq_kernel<64>, dim3((unsigned)(bh * n_qt)),
+                            dim3(kThreads), stream, qp, kp, vp, gp, (const f32x2*)stp, dqp, Hi, Nq, Nk, cc, sc,
+                            causal01, coff, seqlens_k, q_start, (int)n_qt);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
   }
   if (has_k) {
-    int nkt = (int)n_kt;
-    void* a2[] = {(void*)&qp, (void*)&kp, (void*)&vp, (void*)&gp, (void*)&stp, (void*)&dkp, (void*)&dvp,
-                  (void*)&Hi, (void*)&Nq, (void*)&Nk, (void*)&cc, (void*)&sc, (void*)&causal01, (void*)&coff,
-                  (void*)&seqlens_k, (void*)&q_start, (void*)&nkt};
-    const void* f2 = d == 128 ? (const void*)attn_bwd_dkdv_kernel<128> : (const void*)attn_bwd_dkdv_kernel<64>;
-    e = hipLaunchKernel(f2, dim3((unsigned)(bh * n_kt)), dim3(kThreads), a2, 0, stream);
+    e = attn_launch::launch(d == 128 ? attn_bwd_dkdv_kernel<128> : attn_bwd_dkdv_kernel<64>,
+                            dim3((unsigned)(bh * n_kt)), dim3(kThreads), stream, qp, kp, vp, gp, (const f32x2*)stp,
+                            dkp, dvp, Hi, Nq, Nk, cc, sc, causal01, coff, seqlens_k, q_start, (int)n_kt);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
   }
   return ATTN_OK;

@@ -42,9 +42,11 @@
 //         by exp2(m_old - m_new) and the slice's exponentials redone. The sum
 //         bounds every term, so the exponentials stay below 2^8 without
 //         taking a row max per slice. O / l does not depend on the subtrahend,
-//         so this is the pages' recurrence in exact arithmetic. Key 0 is
-//         allowed for every row that has any allowed key, so a row whose m is
-//         still -inf after the first slice has no allowed key at all.
+//         so this is the pages' recurrence in exact arithmetic. A row whose m
+//         is still -inf (no allowed key in the slices seen so far: under the
+//         rule masks that means none at all, under a dense mask its first keys
+//         may be masked) uses the subtrahend 0 until a rescale sets m, and its
+//         LSE counts that 0.
 //   P     = exp2(S*c - m) in fp32, summed into l in fp32, then rounded to bf16.
 //         Its accumulator layout is already the B operand layout of the next
 //         MFMA, so P never leaves registers.
@@ -71,6 +73,7 @@
 #include <type_traits>
 
 #include "attn.h"
+#include "launch.h"
 
 namespace {
 
@@ -189,14 +192,20 @@ __device__ __forceinline__ void wait_copies() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
-template <int D>
+// Dense: a bit-packed boolean mask is intersected with the rule masks. Bit
+// j % 32 of word j / 32 of row i (rows of mrw words, mrw a multiple of 8;
+// matrix (b, h) at word b*msb + h*msh) set means row i may attend to key j.
+// Each wave copies its rows' words for the next 8 slices into LDS with one
+// buffer_load ... lds per 8 steps; every slice is masked.
+template <int D, bool Dense>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int H, int N_q, int N_k, float c, int neg_scale,
     int causal, int coff, const int32_t* __restrict__ seqlens_k, const int32_t* __restrict__ q_start, int n_qt,
-    int n_wg) {
+    int n_wg, const uint32_t* __restrict__ mbits, long long msb, long long msh, int mrw) {
   using T = Slice<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[T::kLds];
+  constexpr int kMaskLds = Dense ? 2 * kWaves * 1024 : 0;   // two 8-slice blocks of mask words per wave
+  __shared__ __attribute__((aligned(1024))) char smem[T::kLds + kMaskLds];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -417,11 +426,50 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // iff (unsigned)(h+1 - mask_from) < mask_span
   const int mask_span = max(nh, mask_from) - mask_from;
   auto mask = [&](int h, f32x16 (&s)[kRB]) __attribute__((always_inline)) {
+    if constexpr (Dense) {
+      // the row's word for slice h, ANDed with the rules' prefix of allowed
+      // keys, shifted so that bit e is the lane's key offset e (+ 4*hf)
+      const uint32_t* wb = (const uint32_t*)(smem + T::kLds) + ((h >> 3) & 1) * (kWaves * 256) + wave * 256;
+      uint32_t w = wb[(lane & 31) * 8 + (h & 7)];
+      const int lim = klim[0] - h * kSlice;   // rule-allowed key offsets within the slice: 0 .. lim
+      const uint32_t pre = lim >= 31 ? 0xffffffffu : (lim < 0 ? 0u : ((2u << lim) - 1u));
+      w = (w & pre) >> (4 * hf);
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-      const int lim = klim[rb] - h * kSlice - 4 * hf;   // key offset within the slice must be <= lim
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t t = (uint32_t)__builtin_amdgcn_sbfe((int)w, 8 * (r >> 2) + (r & 3), 1);   // 0 or ~0
+        s[0][r] = __uint_as_float((t & __float_as_uint(s[0][r])) | (~t & 0xff800000u));
+      }
+    } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[rb][r] = (8 * (r >> 2) + (r & 3)) <= lim ? s[rb][r] : -INFINITY;
+      for (int rb = 0; rb < kRB; ++rb) {
+        const int lim = klim[rb] - h * kSlice - 4 * hf;   // key offset within the slice must be <= lim
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[rb][r] = (8 * (r >> 2) + (r & 3)) <= lim ? s[rb][r] : -INFINITY;
+      }
+    }
+  };
+  // Dense: copy this wave's rows' mask words of slices 8*blk .. 8*blk+7 into
+  // LDS buffer blk % 2 (lane L brings 16 bytes of row L/2).
+  [[maybe_unused]] int m_off = 0;
+  [[maybe_unused]] i32x4 m_rsrc = {0, 0, 0, 0};
+  if constexpr (Dense) {
+    m_off = (row_lo + (lane >> 1)) * mrw * 4 + (lane & 1) * 16;
+    const uint32_t* mb = mbits + (size_t)b * msb + (size_t)(bh - b * H) * msh;
+    const uint64_t a = sgpr64((const char*)mb);
+    m_rsrc[0] = (int)(uint32_t)a;
+    m_rsrc[1] = (int)(uint32_t)(a >> 32);
+    m_rsrc[2] = __builtin_amdgcn_readfirstlane(N_q * mrw * 4);
+    m_rsrc[3] = 0x00020000;
+    asm volatile("" : "+s"(m_rsrc));
+  }
+  auto copy_mask = [&](int blk) __attribute__((always_inline)) {
+    if constexpr (Dense) {
+      const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(smem + T::kLds) +
+                           (uint32_t)(((blk & 1) * kWaves + wave) * 1024);
+      const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)blk * 32u);
+      uint32_t voff;
+      asm volatile("s_mov_b32 m0, %1\n\tv_add_u32 %0, %2, %3\n\tbuffer_load_dwordx4 %0, %4, 0 offen lds"
+                   : "=&v"(voff) : "s"(lds), "s"(soff), "v"(m_off), "s"(m_rsrc) : "memory", "m0");
     }
   };
 
@@ -525,8 +573,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // m) add up to more than kSumCap: raise m to the slice's row max where that
   // max is above m, rescale l and O by exp2(m_old - m_new), and redo the
   // slice's exponentials. Rows whose max is not above m keep everything
-  // (their shift d is 0). A row with no allowed key so far has m = -inf and
-  // only -inf scores, so its d is 0 as well.
+  // (their shift d is 0). A row that has met no allowed key before this
+  // slice still has m = -inf and the subtrahend 0; its new m is 0 + d.
   auto raise_max = [&](f32x16 (&s)[kRB], int par) __attribute__((always_inline)) {
     mfma_result_wait();   // o_acc is rescaled below
 #pragma unroll
@@ -538,8 +586,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       mx = lane_swap_max(mx);                  // row max of S*c - m over the slice
       const float d = mx > 0.f ? mx : 0.f;     // 0 for -inf and NaN too
       const float a = __builtin_amdgcn_exp2f(-d);
-      m_run[rb] += d;
-      negm[rb] = (m_run[rb] == -INFINITY) ? 0.f : -m_run[rb];
+      // the subtrahend in use is 0 while m is still -inf (a row that has met
+      // no allowed key yet); from now on it is that plus d
+      m_run[rb] = (m_run[rb] == -INFINITY ? 0.f : m_run[rb]) + d;
+      negm[rb] = -m_run[rb];
       l_run[rb] *= a;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o_acc[rb][db] *= a;
@@ -634,10 +684,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     // where the waves arrive at different times, so the workgroup's copies
     // reach the address unit spread out rather than all at once.
     copy_slice(k_rsrc, h + kStages - 1, kst((Hm + kStages - 1) % kStages));
+    // Dense: the next 8-slice block's mask words (used from step h+7 on; the
+    // copies issued in between make the waits of those steps cover it).
+    if constexpr (Dense && Hm == 0) copy_mask((h >> 3) + 1);
     // S of slice h+1 is read below. The mask reads it at once and needs the
     // wait states; for d = 128 the phase-B shifts come late enough without
     // them (the build's hazard check verifies that distance), for d = 64 not.
-    const bool msk = (unsigned)(h + 1 - mask_from) < (unsigned)mask_span;
+    const bool msk = Dense || (unsigned)(h + 1 - mask_from) < (unsigned)mask_span;
     if (D == 64 || msk) mfma_result_wait();
     if (msk) mask(h + 1, sn);
     // ---- phase B ----
@@ -672,6 +725,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   f32x16 sa[kRB], sb[kRB];
   if (nh_wg > 0) {
     if (it > 0) __syncthreads();   // every wave is done reading the previous tile's stages
+    copy_mask(0);   // Dense: the first block's mask words, ahead of the copies the wait below covers
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s) copy_slices(s);
     wait_copies<4 * kC>();
@@ -679,7 +733,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     if (nh > 0) {
       load_k(std::integral_constant<int, 0>{});
       qk(sa);
-      if (need_mask(0)) mask(0, sa);
+      if (Dense || need_mask(0)) mask(0, sa);
       first_max(sa);
 #pragma unroll
       for (int j = 0; j < 8; ++j) exp_one(sa[0], j, pbw_lo[0], lsum_lo[0]);
@@ -735,7 +789,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       }
     }
     if (LSE && lane < 32 && row < N_q)
-      LSE[(size_t)bh * N_q + row] = l_tot > 0.f ? (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+      LSE[(size_t)bh * N_q + row] =
+          l_tot > 0.f ? ((m_run[rb] == -INFINITY ? 0.f : m_run[rb]) + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   }
 #pragma unroll
   for (int i = 0; i < kRows * kChunksPerRow / 64; ++i) {
@@ -753,11 +808,26 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-}  // namespace
+// Bit-packed mask: pack rows of a byte mask (nonzero = may attend) into 32-bit
+// words, bit j % 32 of word j / 32, rows of `row_words` words (the tail of a
+// row past n_k is written as zeros). One thread per output word.
+__global__ __launch_bounds__(256) void attn_mask_pack_kernel(const uint8_t* __restrict__ m, uint32_t* __restrict__ bits,
+                                                            long long rows, int n_k, int row_words) {
+  const long long id = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (id >= rows * row_words) return;
+  const long long r = id / row_words;
+  const int w = (int)(id - r * row_words);
+  uint32_t x = 0;
+  for (int t = 0; t < 32; ++t) {
+    const int j = 32 * w + t;
+    if (j < n_k && m[r * n_k + j] != 0) x |= 1u << t;
+  }
+  bits[id] = x;
+}
 
-extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                        int N_q, int N_k, int d, float scale, int causal, const int32_t* seqlens_k,
-                        const int32_t* q_start, hipStream_t stream) {
+int fwd_launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q, int N_k,
+               int d, float scale, int causal, const int32_t* seqlens_k, const int32_t* q_start,
+               const uint32_t* mbits, long long msb, long long msh, int mrw, hipStream_t stream) {
   if (B < 0 || H < 0 || N_q < 0 || N_k < 0) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
@@ -795,11 +865,50 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   uint16_t* op = (uint16_t*)o;
   // causal mode 1: key j visible to row i iff j <= i; mode 2: iff j <= i + N_k - N_q
   int causal01 = causal ? 1 : 0, coff = causal == 2 ? N_k - N_q : 0, n_qt_i = (int)n_qt, n_wg_i = (int)n_wg;
-  void* args[] = {(void*)&qp, (void*)&kp, (void*)&vp, (void*)&op, (void*)&lse, (void*)&H, (void*)&N_q,
-                  (void*)&N_k, (void*)&c, (void*)&neg, (void*)&causal01, (void*)&coff,
-                  (void*)&seqlens_k, (void*)&q_start, (void*)&n_qt_i, (void*)&n_wg_i};
-  const void* fn = d == 128 ? (const void*)attn_fwd_kernel<128> : (const void*)attn_fwd_kernel<64>;
-  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)n_wg), dim3(kThreads), args, 0, stream);
+  const bool dense = mbits != nullptr;
+  auto kern = d == 128 ? (dense ? attn_fwd_kernel<128, true> : attn_fwd_kernel<128, false>)
+                       : (dense ? attn_fwd_kernel<64, true> : attn_fwd_kernel<64, false>);
+  const hipError_t e = attn_launch::launch(kern, dim3((unsigned)n_wg), dim3(kThreads), stream, qp, kp, vp, op, lse, H, N_q, N_k, c,
+                              neg, causal01, coff, seqlens_k, q_start, n_qt_i, n_wg_i, mbits, msb, msh, mrw);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                        int N_q, int N_k, int d, float scale, int causal, const int32_t* seqlens_k,
+                        const int32_t* q_start, hipStream_t stream) {
+  return fwd_launch(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, seqlens_k, q_start, nullptr, 0, 0, 0, stream);
+}
+
+extern "C" int attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                               int N_q, int N_k, int d, float scale, int causal, const int32_t* seqlens_k,
+                               const int32_t* q_start, const uint32_t* mask_bits, long long mask_stride_b,
+                               long long mask_stride_h, int mask_row_words, hipStream_t stream) {
+  if (B < 0 || H < 0 || N_q < 0 || N_k < 0) return ATTN_ERR_SHAPE;
+  if (!mask_bits) {
+    if ((long long)B * H * N_q == 0) return fwd_launch(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, seqlens_k,
+                                                       q_start, nullptr, 0, 0, 0, stream);
+    return ATTN_ERR_NULL;
+  }
+  if ((uintptr_t)mask_bits & 15) return ATTN_ERR_ALIGN;
+  if (mask_row_words < (N_k + 31) / 32 || mask_row_words % 8 != 0 || mask_stride_b < 0 || mask_stride_h < 0)
+    return ATTN_ERR_MASK;
+  if ((long long)N_q * mask_row_words * 4 > 0x7fffffffLL) return ATTN_ERR_SHAPE;   // 32-bit copy offsets
+  return fwd_launch(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, seqlens_k, q_start, mask_bits,
+                    mask_stride_b, mask_stride_h, mask_row_words, stream);
+}
+
+extern "C" int attn_mask_pack(const uint8_t* mask, uint32_t* bits, long long rows, int N_k, int row_words,
+                              hipStream_t stream) {
+  if (rows < 0 || N_k < 0 || row_words < (N_k + 31) / 32) return ATTN_ERR_SHAPE;
+  if (rows == 0 || row_words == 0) return ATTN_OK;
+  if (!bits || (N_k > 0 && !mask)) return ATTN_ERR_NULL;
+  if (((uintptr_t)bits & 3)) return ATTN_ERR_ALIGN;
+  const long long n = rows * row_words;
+  if ((n + 255) / 256 > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  const hipError_t e = attn_launch::launch(attn_mask_pack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), stream,
+                                           mask, bits, rows, N_k, row_words);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -813,7 +922,7 @@ extern "C" const char* attn_status_str(int status) {
     case ATTN_ERR_ALIGN: return "misaligned pointer (bf16 tensors need 16 bytes, lse and delta 4)";
     case ATTN_ERR_ALIAS: return "output overlaps an input or the other output";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
-    case ATTN_ERR_MASK: return "causal must be 0 (none), 1 (top-left) or 2 (bottom-right)";
+    case ATTN_ERR_MASK: return "causal must be 0, 1 or 2; mask rows need >= ceil(N_k/32) words, a multiple of 8";
     default: return "unknown status";
   }
 }
