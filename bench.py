@@ -130,6 +130,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(ALL_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--window", type=int, default=0, metavar="W",
+                    help="forward with a dense boolean mask (attn_fwd_masked): key j visible to row i iff "
+                         "i - W < j <= i, one mask shared by all heads, packed once before the timed region")
     ap.add_argument("--backward", action="store_true",
                     help="time attn_bwd (dQ, dK, dV; its three launches) instead of the forward; O and LSE come "
                          "from one attn_fwd call before the timed region")
@@ -171,11 +174,17 @@ def main():
     if args.backward:
         return bench_backward(args, torch, ta, w, inp, sets[0], sl, qs, stream, dev)
 
+    packed = None
+    if args.window:
+        i = torch.arange(w.N_q, device=dev)[:, None]
+        j = torch.arange(w.N_k, device=dev)[None, :]
+        packed = ta.pack_mask(((j > i - args.window) & (j <= i))[None, None], stream=stream)
+
     def step():
         sq, sk, sv, so, slse = sets[n_step[0] % len(sets)]
         n_step[0] += 1
         ta.attn_fwd(sq, sk, sv, causal=w.causal, scale=float(inp.scale), seqlens_k=sl, q_start=qs, out=so,
-                    lse=slse, stream=stream)
+                    lse=slse, stream=stream, packed_mask=packed)
 
     for _ in range(args.warmup):
         step()
@@ -227,7 +236,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.N_q, "N_k": w.N_k, "d": w.d,
-                   "causal": w.causal, "varlen": inp.seqlens_k is not None},
+                   "causal": w.causal, "varlen": inp.seqlens_k is not None,
+                   **({"dense_mask": f"sliding window {args.window}"} if args.window else {})},
         "pct_of_mfma_bf16_peak": round(100.0 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
