@@ -260,7 +260,7 @@ def bench_backward(args, torch, ta, w, inp, tensors, sl, qs, stream, dev):
     ta.attn_fwd(q, k, v, causal=w.causal, scale=float(inp.scale), seqlens_k=sl, q_start=qs, out=o, lse=lse,
                 stream=stream)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    delta = torch.empty((w.B, w.H, w.N_q), dtype=torch.float32, device=dev)
+    delta = torch.empty((w.B, w.H, w.N_q, 2), dtype=torch.float32, device=dev)
 
     def step():
         ta.attn_bwd(q, k, v, o, lse, g, causal=w.causal, scale=float(inp.scale), seqlens_k=sl, q_start=qs, dq=dq,

@@ -156,10 +156,12 @@ int attn_mask_pack(const uint8_t* mask, uint32_t* bits, long long rows, int N_k,
  *   dout        bf16 [B, H, N_q, d], the gradient of the loss with respect to o.
  *   dq          bf16 [B, H, N_q, d], written in full.
  *   dk, dv      bf16 [B, H, N_k, d], written in full.
- *   delta       float32 [B, H, N_q] workspace, overwritten (Delta above).
+ *   delta       float32 [B, H, N_q, 2] workspace, overwritten: per row
+ *               (LSE * log2 e, Delta), with +inf in place of LSE * log2 e on a
+ *               row with no allowed key.
  *   B .. q_start, stream  as in attn_fwd.
  * q, o, dout, lse, dq and delta may be NULL iff N_q == 0; k, v, dk and dv iff
- * N_k == 0. Alignment: the bf16 tensors 16 bytes, lse and delta 4 bytes.
+ * N_k == 0. Alignment: the bf16 tensors 16 bytes, lse 4 bytes, delta 8 bytes.
  * No output (dq, dk, dv, delta) may overlap an input or another output.
  * Errors as in attn_fwd: argument errors return before any HIP call; when
  * B*H == 0 or N_q == N_k == 0 the call returns ATTN_OK without launching.
@@ -168,6 +170,19 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              const float* lse, void* dq, void* dk, void* dv, float* delta,
              int B, int H, int N_q, int N_k, int d, float scale, int causal,
              const int32_t* seqlens_k, const int32_t* q_start, hipStream_t stream);
+
+/*
+ * attn_bwd_masked - attn_bwd for attn_fwd_masked: the same gradients with the
+ * bit-packed mask (same layout, strides and checks as attn_fwd_masked)
+ * intersected with the rules. o and lse must come from attn_fwd_masked with
+ * the same mask. Keys no row may attend to get dK = dV = 0.
+ */
+int attn_bwd_masked(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, float* delta,
+                    int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                    const int32_t* seqlens_k, const int32_t* q_start,
+                    const uint32_t* mask_bits, long long mask_stride_b, long long mask_stride_h,
+                    int mask_row_words, hipStream_t stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* attn_status_str(int status);

@@ -170,3 +170,14 @@ def test_mask_pack_argument_errors(lib):
 
 def test_mask_row_words():
     assert [ta.mask_row_words(n) for n in (1, 256, 257, 4096)] == [8, 8, 16, 128]
+
+
+def test_bwd_masked_argument_errors(lib):
+    base = dict(q=A16, k=A16 * 2, v=A16 * 3, o=A16 * 4, dout=A16 * 5, lse=A16 * 6, dq=A16 * 7, dk=A16 * 8,
+                dv=A16 * 9, delta=A16 * 10)
+    p = [base[n] for n in ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "delta")]
+    common = p + [1, 2, 8, 300, 64, ctypes.c_float(0.125), 0, None, None]
+    assert lib.attn_bwd_masked(*common, None, 0, 0, 16, None) == ta.ATTN_ERR_NULL
+    assert lib.attn_bwd_masked(*common, A16 * 40 + 4, 0, 0, 16, None) == ta.ATTN_ERR_ALIGN
+    assert lib.attn_bwd_masked(*common, A16 * 40, 0, 0, 8, None) == ta.ATTN_ERR_MASK
+    assert lib.attn_bwd_masked(*common, A16 * 40, -1, 0, 16, None) == ta.ATTN_ERR_MASK

@@ -173,3 +173,60 @@ def test_bwd_bottom_right_causal(case):
     g = make_dout((B, H, nq, d), seed=nq + nk)
     compare(q, k, v, g, np.float32(d ** -0.5), 2, None if sl is None else np.array(sl, np.int32),
             None if qs is None else np.array(qs, np.int32))
+
+
+def test_bwd_workspace_and_outputs_stay_in_bounds():
+    """delta is [B, H, N_q, 2] floats; the kernels write nothing outside it or the gradients."""
+    import tiled_attention_16_amd as ta
+    B, H, n, d = 2, 2, 150, 128
+    q, k, v = make_random(B, H, n, n, d, seed=61)
+    tq, tk, tv, tg = to_dev(q), to_dev(k), to_dev(v), to_dev(make_dout((B, H, n, d), seed=62))
+    o, lse = ta.attn_fwd(tq, tk, tv, causal=True)
+    guard = 4096
+    nd = B * H * n * 2
+    dbuf = torch.full((nd + 2 * guard,), float("nan"), dtype=torch.float32, device="cuda")
+    gbuf = torch.full((3 * B * H * n * d + 2 * guard,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    m = B * H * n * d
+    dq = gbuf[guard:guard + m].view(B, H, n, d)
+    dk = gbuf[guard + m:guard + 2 * m].view(B, H, n, d)
+    dv = gbuf[guard + 2 * m:guard + 3 * m].view(B, H, n, d)
+    ta.attn_bwd(tq, tk, tv, o, lse, tg, causal=True, dq=dq, dk=dk, dv=dv, delta=dbuf[guard:guard + nd].view(B, H, n, 2))
+    torch.cuda.synchronize()
+    assert torch.isnan(dbuf[:guard]).all().item() and torch.isnan(dbuf[guard + nd:]).all().item()
+    assert torch.isnan(gbuf[:guard]).all().item() and torch.isnan(gbuf[guard + 3 * m:]).all().item()
+    assert not torch.isnan(gbuf[guard:guard + 3 * m]).any().item()
+
+
+MASKED = [
+    # B, H, N_q, N_k, d, causal, mask shape (b, h), density
+    (1, 2, 200, 300, 128, 0, (1, 2), 0.5),
+    (2, 1, 300, 200, 64, 1, (2, 1), 0.7),
+    (1, 2, 130, 700, 128, 2, (1, 1), 0.1),
+]
+
+
+@pytest.mark.parametrize("case", MASKED, ids=[f"{c[2]}x{c[3]}_d{c[4]}_c{c[5]}_p{c[7]}" for c in MASKED])
+def test_bwd_dense_mask(case):
+    import tiled_attention_16_amd as ta
+    B, H, nq, nk, d, causal, (mb, mh), dens = case
+    q, k, v = make_random(B, H, nq, nk, d, seed=nq + 7 * nk + d)
+    g = make_dout((B, H, nq, d), seed=nq + 11 * nk)
+    rng = np.random.default_rng(nq + nk)
+    mask = rng.random((mb, mh, nq, nk)) < dens
+    mask[0, 0, 3] = False                      # a row that sees no key
+    mask[..., 7] = False                       # a key no row sees
+    scale = np.float32(d ** -0.5)
+    print(f"  masked bwd {case}", flush=True)
+    tq, tk, tv, tg = to_dev(q), to_dev(k), to_dev(v), to_dev(g)
+    tm = torch.from_numpy(mask).cuda()
+    o, lse = ta.attn_fwd(tq, tk, tv, causal=causal, scale=float(scale), attn_mask=tm)
+    dq, dk, dv = ta.attn_bwd(tq, tk, tv, o, lse, tg, causal=causal, scale=float(scale), attn_mask=tm)
+    torch.cuda.synchronize()
+    dq, dk, dv = f64(dq), f64(dk), f64(dv)
+    rq, rk, rv = attention_bwd(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), bf16_bits_to_f64(g),
+                               float(scale), causal, attn_mask=mask)
+    r = check_grads({"dq": dq, "dk": dk, "dv": dv}, {"dq": rq, "dk": rk, "dv": rv})
+    print("  ", r, flush=True)
+    assert r.ok, str(r)
+    assert np.all(dk[:, :, 7] == 0) and np.all(dv[:, :, 7] == 0)
+    assert np.all(dq[0, 0, 3] == 0)

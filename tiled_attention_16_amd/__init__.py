@@ -38,7 +38,8 @@ def causal_mode(causal) -> int:
     return int(causal)
 
 # every symbol include/attn.h declares
-EXPORTS = ("attn_bwd", "attn_fwd", "attn_fwd_masked", "attn_mask_pack", "attn_status_str", "attn_version")
+EXPORTS = ("attn_bwd", "attn_bwd_masked", "attn_fwd", "attn_fwd_masked", "attn_mask_pack", "attn_status_str",
+           "attn_version")
 
 _lib = None
 
@@ -66,6 +67,9 @@ def load_library() -> ctypes.CDLL:
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int] + \
         [ctypes.c_void_p] * 3
+    lib.attn_bwd_masked.restype = ctypes.c_int
+    lib.attn_bwd_masked.argtypes = lib.attn_bwd.argtypes[:19] + [ctypes.c_void_p, ctypes.c_longlong,
+                                                                 ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_version.restype = ctypes.c_int
@@ -198,14 +202,15 @@ def attn_bwd_raw(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, d
 
 
 def attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] = None, seqlens_k=None,
-             q_start=None, dq=None, dk=None, dv=None, delta=None, stream=None):
+             q_start=None, dq=None, dk=None, dv=None, delta=None, stream=None, attn_mask=None, packed_mask=None):
     """Gradients ``(dq, dk, dv)`` of ``attn_fwd`` for upstream gradient ``dout``.
 
     ``o`` and ``lse`` are ``attn_fwd``'s outputs for the same inputs, mask and
     scale. All tensors are contiguous GPU tensors: q, o, dout bf16
     ``[B, H, N_q, d]``; k, v bf16 ``[B, H, N_k, d]``; lse float32 ``[B, H, N_q]``.
-    ``delta`` (float32 ``[B, H, N_q]``) is the kernels' workspace; it is
-    allocated here when not given.
+    ``delta`` (float32 ``[B, H, N_q, 2]``) is the kernels' workspace; it is
+    allocated here when not given. ``attn_mask`` / ``packed_mask``: the mask
+    the forward used (see ``attn_fwd``).
     """
     import torch
 
@@ -236,15 +241,21 @@ def attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[flo
         if t.shape != ref.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous bf16 tensor shaped like {name[1:]}")
     if delta is None:
-        delta = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
-    elif delta.shape != (B, H, N_q) or delta.dtype != torch.float32 or not delta.is_contiguous():
-        raise ValueError("delta must be a contiguous float32 [B, H, N_q] tensor")
+        delta = torch.empty((B, H, N_q, 2), dtype=torch.float32, device=q.device)
+    elif delta.shape != (B, H, N_q, 2) or delta.dtype != torch.float32 or not delta.is_contiguous():
+        raise ValueError("delta must be a contiguous float32 [B, H, N_q, 2] tensor")
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     ptr = lambda t: t.data_ptr() or None  # noqa: E731
-    status = lib.attn_bwd(ptr(q), ptr(k), ptr(v), ptr(o), ptr(dout), ptr(lse), ptr(dq), ptr(dk), ptr(dv),
-                          ptr(delta), B, H, N_q, N_k, d, ctypes.c_float(scale), causal_mode(causal),
-                          seqlens_k.data_ptr() if seqlens_k is not None else None,
-                          q_start.data_ptr() if q_start is not None else None, ctypes.c_void_p(st.cuda_stream))
+    if attn_mask is not None and packed_mask is None:
+        packed_mask = pack_mask(attn_mask, stream=st)
+    args = [ptr(q), ptr(k), ptr(v), ptr(o), ptr(dout), ptr(lse), ptr(dq), ptr(dk), ptr(dv), ptr(delta), B, H, N_q,
+            N_k, d, ctypes.c_float(scale), causal_mode(causal), seqlens_k.data_ptr() if seqlens_k is not None else None,
+            q_start.data_ptr() if q_start is not None else None]
+    if packed_mask is not None:
+        bits, sb, sh, rw = packed_mask
+        status = lib.attn_bwd_masked(*args, bits.data_ptr() or None, sb, sh, rw, ctypes.c_void_p(st.cuda_stream))
+    else:
+        status = lib.attn_bwd(*args, ctypes.c_void_p(st.cuda_stream))
     if status != ATTN_OK:
         raise AttnError(status, "attn_bwd")
     return dq, dk, dv

@@ -157,6 +157,22 @@ __device__ __forceinline__ void copy_kb(const i32x4& rs, uint32_t soff, uint32_t
 // also drain the ring) inside the loop.
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// One 4-byte-per-lane global -> LDS copy (256 bytes at LDS byte lds + 4*lane).
+__device__ __forceinline__ void copy_dw(const i32x4& rs, uint32_t soff, uint32_t off, uint32_t lds) {
+  uint32_t v;
+  asm volatile("s_mov_b32 m0, %1\n\tv_add_u32 %0, %2, %3\n\tbuffer_load_dword %0, %4, 0 offen lds"
+               : "=&v"(v) : "s"(lds), "s"(soff), "v"(off), "s"(rs) : "memory", "m0");
+}
+
+// Bit-packed dense mask (the layout of attn_fwd_masked): bit t of word w of
+// row i set means row i may attend to key 32*w + t; rows of mrw words,
+// matrix (b, h) at word b*msb + h*msh.
+struct DenseMask {
+  const uint32_t* bits;
+  long long sb, sh;
+  int rw;
+};
+
 template <int N>
 __device__ __forceinline__ void wait_copies() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -203,14 +219,18 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const uint16_t* __r
 }
 
 // ---------------------------------------------------------------- dq
-template <int D>
+// Dense: a bit-packed mask is intersected with the rules; each wave copies
+// its 32 rows' words of the block with the block (one more copy per block).
+template <int D, bool Dense>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const f32x2* __restrict__ stats, uint16_t* __restrict__ dQ, int H, int N_q,
     int N_k, float c, float scale, int causal, int coff, const int32_t* __restrict__ seqlens_k,
-    const int32_t* __restrict__ q_start, int n_qt) {
+    const int32_t* __restrict__ q_start, int n_qt, DenseMask dm) {
   using R = Ring<D>;
-  constexpr int kStage = 2 * R::kBlkBytes;   // [K block][V block]
+  constexpr int kMaskBytes = Dense ? kWaves * 256 : 0;
+  constexpr int kStage = 2 * R::kBlkBytes + kMaskBytes;   // [K block][V block][mask words of each wave]
+  constexpr int kCpb = R::kCpw + (Dense ? 1 : 0);         // copies per wave per block
   __shared__ __attribute__((aligned(1024))) char smem[kDepth * kStage];
   const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
@@ -275,6 +295,13 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
   int cpoff[R::kCpw];
 #pragma unroll
   for (int i = 0; i < R::kCpw; ++i) cpoff[i] = copy_lane_off<D>(wave * R::kCpw + i, lane);
+  // Dense: lane L < 32 brings the word of row wrow0 + L for the block
+  [[maybe_unused]] i32x4 m_rs = {0, 0, 0, 0};
+  [[maybe_unused]] uint32_t m_off = 0;
+  if constexpr (Dense) {
+    m_rs = rsrc(dm.bits + (size_t)b * dm.sb + (size_t)(bh - b * H) * dm.sh, (uint32_t)N_q * dm.rw * 4);
+    m_off = lane < 32 ? (uint32_t)(wrow0 + lane) * dm.rw * 4 : 0x40000000u;
+  }
   auto issue = [&](int n) {   // block n into stage n % kDepth
     const uint32_t st = lds0 + (uint32_t)(n % kDepth) * kStage;
     const uint32_t soff = (uint32_t)n * R::kBlkBytes;
@@ -284,6 +311,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
       const bool is_v = ci >= R::kKB;
       copy_kb(is_v ? v_rs : k_rs, soff, cpoff[i], st + (uint32_t)ci * 1024);
     }
+    if constexpr (Dense) copy_dw(m_rs, (uint32_t)n * 4, m_off, st + 2 * R::kBlkBytes + wave * 256);
   };
 
   const Offs<D> off(lane);
@@ -293,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
 #pragma unroll
   for (int n = 0; n < kDepth - 1; ++n) issue(n);
   for (int n = 0; n < nblk; ++n) {
-    wait_copies<(kDepth - 2) * R::kCpw>();   // block n has landed (this wave's copies)
+    wait_copies<(kDepth - 2) * kCpb>();   // block n has landed (this wave's copies)
     __syncthreads();                          // everyone's copies; block n-1's stage is free
     issue(n + kDepth - 1);
     const char* kb = smem + (n % kDepth) * kStage;
@@ -315,11 +343,26 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
     }
     // P and dS; register r holds key n*32 + 8*(r/4) + 4*hf + r%4
     uint32_t w[8];
-    if (n < full_below) {   // every key of the block is allowed for every row of the wave
+    if (!Dense && n < full_below) {   // every key of the block is allowed for every row of the wave
 #pragma unroll
       for (int r = 0; r < 16; r += 2)
         w[r >> 1] = pack2(__builtin_amdgcn_exp2f(s[r] * c - lse2) * (dp[r] - dl),
                           __builtin_amdgcn_exp2f(s[r + 1] * c - lse2) * (dp[r + 1] - dl));
+    } else if constexpr (Dense) {
+      // the row's word for the block, ANDed with the rules' prefix of allowed
+      // keys and shifted so that bit e is the lane's key offset e (+ 4*hf)
+      uint32_t mw = *(const __attribute__((address_space(3))) uint32_t*)(kb + 2 * R::kBlkBytes + wave * 256 +
+                                                                          4 * (lane & 31));
+      const int lim0 = klim - n * kBlk;
+      const uint32_t pre = lim0 >= 31 ? 0xffffffffu : (lim0 < 0 ? 0u : ((2u << lim0) - 1u));
+      mw = (mw & pre) >> (4 * hf);
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const int j0 = 8 * (r >> 2) + (r & 3);
+        const float d0 = (mw >> j0) & 1u ? __builtin_amdgcn_exp2f(s[r] * c - lse2) * (dp[r] - dl) : 0.f;
+        const float d1 = (mw >> (j0 + 1)) & 1u ? __builtin_amdgcn_exp2f(s[r + 1] * c - lse2) * (dp[r + 1] - dl) : 0.f;
+        w[r >> 1] = pack2(d0, d1);
+      }
     } else {
       const int lim = klim - n * kBlk - 4 * hf;
 #pragma unroll
@@ -357,14 +400,19 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------- dk, dv
-template <int D>
+// Dense: as in the dQ kernel; each wave copies, per block, the words of the
+// block's 32 rows that hold its own 32 keys.
+template <int D, bool Dense>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const f32x2* __restrict__ stats, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int H, int N_q, int N_k, float c, float scale, int causal, int coff,
-    const int32_t* __restrict__ seqlens_k, const int32_t* __restrict__ q_start, int n_kt) {
+    const int32_t* __restrict__ seqlens_k, const int32_t* __restrict__ q_start, int n_kt, DenseMask dm) {
   using R = Ring<D>;
-  constexpr int kStage = 2 * R::kBlkBytes + 1024;   // [Q block][dO block][stats of the 32 rows]
+  constexpr int kMaskBytes = Dense ? kWaves * 256 : 0;
+  // [Q block][dO block][stats of the 32 rows][mask words of each wave]
+  constexpr int kStage = 2 * R::kBlkBytes + 1024 + kMaskBytes;
+  constexpr int kCpb = R::kCpw + (Dense ? 1 : 0);   // copies per wave per block (wave 0: one more)
   __shared__ __attribute__((aligned(1024))) char smem[(kDepth + 1) * kStage];
   const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
@@ -420,6 +468,13 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
   // S and dP are already computed, so two stages are being read and up to
   // three more blocks are in flight.
   constexpr int kDepthKV = kDepth + 1;
+  // Dense: lane L < 32 brings, for row r0 + L, the word that holds this wave's keys
+  [[maybe_unused]] i32x4 m_rs = {0, 0, 0, 0};
+  [[maybe_unused]] uint32_t m_off = 0;
+  if constexpr (Dense) {
+    m_rs = rsrc(dm.bits + (size_t)b * dm.sb + (size_t)(bh - b * H) * dm.sh, (uint32_t)N_q * dm.rw * 4);
+    m_off = lane < 32 ? (uint32_t)lane * dm.rw * 4 + (uint32_t)(wkey0 >> 5) * 4 : 0x40000000u;
+  }
   auto issue = [&](int n) {   // block n (rows (blk0 + n)*32 ..) into stage n % kDepthKV
     const uint32_t st = lds0 + (uint32_t)(n % kDepthKV) * kStage;
     const uint32_t r0 = (uint32_t)(blk0 + n) * kBlk;
@@ -430,13 +485,14 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
       copy_kb(is_g ? g_rs : q_rs, r0 * 2 * D, cpoff[i], st + (uint32_t)ci * 1024);
     }
     if (wave == 0) copy_kb(s_rs, r0 * 8, soff_lane, st + 2 * R::kBlkBytes);
+    if constexpr (Dense) copy_dw(m_rs, r0 * dm.rw * 4, m_off, st + 2 * R::kBlkBytes + 1024 + wave * 256);
   };
   // Block n has landed once at most the `ahead` newest blocks' copies of this
   // wave are in flight (wave 0 issues one copy more per block).
   auto wait_block = [&](auto ahead) {
     constexpr int A = decltype(ahead)::value;
-    if (wave == 0) wait_copies<A * (R::kCpw + 1)>();
-    else wait_copies<A * R::kCpw>();
+    if (wave == 0) wait_copies<A * (kCpb + 1)>();
+    else wait_copies<A * kCpb>();
   };
   auto stage_of = [&](int n) { return (const char*)smem + (n % kDepthKV) * kStage; };
 
@@ -476,6 +532,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
     constexpr bool full = decltype(full_t)::value;
     const int r0 = (blk0 + n) * kBlk;
     const char* sb = stage_of(n) + 2 * R::kBlkBytes;
+    [[maybe_unused]] const char* mb = sb + 1024 + wave * 256;   // Dense: word of row r0 + t at 4*t
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       // stats of rows 8g + 4hf .. +3: (lse2, D) pairs, 32 bytes
@@ -495,7 +552,10 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
           const int qrow = r0 + 8 * g + 4 * hf + e;
-          const bool ok = key_live && qrow < N_q && qrow >= qs && (!causal || key <= qrow + coff);
+          bool ok = key_live && qrow < N_q && qrow >= qs && (!causal || key <= qrow + coff);
+          if constexpr (Dense)
+            ok = ok && ((*(const __attribute__((address_space(3))) uint32_t*)(mb + 4 * (8 * g + 4 * hf + e)) >>
+                         (lane & 31)) & 1u);
           p[e] = ok ? __builtin_amdgcn_exp2f(s[r] * c - l2[e]) : 0.f;
           ds[e] = ok ? p[e] * (dp[r] - dd[e]) : 0.f;
         }
@@ -556,7 +616,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
     // fetched nothing: finite values, discarded)
     f32x16 s_nxt, dp_nxt;
     uint32_t wp[8], wd[8];
-    if (block_full(n)) {
+    if (!Dense && block_full(n)) {
       sdp(stage_of(n + 1), s_nxt, dp_nxt);
       softmax_grad(std::true_type{}, n, s_cur, dp_cur, wp, wd);
       interleave(std::integral_constant<int, 6>{});
@@ -592,12 +652,9 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-}  // namespace
-
-extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                        const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N_q,
-                        int N_k, int d, float scale, int causal, const int32_t* seqlens_k,
-                        const int32_t* q_start, hipStream_t stream) {
+int bwd_launch(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+               void* dq, void* dk, void* dv, float* delta, int B, int H, int N_q, int N_k, int d, float scale,
+               int causal, const int32_t* seqlens_k, const int32_t* q_start, DenseMask dm, hipStream_t stream) {
   if (B < 0 || H < 0 || N_q < 0 || N_k < 0) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
@@ -644,16 +701,46 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     e = attn_launch::launch(d == 128 ? attn_bwd_delta_kernel<128> : attn_bwd_delta_kernel<64>, dim3((unsigned)nb),
                             dim3(256), stream, op, gp, lse, stp, rows);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
-    e = attn_launch::launch(d == 128 ? attn_bwd_dq_kernel<128> : attn_bwd_dq_kernel<64>, dim3((unsigned)(bh * n_qt)),
-                            dim3(kThreads), stream, qp, kp, vp, gp, (const f32x2*)stp, dqp, Hi, Nq, Nk, cc, sc,
-                            causal01, coff, seqlens_k, q_start, (int)n_qt);
+    const bool dense = dm.bits != nullptr;
+    auto kq = d == 128 ? (dense ? attn_bwd_dq_kernel<128, true> : attn_bwd_dq_kernel<128, false>)
+                       : (dense ? attn_bwd_dq_kernel<64, true> : attn_bwd_dq_kernel<64, false>);
+    e = attn_launch::launch(kq, dim3((unsigned)(bh * n_qt)), dim3(kThreads), stream, qp, kp, vp, gp, (const f32x2*)stp,
+                            dqp, Hi, Nq, Nk, cc, sc, causal01, coff, seqlens_k, q_start, (int)n_qt, dm);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
   }
   if (has_k) {
-    e = attn_launch::launch(d == 128 ? attn_bwd_dkdv_kernel<128> : attn_bwd_dkdv_kernel<64>,
-                            dim3((unsigned)(bh * n_kt)), dim3(kThreads), stream, qp, kp, vp, gp, (const f32x2*)stp,
-                            dkp, dvp, Hi, Nq, Nk, cc, sc, causal01, coff, seqlens_k, q_start, (int)n_kt);
+    const bool dense = dm.bits != nullptr;
+    auto kk = d == 128 ? (dense ? attn_bwd_dkdv_kernel<128, true> : attn_bwd_dkdv_kernel<128, false>)
+                       : (dense ? attn_bwd_dkdv_kernel<64, true> : attn_bwd_dkdv_kernel<64, false>);
+    e = attn_launch::launch(kk, dim3((unsigned)(bh * n_kt)), dim3(kThreads), stream, qp, kp, vp, gp, (const f32x2*)stp,
+                            dkp, dvp, Hi, Nq, Nk, cc, sc, causal01, coff, seqlens_k, q_start, (int)n_kt, dm);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
   }
   return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N_q,
+                        int N_k, int d, float scale, int causal, const int32_t* seqlens_k,
+                        const int32_t* q_start, hipStream_t stream) {
+  return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N_q, N_k, d, scale, causal, seqlens_k, q_start,
+                    DenseMask{nullptr, 0, 0, 0}, stream);
+}
+
+extern "C" int attn_bwd_masked(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                               const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H,
+                               int N_q, int N_k, int d, float scale, int causal, const int32_t* seqlens_k,
+                               const int32_t* q_start, const uint32_t* mask_bits, long long mask_stride_b,
+                               long long mask_stride_h, int mask_row_words, hipStream_t stream) {
+  if (B < 0 || H < 0 || N_q < 0 || N_k < 0) return ATTN_ERR_SHAPE;
+  const bool work = (long long)B * H > 0 && (N_q > 0 || N_k > 0);
+  if (!mask_bits) return work ? ATTN_ERR_NULL : ATTN_OK;
+  if ((uintptr_t)mask_bits & 15) return ATTN_ERR_ALIGN;
+  if (mask_row_words < (N_k + 31) / 32 || mask_row_words % 8 != 0 || mask_stride_b < 0 || mask_stride_h < 0)
+    return ATTN_ERR_MASK;
+  if ((long long)(N_q + kTile) * mask_row_words * 4 > 0x7fffffffLL) return ATTN_ERR_SHAPE;   // 32-bit offsets
+  return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N_q, N_k, d, scale, causal, seqlens_k, q_start,
+                    DenseMask{mask_bits, mask_stride_b, mask_stride_h, mask_row_words}, stream);
 }
