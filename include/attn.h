@@ -123,6 +123,31 @@ int attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float*
                     int mask_row_words, hipStream_t stream);
 
 /*
+ * attn_fwd_block_sparse - attn_fwd computing only the blocks a block mask
+ * keeps (block-sparse attention, [MEMWALL] §7): blocks the mask drops are
+ * neither loaded nor computed, and their keys get probability 0.
+ *
+ *   block_mask       uint8 device array, read only: for batch b, head h, query
+ *                    tile t (rows 256*t .. 256*t+255) and key slice s (keys
+ *                    32*s .. 32*s+31) the byte block_mask[b*block_stride_b +
+ *                    h*block_stride_h + t*ceil(N_k/32) + s]; nonzero = compute
+ *                    the block. Rows of ceil(N_k/32) bytes, ceil(N_q/256) rows
+ *                    per (b, h).
+ *   block_stride_b,  byte strides between batches and heads (>= 0; 0 broadcasts).
+ *   block_stride_h
+ * The rules (causal, seqlens_k, q_start) still apply inside kept blocks. A
+ * row with no kept, allowed key outputs O = 0, LSE = -inf. N_k is limited to
+ * 32768 (1024 slices) on this path (else ATTN_ERR_SHAPE). Other arguments,
+ * outputs and errors as in attn_fwd; a NULL block_mask with work to do is
+ * ATTN_ERR_NULL, negative strides ATTN_ERR_MASK.
+ */
+int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                          const int32_t* seqlens_k, const int32_t* q_start,
+                          const uint8_t* block_mask, long long block_stride_b, long long block_stride_h,
+                          hipStream_t stream);
+
+/*
  * attn_mask_pack - pack a byte mask into the bit layout attn_fwd_masked reads.
  *   mask       uint8 device array [rows, N_k], row major; nonzero = may attend.
  *   bits       uint32 device array [rows, row_words], written in full (bits of

@@ -18,6 +18,7 @@ Parity status of each function (what pins it, all in ``tests/test_oracle.py``):
                     Q = 0 closed form of dV, torch CPU fp64 autograd cross-check.
   check_grads       pinned by planted mistakes (NaN, out of band).
 """
-from .attention import allowed_mask, attention, attention_online, bf16_bits_to_f64, causal_offset  # noqa: F401
+from .attention import (allowed_mask, attention, attention_online, bf16_bits_to_f64, causal_offset,  # noqa: F401
+                        expand_block_mask)
 from .backward import attention_bwd  # noqa: F401
 from .checker import check, check_grads, CheckResult, GradCheckResult  # noqa: F401

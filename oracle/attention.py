@@ -101,6 +101,17 @@ def dense_allowed(attn_mask: Optional[np.ndarray], b: int, h: int, rows: np.ndar
     return m[b if m.shape[0] > 1 else 0, h if m.shape[1] > 1 else 0][rows]
 
 
+def expand_block_mask(block_mask: np.ndarray, n_q: int, n_k: int, block_q: int, block_k: int) -> np.ndarray:
+    """Boolean [.., n_q, n_k] mask from a block mask [.., ceil(n_q/block_q), ceil(n_k/block_k)]:
+    entry (i, j) is the flag of block (i // block_q, j // block_k).
+
+    Block-sparse attention ([MEMWALL] §7) computes only the blocks whose flag is
+    set; in exact arithmetic that is attention under this expanded mask.
+    """
+    bm = np.asarray(block_mask, dtype=bool)
+    return bm[..., np.arange(n_q) // block_q, :][..., np.arange(n_k) // block_k]
+
+
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool = False,
               seqlens_k: Optional[np.ndarray] = None, q_start: Optional[np.ndarray] = None,
               rows: Optional[Sequence[int]] = None, return_probs: bool = False, row_block: int = 1024,

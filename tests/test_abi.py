@@ -181,3 +181,13 @@ def test_bwd_masked_argument_errors(lib):
     assert lib.attn_bwd_masked(*common, A16 * 40 + 4, 0, 0, 16, None) == ta.ATTN_ERR_ALIGN
     assert lib.attn_bwd_masked(*common, A16 * 40, 0, 0, 8, None) == ta.ATTN_ERR_MASK
     assert lib.attn_bwd_masked(*common, A16 * 40, -1, 0, 16, None) == ta.ATTN_ERR_MASK
+
+
+def test_block_sparse_argument_errors(lib):
+    p = [A16, A16 * 2, A16 * 3, A16 * 4, A16 * 5, 1, 2, 8, 300, 64, ctypes.c_float(0.125), 0, None, None]
+    assert lib.attn_fwd_block_sparse(*p, None, 0, 0, None) == ta.ATTN_ERR_NULL
+    assert lib.attn_fwd_block_sparse(*p, A16 * 40, -1, 0, None) == ta.ATTN_ERR_MASK
+    p_long = p[:8] + [40000] + p[9:]
+    assert lib.attn_fwd_block_sparse(*p_long, A16 * 40, 0, 0, None) == ta.ATTN_ERR_SHAPE   # > 32768 keys
+    p_bad = p[:11] + [3] + p[12:]
+    assert lib.attn_fwd_block_sparse(*p_bad, A16 * 40, 0, 0, None) == ta.ATTN_ERR_MASK

@@ -374,3 +374,16 @@ def test_dense_mask_torch_cross_check():
         torch.tensor(q), torch.tensor(k), torch.tensor(v), attn_mask=torch.tensor(mask), scale=0.35).numpy()
     o, _ = attention(q, k, v, 0.35, False, attn_mask=mask)
     np.testing.assert_allclose(o, want, atol=1e-12)
+
+
+def test_block_mask_expansion_brute_force():
+    from oracle import expand_block_mask
+    rng = np.random.default_rng(101)
+    bm = rng.random((2, 3, 3, 5)) < 0.5
+    m = expand_block_mask(bm, 7, 9, 3, 2)
+    assert m.shape == (2, 3, 7, 9)
+    for b in range(2):
+        for h in range(3):
+            for i in range(7):
+                for j in range(9):
+                    assert m[b, h, i, j] == bm[b, h, i // 3, j // 2]

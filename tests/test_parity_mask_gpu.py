@@ -137,3 +137,72 @@ def test_first_allowed_key_late_with_large_logits(d):
         if i % 2:
             mask[0, 0, i, :first[i]] = False
     compare(q, k, v, np.float32(d ** -0.5), 0, mask)
+
+
+# ---------------------------------------------------------------- block-sparse (attn_fwd_block_sparse)
+SPARSE = [
+    # B, H, N_q, N_k, d, causal, block-mask shape (b, h), density, seqlens, q_start
+    (1, 2, 300, 700, 128, 0, (1, 2), 0.5, None, None),
+    (2, 1, 600, 600, 64, 1, (2, 1), 0.6, [600, 333], [0, 100]),
+    (1, 1, 512, 2100, 128, 0, (1, 1), 0.2, None, None),
+    (1, 2, 257, 1000, 128, 2, (1, 1), 0.7, None, None),
+]
+
+
+@pytest.mark.parametrize("case", SPARSE, ids=[f"{c[2]}x{c[3]}_d{c[4]}_c{c[5]}_p{c[7]}" for c in SPARSE])
+def test_block_sparse(case):
+    import tiled_attention_16_amd as ta
+    from oracle import expand_block_mask
+    B, H, nq, nk, d, causal, (mb, mh), dens, sl, qs = case
+    q, k, v = make_random(B, H, nq, nk, d, seed=nq + 13 * nk + d)
+    rng = np.random.default_rng(nq + 17 * nk)
+    nqb, nkb = -(-nq // 256), -(-nk // 32)
+    bm = rng.random((mb, mh, nqb, nkb)) < dens
+    bm[0, 0, 0, :] = False                    # a tile with no block at all: its rows output 0
+    scale = np.float32(d ** -0.5)
+    slt = torch.from_numpy(np.array(sl, np.int32)).cuda() if sl is not None else None
+    qst = torch.from_numpy(np.array(qs, np.int32)).cuda() if qs is not None else None
+    print(f"  block-sparse {case}", flush=True)
+    o, lse = ta.attn_fwd(to_dev(q), to_dev(k), to_dev(v), causal=causal, scale=float(scale), seqlens_k=slt,
+                         q_start=qst, block_mask=torch.from_numpy(bm).cuda())
+    torch.cuda.synchronize()
+    o, lse = f64(o), lse.cpu().numpy().astype(np.float64)
+    ro, rl = attention(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), float(scale), causal,
+                       seqlens_k=None if sl is None else np.array(sl), q_start=None if qs is None else np.array(qs),
+                       attn_mask=expand_block_mask(bm, nq, nk, 256, 32))
+    r = check(o, ro, lse, rl)
+    print("  ", r, flush=True)
+    assert r.ok, str(r)
+    assert np.all(o[0, 0, :256] == 0) and np.all(np.isneginf(lse[0, 0, :256]))
+
+
+def test_block_sparse_all_kept_equals_plain():
+    import tiled_attention_16_amd as ta
+    q, k, v = make_random(1, 2, 700, 700, 128, seed=111)
+    tq, tk, tv = to_dev(q), to_dev(k), to_dev(v)
+    bm = torch.ones((1, 1, 3, 22), dtype=torch.bool, device="cuda")
+    o1, l1 = ta.attn_fwd(tq, tk, tv, causal=True)
+    o2, l2 = ta.attn_fwd(tq, tk, tv, causal=True, block_mask=bm)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_block_sparse_full_size_sampled():
+    """The causal N = 4096 workload with half of its blocks kept (one mask for all heads)."""
+    import tiled_attention_16_amd as ta
+    from oracle import expand_block_mask
+    w = WORKLOADS["causal_n4096_d128"]
+    inp = make_inputs(w)
+    bm = np.random.default_rng(7).random((1, 1, 16, 128)) < 0.5
+    o, lse = ta.attn_fwd(to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), causal=True, scale=float(inp.scale),
+                         block_mask=torch.from_numpy(bm).cuda())
+    torch.cuda.synchronize()
+    o, lse = f64(o), lse.cpu().numpy().astype(np.float64)
+    rows = np.unique(np.concatenate([[0, 255, 256, 2047, 4095], np.random.default_rng(8).choice(4096, 40, replace=False)]))
+    full = expand_block_mask(bm, 4096, 4096, 256, 32)
+    for b, h in [(0, 0), (0, 31)]:
+        ro, rl = attention(bf16_bits_to_f64(inp.q[b:b + 1, h:h + 1]), bf16_bits_to_f64(inp.k[b:b + 1, h:h + 1]),
+                           bf16_bits_to_f64(inp.v[b:b + 1, h:h + 1]), float(inp.scale), True, rows=rows, attn_mask=full)
+        r = check(o[b:b + 1, h:h + 1, rows], ro, lse[b:b + 1, h:h + 1, rows], rl)
+        print(f"  block-sparse b={b} h={h}: {r}", flush=True)
+        assert r.ok, str(r)

@@ -38,8 +38,11 @@ def causal_mode(causal) -> int:
     return int(causal)
 
 # every symbol include/attn.h declares
-EXPORTS = ("attn_bwd", "attn_bwd_masked", "attn_fwd", "attn_fwd_masked", "attn_mask_pack", "attn_status_str",
-           "attn_version")
+EXPORTS = ("attn_bwd", "attn_bwd_masked", "attn_fwd", "attn_fwd_block_sparse", "attn_fwd_masked", "attn_mask_pack",
+           "attn_status_str", "attn_version")
+
+SPARSE_BLOCK_Q = 256   # query rows per block of attn_fwd_block_sparse's block mask
+SPARSE_BLOCK_K = 32    # keys per block
 
 _lib = None
 
@@ -61,6 +64,9 @@ def load_library() -> ctypes.CDLL:
     lib.attn_fwd_masked.restype = ctypes.c_int
     lib.attn_fwd_masked.argtypes = lib.attn_fwd.argtypes[:14] + [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_longlong,
                                                                  ctypes.c_int, ctypes.c_void_p]
+    lib.attn_fwd_block_sparse.restype = ctypes.c_int
+    lib.attn_fwd_block_sparse.argtypes = lib.attn_fwd.argtypes[:14] + [ctypes.c_void_p, ctypes.c_longlong,
+                                                                       ctypes.c_longlong, ctypes.c_void_p]
     lib.attn_mask_pack.restype = ctypes.c_int
     lib.attn_mask_pack.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_void_p]
@@ -134,14 +140,16 @@ def pack_mask(mask, stream=None):
 
 def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None, seqlens_k=None, q_start=None,
              return_lse: bool = True, out=None, lse=None, stream=None, attn_mask=None,
-             packed_mask=None) -> Tuple[object, Optional[object]]:
+             packed_mask=None, block_mask=None) -> Tuple[object, Optional[object]]:
     """Fused attention forward on bf16 ``[B, H, N, d]`` CUDA (HIP) tensors.
 
     ``causal``: False (none), True or "top_left" (key j visible to row i iff
     j <= i), "bottom_right" (iff j <= i + N_k - N_q). ``attn_mask``: optional
     bool GPU tensor ``[B or 1, H or 1, N_q, N_k]``, True = may attend,
     intersected with the other rules (packed by the library on each call;
-    pass ``packed_mask=pack_mask(m)`` to pack once).
+    pass ``packed_mask=pack_mask(m)`` to pack once). ``block_mask``: optional
+    bool/uint8 GPU tensor ``[B or 1, H or 1, ceil(N_q/256), ceil(N_k/32)]``;
+    only the blocks it keeps are computed (``attn_fwd_block_sparse``).
     Returns ``(o, lse)``; ``lse`` is None unless ``return_lse``. ``scale``
     defaults to ``d ** -0.5``. ``seqlens_k`` / ``q_start`` are optional int32
     device tensors of shape ``[B]``. The kernel is launched on ``stream`` (a
@@ -182,7 +190,21 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None, se
             (lse.data_ptr() or None) if lse is not None else None, B, H, N_q, N_k, d, ctypes.c_float(scale),
             causal_mode(causal), seqlens_k.data_ptr() if seqlens_k is not None else None,
             q_start.data_ptr() if q_start is not None else None]
-    if packed_mask is not None:
+    if block_mask is not None:
+        if packed_mask is not None:
+            raise ValueError("block_mask and attn_mask cannot be combined")
+        nqb, nkb = -(-N_q // SPARSE_BLOCK_Q), -(-N_k // SPARSE_BLOCK_K)
+        if not isinstance(block_mask, torch.Tensor) or not block_mask.is_cuda or block_mask.dim() != 4 or \
+                block_mask.dtype not in (torch.bool, torch.uint8) or block_mask.shape[2:] != (nqb, nkb) or \
+                block_mask.shape[0] not in (1, B) or block_mask.shape[1] not in (1, H):
+            raise ValueError(f"block_mask must be a bool/uint8 GPU tensor [1 or {B}, 1 or {H}, {nqb}, {nkb}]")
+        bm = block_mask.contiguous()
+        if bm.dtype == torch.bool:
+            bm = bm.view(torch.uint8)
+        sb = 0 if bm.shape[0] == 1 else bm.shape[1] * nqb * nkb
+        sh = 0 if bm.shape[1] == 1 else nqb * nkb
+        status = lib.attn_fwd_block_sparse(*args, bm.data_ptr(), sb, sh, ctypes.c_void_p(st.cuda_stream))
+    elif packed_mask is not None:
         bits, sb, sh, rw = packed_mask
         status = lib.attn_fwd_masked(*args, bits.data_ptr() or None, sb, sh, rw, ctypes.c_void_p(st.cuda_stream))
     else:

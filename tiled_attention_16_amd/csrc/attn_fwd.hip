@@ -197,14 +197,27 @@ __device__ __forceinline__ void wait_copies() {
 // matrix (b, h) at word b*msb + h*msh) set means row i may attend to key j.
 // Each wave copies its rows' words for the next 8 slices into LDS with one
 // buffer_load ... lds per 8 steps; every slice is masked.
-template <int D, bool Dense>
+// Sparse (block-sparse attention, [MEMWALL] §7): a byte per (256-row query
+// tile, 32-key slice) says whether the slice is computed for that tile at
+// all (rows of n_ks bytes, matrix (b, h) at byte b*bsb + h*bsh). At each tile
+// start wave 0 compacts the tile's set flags into a list of slice indices in
+// LDS; the ring walks that list, so unset slices cost neither copies nor
+// arithmetic. The rules still mask inside the slices that are computed.
+constexpr int kMaxSparseSlices = 1024;   // keys per head up to 32768 on the sparse path
+constexpr int kListPad = 80;             // sentinel entries past the list (the copies look 7 ahead)
+
+template <int D, int Mode>   // Mode 0: rules only; 1: dense mask (Dense); 2: block-sparse (Sparse)
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int H, int N_q, int N_k, float c, int neg_scale,
     int causal, int coff, const int32_t* __restrict__ seqlens_k, const int32_t* __restrict__ q_start, int n_qt,
-    int n_wg, const uint32_t* __restrict__ mbits, long long msb, long long msh, int mrw) {
+    int n_wg, const uint32_t* __restrict__ mbits, long long msb, long long msh, int mrw,
+    const uint8_t* __restrict__ bmask, long long bsb, long long bsh, int n_ks) {
+  constexpr bool Dense = Mode == 1, Sparse = Mode == 2;
   using T = Slice<D>;
-  constexpr int kMaskLds = Dense ? 2 * kWaves * 1024 : 0;   // two 8-slice blocks of mask words per wave
+  constexpr int kMaskLds = Dense ? 2 * kWaves * 1024                              // two 8-slice blocks of mask words per wave
+                                 : Sparse ? 4 * (kMaxSparseSlices + kListPad + 16)   // the slice list
+                                          : 0;
   __shared__ __attribute__((aligned(1024))) char smem[T::kLds + kMaskLds];
 
   const int tid = threadIdx.x;
@@ -296,10 +309,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // the V stage base relative to the folded-in kVBase (see v_off below)
   auto vst_rel = [&](int st) __attribute__((always_inline)) { return (const char*)smem + st * T::kBytes; };
   constexpr int kC = 2 * T::kCopiesPerWave;   // copies per wave per K+V slice
-  auto copy_slices = [&](int s) __attribute__((always_inline)) {
+  // K and V of key slice sl into the stage of ring position s
+  auto copy_slices = [&](int s, int sl) __attribute__((always_inline)) {
     const int st = s & (kStages - 1);
-    copy_slice(k_rsrc, s, kst(st));
-    copy_slice(v_rsrc, s, vst(st));
+    copy_slice(k_rsrc, sl, kst(st));
+    copy_slice(v_rsrc, sl, vst(st));
   };
 
   // ---- per-lane LDS offsets of the MFMA operand reads ----
@@ -372,10 +386,59 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   const size_t q_base = (size_t)bh * N_q * D;
 
   // slices: nh_wg for the workgroup, nh (a prefix) for this wave
-  const int nh_wg = (kv_end + kSlice - 1) / kSlice;
+  const int nsl = (kv_end + kSlice - 1) / kSlice;   // slices below kv_end
+  int nh_wg = nsl;
   int nh = wave_live ? nh_wg : 0;
   if (causal) nh = min(nh, row_hi + coff < 0 ? 0 : (row_hi + coff) / kSlice + 1);
   nh = __builtin_amdgcn_readfirstlane(nh);
+  // Sparse: the list of the tile's computed slices (ring position -> slice),
+  // then nh_wg = its length and nh = its entries at or below this wave's
+  // last slice. Entries past the list are nsl: their copies fetch nothing.
+  [[maybe_unused]] int* lst = (int*)(smem + T::kLds);
+  [[maybe_unused]] int lst_v = 0;   // entries h0 .. h0+63 of the list, one per lane
+  if constexpr (Sparse) {
+    if (it > 0) __syncthreads();   // every wave is done with the previous tile's list
+    if (wave == 0) {
+      const uint8_t* fl = bmask + (size_t)b * bsb + (size_t)(bh - b * H) * bsh + (size_t)qt * n_ks;
+      uint32_t bits = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int sl = 16 * lane + i;
+        if (sl < nsl && fl[sl] != 0) bits |= 1u << i;
+      }
+      const int cnt = __builtin_popcount(bits);
+      int incl = cnt;   // inclusive prefix sum over the wave
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      int pos = incl - cnt;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if ((bits >> i) & 1u) lst[pos++] = 16 * lane + i;
+      const int total = __shfl(incl, 63, 64);
+      for (int i = lane; i < kListPad; i += 64) lst[total + i] = nsl;
+      if (lane == 0) lst[kMaxSparseSlices + kListPad] = total;
+    }
+    __syncthreads();
+    nh_wg = __builtin_amdgcn_readfirstlane(lst[kMaxSparseSlices + kListPad]);
+    int lim_sl = 0x7fffffff;   // this wave's last slice
+    if (causal) lim_sl = row_hi + coff < 0 ? -1 : (row_hi + coff) / kSlice;
+    int cnt = 0;
+    for (int base = 0; base < nh_wg; base += 64) {
+      const int idx = base + lane;
+      const bool in = idx < nh_wg && lst[idx] <= lim_sl;
+      cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(in));
+    }
+    nh = wave_live ? __builtin_amdgcn_readfirstlane(cnt) : 0;
+    lst_v = lst[lane];
+  }
+  // slice index of ring position h = h0 + j (Sparse: from the list; j < 64)
+  auto slice_of = [&](int h, int j) __attribute__((always_inline)) {
+    if constexpr (Sparse) return __builtin_amdgcn_readlane(lst_v, j);
+    else return h;
+  };
 
   // ---- Q rows -> VGPRs as the B operand of S^T = K Q^T ----
   bf16x8 qreg[kRB][D / 16];
@@ -645,7 +708,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     wait_copies<4 * kC>();
     __syncthreads();   // slices <= h+2 have landed; slice h-1's stage is no longer read
     if (h >= nh) {   // this wave's rows are done; it still copies its share
-      copy_slices(h + kStages - 1);
+      copy_slices(h + kStages - 1, slice_of(h + kStages - 1, Hm + kStages - 1));
       return;
     }
     // ---- phase A ----
@@ -683,16 +746,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     // freed. The copies go out between the phases and at the end of the step,
     // where the waves arrive at different times, so the workgroup's copies
     // reach the address unit spread out rather than all at once.
-    copy_slice(k_rsrc, h + kStages - 1, kst((Hm + kStages - 1) % kStages));
+    copy_slice(k_rsrc, slice_of(h + kStages - 1, Hm + kStages - 1), kst((Hm + kStages - 1) % kStages));
     // Dense: the next 8-slice block's mask words (used from step h+7 on; the
     // copies issued in between make the waits of those steps cover it).
     if constexpr (Dense && Hm == 0) copy_mask((h >> 3) + 1);
     // S of slice h+1 is read below. The mask reads it at once and needs the
     // wait states; for d = 128 the phase-B shifts come late enough without
     // them (the build's hazard check verifies that distance), for d = 64 not.
-    const bool msk = Dense || (unsigned)(h + 1 - mask_from) < (unsigned)mask_span;
+    bool msk;
+    if constexpr (Sparse) msk = h + 1 < nh && slice_of(h + 1, Hm + 1) >= mask_from;
+    else msk = Dense || (unsigned)(h + 1 - mask_from) < (unsigned)mask_span;
     if (D == 64 || msk) mfma_result_wait();
-    if (msk) mask(h + 1, sn);
+    if (msk) mask(slice_of(h + 1, Hm + 1), sn);
     // ---- phase B ----
     {
       const char* kb = kst((Hm + 2) % kStages);
@@ -719,7 +784,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    copy_slice(v_rsrc, h + kStages - 1, vst((Hm + kStages - 1) % kStages));   // the V share
+    copy_slice(v_rsrc, slice_of(h + kStages - 1, Hm + kStages - 1), vst((Hm + kStages - 1) % kStages));   // the V share
   };
 
   f32x16 sa[kRB], sb[kRB];
@@ -727,13 +792,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     if (it > 0) __syncthreads();   // every wave is done reading the previous tile's stages
     copy_mask(0);   // Dense: the first block's mask words, ahead of the copies the wait below covers
 #pragma unroll
-    for (int s = 0; s < kStages - 1; ++s) copy_slices(s);
+    for (int s = 0; s < kStages - 1; ++s) copy_slices(s, slice_of(s, s));
     wait_copies<4 * kC>();
     __syncthreads();   // slices 0 .. 2 have landed
     if (nh > 0) {
       load_k(std::integral_constant<int, 0>{});
       qk(sa);
-      if (Dense || need_mask(0)) mask(0, sa);
+      if (Dense || need_mask(slice_of(0, 0))) mask(slice_of(0, 0), sa);
       first_max(sa);
 #pragma unroll
       for (int j = 0; j < 8; ++j) exp_one(sa[0], j, pbw_lo[0], lsum_lo[0]);
@@ -741,6 +806,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     }
     static_assert(kStages == 8, "the loop below is unrolled over kStages slices");
     for (int h0 = 0; h0 < nh_wg; h0 += 8) {
+      if constexpr (Sparse) lst_v = lst[h0 + lane];   // list entries h0 .. h0+63
       step(std::integral_constant<int, 0>{}, h0, sa, sb);
       if (h0 + 1 >= nh_wg) break;
       step(std::integral_constant<int, 1>{}, h0 + 1, sb, sa);
@@ -827,7 +893,8 @@ __global__ __launch_bounds__(256) void attn_mask_pack_kernel(const uint8_t* __re
 
 int fwd_launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q, int N_k,
                int d, float scale, int causal, const int32_t* seqlens_k, const int32_t* q_start,
-               const uint32_t* mbits, long long msb, long long msh, int mrw, hipStream_t stream) {
+               const uint32_t* mbits, long long msb, long long msh, int mrw, const uint8_t* bmask, long long bsb,
+               long long bsh, int n_ks, hipStream_t stream) {
   if (B < 0 || H < 0 || N_q < 0 || N_k < 0) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
@@ -865,11 +932,12 @@ int fwd_launch(const void* q, const void* k, const void* v, void* o, float* lse,
   uint16_t* op = (uint16_t*)o;
   // causal mode 1: key j visible to row i iff j <= i; mode 2: iff j <= i + N_k - N_q
   int causal01 = causal ? 1 : 0, coff = causal == 2 ? N_k - N_q : 0, n_qt_i = (int)n_qt, n_wg_i = (int)n_wg;
-  const bool dense = mbits != nullptr;
-  auto kern = d == 128 ? (dense ? attn_fwd_kernel<128, true> : attn_fwd_kernel<128, false>)
-                       : (dense ? attn_fwd_kernel<64, true> : attn_fwd_kernel<64, false>);
-  const hipError_t e = attn_launch::launch(kern, dim3((unsigned)n_wg), dim3(kThreads), stream, qp, kp, vp, op, lse, H, N_q, N_k, c,
-                              neg, causal01, coff, seqlens_k, q_start, n_qt_i, n_wg_i, mbits, msb, msh, mrw);
+  const int mode = mbits ? 1 : bmask ? 2 : 0;
+  auto kern = d == 128 ? (mode == 1 ? attn_fwd_kernel<128, 1> : mode == 2 ? attn_fwd_kernel<128, 2> : attn_fwd_kernel<128, 0>)
+                       : (mode == 1 ? attn_fwd_kernel<64, 1> : mode == 2 ? attn_fwd_kernel<64, 2> : attn_fwd_kernel<64, 0>);
+  const hipError_t e = attn_launch::launch(kern, dim3((unsigned)n_wg), dim3(kThreads), stream, qp, kp, vp, op, lse, H, N_q,
+                                           N_k, c, neg, causal01, coff, seqlens_k, q_start, n_qt_i, n_wg_i, mbits, msb,
+                                           msh, mrw, bmask, bsb, bsh, n_ks);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -878,7 +946,8 @@ int fwd_launch(const void* q, const void* k, const void* v, void* o, float* lse,
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                         int N_q, int N_k, int d, float scale, int causal, const int32_t* seqlens_k,
                         const int32_t* q_start, hipStream_t stream) {
-  return fwd_launch(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, seqlens_k, q_start, nullptr, 0, 0, 0, stream);
+  return fwd_launch(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, seqlens_k, q_start, nullptr, 0, 0, 0, nullptr,
+                    0, 0, 0, stream);
 }
 
 extern "C" int attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -888,7 +957,7 @@ extern "C" int attn_fwd_masked(const void* q, const void* k, const void* v, void
   if (B < 0 || H < 0 || N_q < 0 || N_k < 0) return ATTN_ERR_SHAPE;
   if (!mask_bits) {
     if ((long long)B * H * N_q == 0) return fwd_launch(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, seqlens_k,
-                                                       q_start, nullptr, 0, 0, 0, stream);
+                                                       q_start, nullptr, 0, 0, 0, nullptr, 0, 0, 0, stream);
     return ATTN_ERR_NULL;
   }
   if ((uintptr_t)mask_bits & 15) return ATTN_ERR_ALIGN;
@@ -896,7 +965,23 @@ extern "C" int attn_fwd_masked(const void* q, const void* k, const void* v, void
     return ATTN_ERR_MASK;
   if ((long long)N_q * mask_row_words * 4 > 0x7fffffffLL) return ATTN_ERR_SHAPE;   // 32-bit copy offsets
   return fwd_launch(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, seqlens_k, q_start, mask_bits,
-                    mask_stride_b, mask_stride_h, mask_row_words, stream);
+                    mask_stride_b, mask_stride_h, mask_row_words, nullptr, 0, 0, 0, stream);
+}
+
+extern "C" int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                     int N_q, int N_k, int d, float scale, int causal, const int32_t* seqlens_k,
+                                     const int32_t* q_start, const uint8_t* block_mask, long long block_stride_b,
+                                     long long block_stride_h, hipStream_t stream) {
+  if (B < 0 || H < 0 || N_q < 0 || N_k < 0) return ATTN_ERR_SHAPE;
+  const int n_ks = (N_k + kSlice - 1) / kSlice;
+  if ((long long)B * H * N_q == 0)
+    return fwd_launch(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, seqlens_k, q_start, nullptr, 0, 0, 0, nullptr,
+                      0, 0, 0, stream);
+  if (!block_mask) return ATTN_ERR_NULL;
+  if (n_ks > kMaxSparseSlices) return ATTN_ERR_SHAPE;
+  if (block_stride_b < 0 || block_stride_h < 0) return ATTN_ERR_MASK;
+  return fwd_launch(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, seqlens_k, q_start, nullptr, 0, 0, 0,
+                    block_mask, block_stride_b, block_stride_h, n_ks, stream);
 }
 
 extern "C" int attn_mask_pack(const uint8_t* mask, uint32_t* bits, long long rows, int N_k, int row_words,
