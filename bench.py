@@ -133,6 +133,9 @@ def main():
     ap.add_argument("--window", type=int, default=0, metavar="W",
                     help="forward with a dense boolean mask (attn_fwd_masked): key j visible to row i iff "
                          "i - W < j <= i, one mask shared by all heads, packed once before the timed region")
+    ap.add_argument("--block-density", type=float, default=0.0, metavar="P",
+                    help="block-sparse forward (attn_fwd_block_sparse): each (256-row tile, 32-key slice) block "
+                         "kept with probability P (seeded, shared by all heads); value counts the kept blocks' work")
     ap.add_argument("--backward", action="store_true",
                     help="time attn_bwd (dQ, dK, dV; its three launches) instead of the forward; O and LSE come "
                          "from one attn_fwd call before the timed region")
@@ -175,6 +178,17 @@ def main():
         return bench_backward(args, torch, ta, w, inp, sets[0], sl, qs, stream, dev)
 
     packed = None
+    bmask = None
+    if args.block_density:
+        nqb, nkb = -(-w.N_q // 256), -(-w.N_k // 32)
+        keep = np.random.default_rng(w.seed + 700).random((1, 1, nqb, nkb)) < args.block_density
+        bmask = torch.from_numpy(keep).to(dev)
+        # counted flops of the kept blocks: allowed (row, key) pairs inside kept blocks
+        i = np.arange(w.N_q)[:, None]
+        j = np.arange(w.N_k)[None, :]
+        allowed = (j <= i) if w.causal else np.ones((w.N_q, w.N_k), bool)
+        kept = keep[0, 0][np.arange(w.N_q) // 256][:, np.arange(w.N_k) // 32]
+        sparse_frac = float((allowed & kept).sum()) / float(allowed.sum())
     if args.window:
         i = torch.arange(w.N_q, device=dev)[:, None]
         j = torch.arange(w.N_k, device=dev)[None, :]
@@ -184,7 +198,7 @@ def main():
         sq, sk, sv, so, slse = sets[n_step[0] % len(sets)]
         n_step[0] += 1
         ta.attn_fwd(sq, sk, sv, causal=w.causal, scale=float(inp.scale), seqlens_k=sl, q_start=qs, out=so,
-                    lse=slse, stream=stream, packed_mask=packed)
+                    lse=slse, stream=stream, packed_mask=packed, block_mask=bmask)
 
     for _ in range(args.warmup):
         step()
@@ -202,10 +216,10 @@ def main():
     wall = time.perf_counter() - t0
     total_ms = e_start.elapsed_time(e_end)
     ms_per_step = total_ms / args.steps
-    flops = w.flops()
+    flops = w.flops() * (sparse_frac if args.block_density else 1.0)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     achieved = tflops
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic(w.name) if not (args.window or args.block_density) else None
     if hbm_probe:
         gbs = w.algorithmic_bytes() / (ms_per_step * 1e-3) / 1e9
         result = {
@@ -237,7 +251,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.N_q, "N_k": w.N_k, "d": w.d,
                    "causal": w.causal, "varlen": inp.seqlens_k is not None,
-                   **({"dense_mask": f"sliding window {args.window}"} if args.window else {})},
+                   **({"dense_mask": f"sliding window {args.window}"} if args.window else {}),
+                   **({"block_sparse": f"density {args.block_density}, kept fraction of the counted work "
+                                       f"{sparse_frac:.3f}"} if args.block_density else {})},
         "pct_of_mfma_bf16_peak": round(100.0 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
