@@ -209,6 +209,20 @@ int attn_bwd_masked(const void* q, const void* k, const void* v, const void* o, 
                     const uint32_t* mask_bits, long long mask_stride_b, long long mask_stride_h,
                     int mask_row_words, hipStream_t stream);
 
+/*
+ * attn_bwd_block_sparse - attn_bwd for attn_fwd_block_sparse: the same
+ * gradients computing only the kept blocks (same block mask layout and
+ * strides). o and lse must come from attn_fwd_block_sparse with the same
+ * block mask. N_q and N_k are each limited to 32768 on this path (else
+ * ATTN_ERR_SHAPE); a NULL block_mask with work to do is ATTN_ERR_NULL.
+ */
+int attn_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                          const float* lse, void* dq, void* dk, void* dv, float* delta,
+                          int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                          const int32_t* seqlens_k, const int32_t* q_start,
+                          const uint8_t* block_mask, long long block_stride_b, long long block_stride_h,
+                          hipStream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* attn_status_str(int status);
 

@@ -191,3 +191,12 @@ def test_block_sparse_argument_errors(lib):
     assert lib.attn_fwd_block_sparse(*p_long, A16 * 40, 0, 0, None) == ta.ATTN_ERR_SHAPE   # > 32768 keys
     p_bad = p[:11] + [3] + p[12:]
     assert lib.attn_fwd_block_sparse(*p_bad, A16 * 40, 0, 0, None) == ta.ATTN_ERR_MASK
+
+
+def test_bwd_block_sparse_argument_errors(lib):
+    p = [A16, A16 * 2, A16 * 3, A16 * 4, A16 * 5, A16 * 6, A16 * 7, A16 * 8, A16 * 9, A16 * 10, 1, 2, 8, 300, 64,
+         ctypes.c_float(0.125), 0, None, None]
+    assert lib.attn_bwd_block_sparse(*p, None, 0, 0, None) == ta.ATTN_ERR_NULL
+    assert lib.attn_bwd_block_sparse(*p, A16 * 40, 0, -2, None) == ta.ATTN_ERR_MASK
+    p_long = p[:12] + [40000] + p[13:]
+    assert lib.attn_bwd_block_sparse(*p_long, A16 * 40, 0, 0, None) == ta.ATTN_ERR_SHAPE

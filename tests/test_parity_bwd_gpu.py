@@ -230,3 +230,37 @@ def test_bwd_dense_mask(case):
     assert r.ok, str(r)
     assert np.all(dk[:, :, 7] == 0) and np.all(dv[:, :, 7] == 0)
     assert np.all(dq[0, 0, 3] == 0)
+
+
+SPARSE = [
+    # B, H, N_q, N_k, d, causal, block-mask shape (b, h), density
+    (1, 2, 300, 700, 128, 0, (1, 2), 0.5),
+    (2, 1, 600, 600, 64, 1, (2, 1), 0.6),
+    (1, 2, 520, 300, 128, 2, (1, 1), 0.4),
+]
+
+
+@pytest.mark.parametrize("case", SPARSE, ids=[f"{c[2]}x{c[3]}_d{c[4]}_c{c[5]}_p{c[7]}" for c in SPARSE])
+def test_bwd_block_sparse(case):
+    import tiled_attention_16_amd as ta
+    from oracle import expand_block_mask
+    B, H, nq, nk, d, causal, (mb, mh), dens = case
+    q, k, v = make_random(B, H, nq, nk, d, seed=nq + 19 * nk + d)
+    g = make_dout((B, H, nq, d), seed=nq + 23 * nk)
+    rng = np.random.default_rng(nq + 29 * nk)
+    bm = rng.random((mb, mh, -(-nq // 256), -(-nk // 32))) < dens
+    bm[..., 1] = False                          # keys 32..63 in no kept block: dK = dV = 0
+    scale = np.float32(d ** -0.5)
+    print(f"  block-sparse bwd {case}", flush=True)
+    tq, tk, tv, tg = to_dev(q), to_dev(k), to_dev(v), to_dev(g)
+    tb = torch.from_numpy(bm).cuda()
+    o, lse = ta.attn_fwd(tq, tk, tv, causal=causal, scale=float(scale), block_mask=tb)
+    dq, dk, dv = ta.attn_bwd(tq, tk, tv, o, lse, tg, causal=causal, scale=float(scale), block_mask=tb)
+    torch.cuda.synchronize()
+    dq, dk, dv = f64(dq), f64(dk), f64(dv)
+    rq, rk, rv = attention_bwd(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), bf16_bits_to_f64(g),
+                               float(scale), causal, attn_mask=expand_block_mask(bm, nq, nk, 256, 32))
+    r = check_grads({"dq": dq, "dk": dk, "dv": dv}, {"dq": rq, "dk": rk, "dv": rv})
+    print("  ", r, flush=True)
+    assert r.ok, str(r)
+    assert np.all(dk[:, :, 32:64] == 0) and np.all(dv[:, :, 32:64] == 0)

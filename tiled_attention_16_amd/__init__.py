@@ -38,8 +38,8 @@ def causal_mode(causal) -> int:
     return int(causal)
 
 # every symbol include/attn.h declares
-EXPORTS = ("attn_bwd", "attn_bwd_masked", "attn_fwd", "attn_fwd_block_sparse", "attn_fwd_masked", "attn_mask_pack",
-           "attn_status_str", "attn_version")
+EXPORTS = ("attn_bwd", "attn_bwd_block_sparse", "attn_bwd_masked", "attn_fwd", "attn_fwd_block_sparse",
+           "attn_fwd_masked", "attn_mask_pack", "attn_status_str", "attn_version")
 
 SPARSE_BLOCK_Q = 256   # query rows per block of attn_fwd_block_sparse's block mask
 SPARSE_BLOCK_K = 32    # keys per block
@@ -76,6 +76,9 @@ def load_library() -> ctypes.CDLL:
     lib.attn_bwd_masked.restype = ctypes.c_int
     lib.attn_bwd_masked.argtypes = lib.attn_bwd.argtypes[:19] + [ctypes.c_void_p, ctypes.c_longlong,
                                                                  ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p]
+    lib.attn_bwd_block_sparse.restype = ctypes.c_int
+    lib.attn_bwd_block_sparse.argtypes = lib.attn_bwd.argtypes[:19] + [ctypes.c_void_p, ctypes.c_longlong,
+                                                                       ctypes.c_longlong, ctypes.c_void_p]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_version.restype = ctypes.c_int
@@ -138,6 +141,23 @@ def pack_mask(mask, stream=None):
     return bits, (0 if Bm == 1 else Hm * N_q * rw), (0 if Hm == 1 else N_q * rw), rw
 
 
+def _block_mask_args(block_mask, B, H, N_q, N_k):
+    """Check a block mask and return (uint8 tensor, batch stride, head stride) in bytes."""
+    import torch
+
+    nqb, nkb = -(-N_q // SPARSE_BLOCK_Q), -(-N_k // SPARSE_BLOCK_K)
+    if not isinstance(block_mask, torch.Tensor) or not block_mask.is_cuda or block_mask.dim() != 4 or \
+            block_mask.dtype not in (torch.bool, torch.uint8) or block_mask.shape[2:] != (nqb, nkb) or \
+            block_mask.shape[0] not in (1, B) or block_mask.shape[1] not in (1, H):
+        raise ValueError(f"block_mask must be a bool/uint8 GPU tensor [1 or {B}, 1 or {H}, {nqb}, {nkb}]")
+    bm = block_mask.contiguous()
+    if bm.dtype == torch.bool:
+        bm = bm.view(torch.uint8)
+    sb = 0 if bm.shape[0] == 1 else bm.shape[1] * nqb * nkb
+    sh = 0 if bm.shape[1] == 1 else nqb * nkb
+    return bm, sb, sh
+
+
 def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None, seqlens_k=None, q_start=None,
              return_lse: bool = True, out=None, lse=None, stream=None, attn_mask=None,
              packed_mask=None, block_mask=None) -> Tuple[object, Optional[object]]:
@@ -193,16 +213,7 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None, se
     if block_mask is not None:
         if packed_mask is not None:
             raise ValueError("block_mask and attn_mask cannot be combined")
-        nqb, nkb = -(-N_q // SPARSE_BLOCK_Q), -(-N_k // SPARSE_BLOCK_K)
-        if not isinstance(block_mask, torch.Tensor) or not block_mask.is_cuda or block_mask.dim() != 4 or \
-                block_mask.dtype not in (torch.bool, torch.uint8) or block_mask.shape[2:] != (nqb, nkb) or \
-                block_mask.shape[0] not in (1, B) or block_mask.shape[1] not in (1, H):
-            raise ValueError(f"block_mask must be a bool/uint8 GPU tensor [1 or {B}, 1 or {H}, {nqb}, {nkb}]")
-        bm = block_mask.contiguous()
-        if bm.dtype == torch.bool:
-            bm = bm.view(torch.uint8)
-        sb = 0 if bm.shape[0] == 1 else bm.shape[1] * nqb * nkb
-        sh = 0 if bm.shape[1] == 1 else nqb * nkb
+        bm, sb, sh = _block_mask_args(block_mask, B, H, N_q, N_k)
         status = lib.attn_fwd_block_sparse(*args, bm.data_ptr(), sb, sh, ctypes.c_void_p(st.cuda_stream))
     elif packed_mask is not None:
         bits, sb, sh, rw = packed_mask
@@ -224,7 +235,8 @@ def attn_bwd_raw(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, d
 
 
 def attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] = None, seqlens_k=None,
-             q_start=None, dq=None, dk=None, dv=None, delta=None, stream=None, attn_mask=None, packed_mask=None):
+             q_start=None, dq=None, dk=None, dv=None, delta=None, stream=None, attn_mask=None, packed_mask=None,
+             block_mask=None):
     """Gradients ``(dq, dk, dv)`` of ``attn_fwd`` for upstream gradient ``dout``.
 
     ``o`` and ``lse`` are ``attn_fwd``'s outputs for the same inputs, mask and
@@ -273,7 +285,12 @@ def attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[flo
     args = [ptr(q), ptr(k), ptr(v), ptr(o), ptr(dout), ptr(lse), ptr(dq), ptr(dk), ptr(dv), ptr(delta), B, H, N_q,
             N_k, d, ctypes.c_float(scale), causal_mode(causal), seqlens_k.data_ptr() if seqlens_k is not None else None,
             q_start.data_ptr() if q_start is not None else None]
-    if packed_mask is not None:
+    if block_mask is not None:
+        if packed_mask is not None:
+            raise ValueError("block_mask and attn_mask cannot be combined")
+        bm, sb, sh = _block_mask_args(block_mask, B, H, N_q, N_k)
+        status = lib.attn_bwd_block_sparse(*args, bm.data_ptr(), sb, sh, ctypes.c_void_p(st.cuda_stream))
+    elif packed_mask is not None:
         bits, sb, sh, rw = packed_mask
         status = lib.attn_bwd_masked(*args, bits.data_ptr() or None, sb, sh, rw, ctypes.c_void_p(st.cuda_stream))
     else:

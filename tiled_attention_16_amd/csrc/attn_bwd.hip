@@ -173,6 +173,16 @@ struct DenseMask {
   int rw;
 };
 
+// Block mask of attn_fwd_block_sparse: a byte per (256-row query tile,
+// 32-key slice), rows of n_ks bytes, matrix (b, h) at byte b*sb + h*sh.
+struct BlockMask {
+  const uint8_t* flags;
+  long long sb, sh;
+  int n_ks;
+};
+constexpr int kMaxSparse = 1024;   // list entries (key slices, or 32-row query blocks) on the sparse path
+constexpr int kListPad = 16;       // sentinel entries past a list (the copies look up to 4 ahead)
+
 template <int N>
 __device__ __forceinline__ void wait_copies() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -221,17 +231,21 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const uint16_t* __r
 // ---------------------------------------------------------------- dq
 // Dense: a bit-packed mask is intersected with the rules; each wave copies
 // its 32 rows' words of the block with the block (one more copy per block).
-template <int D, bool Dense>
+// Mode 2 (Sparse): the key slices the block mask keeps for the tile's
+// 256-row block-mask tile are compacted into an LDS list that the ring walks.
+template <int D, int Mode>   // 0: rules only; 1: dense mask (Dense); 2: block-sparse (Sparse)
 __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const f32x2* __restrict__ stats, uint16_t* __restrict__ dQ, int H, int N_q,
     int N_k, float c, float scale, int causal, int coff, const int32_t* __restrict__ seqlens_k,
-    const int32_t* __restrict__ q_start, int n_qt, DenseMask dm) {
+    const int32_t* __restrict__ q_start, int n_qt, DenseMask dm, BlockMask bmk) {
+  constexpr bool Dense = Mode == 1, Sparse = Mode == 2;
   using R = Ring<D>;
   constexpr int kMaskBytes = Dense ? kWaves * 256 : 0;
   constexpr int kStage = 2 * R::kBlkBytes + kMaskBytes;   // [K block][V block][mask words of each wave]
   constexpr int kCpb = R::kCpw + (Dense ? 1 : 0);         // copies per wave per block
-  __shared__ __attribute__((aligned(1024))) char smem[kDepth * kStage];
+  constexpr int kListBytes = Sparse ? 4 * (kMaxSparse + kListPad + 4) : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[kDepth * kStage + kListBytes];
   const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   // Under a causal mask a tile's work grows with its index: launch the tiles
@@ -252,7 +266,43 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
   int kv_end = kv;
   if (causal) kv_end = min(kv_end, max(q_end + coff, 0));   // row i sees keys <= i + coff
   if (qs >= q_end) kv_end = 0;
-  const int nblk = (kv_end + kBlk - 1) / kBlk;
+  int nblk = (kv_end + kBlk - 1) / kBlk;
+  // Sparse: list of the kept slices below kv_end (ring position -> slice),
+  // padded with the slice nblk, whose copies fetch nothing
+  [[maybe_unused]] int* lst = (int*)(smem + kDepth * kStage);
+  if constexpr (Sparse) {
+    if (wave == 0) {
+      const uint8_t* fl = bmk.flags + (size_t)b * bmk.sb + (size_t)(bh - b * H) * bmk.sh +
+                          (size_t)(q0 / 256) * bmk.n_ks;
+      uint32_t bits = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int sl = 16 * lane + i;
+        if (sl < nblk && fl[sl] != 0) bits |= 1u << i;
+      }
+      const int cnt = __builtin_popcount(bits);
+      int incl = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      int pos = incl - cnt;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if ((bits >> i) & 1u) lst[pos++] = 16 * lane + i;
+      const int total = __shfl(incl, 63, 64);
+      if (lane < kListPad) lst[total + lane] = nblk;
+      if (lane == 0) lst[kMaxSparse + kListPad] = total;
+    }
+    __syncthreads();
+    nblk = __builtin_amdgcn_readfirstlane(lst[kMaxSparse + kListPad]);
+  }
+  // key slice of ring position n
+  auto slice_of = [&](int n) __attribute__((always_inline)) {
+    if constexpr (Sparse) return __builtin_amdgcn_readfirstlane(lst[n]);
+    else return n;
+  };
 
   const int row = q0 + kBlk * wave + (lane & 31);
   const bool row_ok = row < N_q;
@@ -302,9 +352,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
     m_rs = rsrc(dm.bits + (size_t)b * dm.sb + (size_t)(bh - b * H) * dm.sh, (uint32_t)N_q * dm.rw * 4);
     m_off = lane < 32 ? (uint32_t)(wrow0 + lane) * dm.rw * 4 : 0x40000000u;
   }
-  auto issue = [&](int n) {   // block n into stage n % kDepth
+  auto issue = [&](int n) {   // the block of ring position n into stage n % kDepth
     const uint32_t st = lds0 + (uint32_t)(n % kDepth) * kStage;
-    const uint32_t soff = (uint32_t)n * R::kBlkBytes;
+    const uint32_t soff = (uint32_t)slice_of(n) * R::kBlkBytes;
 #pragma unroll
     for (int i = 0; i < R::kCpw; ++i) {
       const int ci = wave * R::kCpw + i;
@@ -324,6 +374,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
     wait_copies<(kDepth - 2) * kCpb>();   // block n has landed (this wave's copies)
     __syncthreads();                          // everyone's copies; block n-1's stage is free
     issue(n + kDepth - 1);
+    const int sl = slice_of(n);
     const char* kb = smem + (n % kDepth) * kStage;
     const char* vb = kb + R::kBlkBytes;
     f32x16 s = {}, dp = {};
@@ -343,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
     }
     // P and dS; register r holds key n*32 + 8*(r/4) + 4*hf + r%4
     uint32_t w[8];
-    if (!Dense && n < full_below) {   // every key of the block is allowed for every row of the wave
+    if (!Dense && sl < full_below) {   // every key of the block is allowed for every row of the wave
 #pragma unroll
       for (int r = 0; r < 16; r += 2)
         w[r >> 1] = pack2(__builtin_amdgcn_exp2f(s[r] * c - lse2) * (dp[r] - dl),
@@ -353,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
       // keys and shifted so that bit e is the lane's key offset e (+ 4*hf)
       uint32_t mw = *(const __attribute__((address_space(3))) uint32_t*)(kb + 2 * R::kBlkBytes + wave * 256 +
                                                                           4 * (lane & 31));
-      const int lim0 = klim - n * kBlk;
+      const int lim0 = klim - sl * kBlk;
       const uint32_t pre = lim0 >= 31 ? 0xffffffffu : (lim0 < 0 ? 0u : ((2u << lim0) - 1u));
       mw = (mw & pre) >> (4 * hf);
 #pragma unroll
@@ -364,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
         w[r >> 1] = pack2(d0, d1);
       }
     } else {
-      const int lim = klim - n * kBlk - 4 * hf;
+      const int lim = klim - sl * kBlk - 4 * hf;
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const int j0 = 8 * (r >> 2) + (r & 3);
@@ -402,18 +453,25 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
 // ---------------------------------------------------------------- dk, dv
 // Dense: as in the dQ kernel; each wave copies, per block, the words of the
 // block's 32 rows that hold its own 32 keys.
-template <int D, bool Dense>
+// Mode 2 (Sparse): the WG walks the 32-row query blocks of every 256-row
+// block-mask tile that keeps the slice of at least one of its waves; each
+// list entry carries the block and a 4-bit mask of the waves whose slice the
+// tile keeps (the others take no part in that block).
+template <int D, int Mode>   // 0: rules only; 1: dense mask (Dense); 2: block-sparse (Sparse)
 __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const f32x2* __restrict__ stats, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int H, int N_q, int N_k, float c, float scale, int causal, int coff,
-    const int32_t* __restrict__ seqlens_k, const int32_t* __restrict__ q_start, int n_kt, DenseMask dm) {
+    const int32_t* __restrict__ seqlens_k, const int32_t* __restrict__ q_start, int n_kt, DenseMask dm,
+    BlockMask bmk) {
+  constexpr bool Dense = Mode == 1, Sparse = Mode == 2;
   using R = Ring<D>;
   constexpr int kMaskBytes = Dense ? kWaves * 256 : 0;
   // [Q block][dO block][stats of the 32 rows][mask words of each wave]
   constexpr int kStage = 2 * R::kBlkBytes + 1024 + kMaskBytes;
   constexpr int kCpb = R::kCpw + (Dense ? 1 : 0);   // copies per wave per block (wave 0: one more)
-  __shared__ __attribute__((aligned(1024))) char smem[(kDepth + 1) * kStage];
+  constexpr int kListBytes = Sparse ? 4 * (kMaxSparse + kListPad + 4) : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[(kDepth + 1) * kStage + kListBytes];
   const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   // Under a causal mask early key tiles have the most rows: tile-major order,
@@ -432,7 +490,52 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
   int r_begin = max(qs, causal ? max(k0 - coff, 0) : 0);   // row i sees keys <= i + coff
   if (k0 >= kv) r_begin = N_q;                  // every key of the tile is masked
   const int blk0 = r_begin / kBlk;
-  const int nblk = r_begin < N_q ? (N_q + kBlk - 1) / kBlk - blk0 : 0;
+  int nblk = r_begin < N_q ? (N_q + kBlk - 1) / kBlk - blk0 : 0;
+  // Sparse: list entries blk | (wave mask << 24) of the kept query blocks,
+  // padded with the block past the last row (its copies fetch nothing)
+  [[maybe_unused]] int* lst = (int*)(smem + (kDepth + 1) * kStage);
+  if constexpr (Sparse) {
+    const int nbq = (N_q + kBlk - 1) / kBlk;   // 32-row query blocks of the head
+    if (wave == 0) {
+      const uint8_t* fl = bmk.flags + (size_t)b * bmk.sb + (size_t)(bh - b * H) * bmk.sh;
+      int base = 0;
+      for (int t0 = blk0 / 8; t0 * 8 < nbq && nblk > 0; t0 += 64) {   // 256-row tiles, one per lane
+        const int t = t0 + lane;
+        uint32_t wm = 0;
+        if (t * 8 < nbq) {
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) {
+            const int sl = (k0 >> 5) + w;
+            if (sl < bmk.n_ks && fl[(size_t)t * bmk.n_ks + sl] != 0) wm |= 1u << w;
+          }
+        }
+        const int lo = max(8 * t, blk0), hi = min(8 * t + 8, nbq);
+        const int cnt = (wm != 0 && hi > lo) ? hi - lo : 0;
+        int incl = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int x = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += x;
+        }
+        int pos = base + incl - cnt;
+        for (int q = lo; q < lo + cnt; ++q) lst[pos++] = q | (int)(wm << 24);
+        base += __shfl(incl, 63, 64);
+      }
+      if (lane < kListPad) lst[base + lane] = nbq;
+      if (lane == 0) lst[kMaxSparse + kListPad] = base;
+    }
+    __syncthreads();
+    nblk = __builtin_amdgcn_readfirstlane(lst[kMaxSparse + kListPad]);
+  }
+  // first query row of ring position n, and whether this wave's slice takes part
+  auto row0_of = [&](int n) __attribute__((always_inline)) {
+    if constexpr (Sparse) return (__builtin_amdgcn_readfirstlane(lst[n]) & 0xffffff) * kBlk;
+    else return (blk0 + n) * kBlk;
+  };
+  auto wave_in = [&](int n) __attribute__((always_inline)) {
+    if constexpr (Sparse) return ((__builtin_amdgcn_readfirstlane(lst[n]) >> (24 + wave)) & 1) != 0;
+    else return true;
+  };
 
   const int wkey0 = k0 + kBlk * wave;   // this wave's first key
   const int key = wkey0 + (lane & 31);
@@ -475,9 +578,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
     m_rs = rsrc(dm.bits + (size_t)b * dm.sb + (size_t)(bh - b * H) * dm.sh, (uint32_t)N_q * dm.rw * 4);
     m_off = lane < 32 ? (uint32_t)lane * dm.rw * 4 + (uint32_t)(wkey0 >> 5) * 4 : 0x40000000u;
   }
-  auto issue = [&](int n) {   // block n (rows (blk0 + n)*32 ..) into stage n % kDepthKV
+  auto issue = [&](int n) {   // the block of ring position n into stage n % kDepthKV
     const uint32_t st = lds0 + (uint32_t)(n % kDepthKV) * kStage;
-    const uint32_t r0 = (uint32_t)(blk0 + n) * kBlk;
+    const uint32_t r0 = (uint32_t)row0_of(n);
 #pragma unroll
     for (int i = 0; i < R::kCpw; ++i) {
       const int ci = wave * R::kCpw + i;
@@ -524,13 +627,14 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
   // rows exist and are past q_start, and (causal) the block starts at or
   // after the wave's last key
   auto block_full = [&](int n) {
-    const int r0 = (blk0 + n) * kBlk;
-    return wkey_live && r0 + kBlk <= N_q && r0 >= qs && (!causal || r0 + coff >= wkey0 + kBlk - 1);
+    const int r0 = row0_of(n);
+    return wkey_live && r0 + kBlk <= N_q && r0 >= qs && (!causal || r0 + coff >= wkey0 + kBlk - 1) && wave_in(n);
   };
   auto softmax_grad = [&](auto full_t, int n, const f32x16& s, const f32x16& dp, uint32_t (&wp)[8],
                           uint32_t (&wd)[8]) __attribute__((always_inline)) {
     constexpr bool full = decltype(full_t)::value;
-    const int r0 = (blk0 + n) * kBlk;
+    const int r0 = row0_of(n);
+    [[maybe_unused]] const bool in = wave_in(n);
     const char* sb = stage_of(n) + 2 * R::kBlkBytes;
     [[maybe_unused]] const char* mb = sb + 1024 + wave * 256;   // Dense: word of row r0 + t at 4*t
 #pragma unroll
@@ -553,6 +657,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
           const int r = 4 * g + e;
           const int qrow = r0 + 8 * g + 4 * hf + e;
           bool ok = key_live && qrow < N_q && qrow >= qs && (!causal || key <= qrow + coff);
+          if constexpr (Sparse) ok = ok && in;
           if constexpr (Dense)
             ok = ok && ((*(const __attribute__((address_space(3))) uint32_t*)(mb + 4 * (8 * g + 4 * hf + e)) >>
                          (lane & 31)) & 1u);
@@ -654,7 +759,8 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 int bwd_launch(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                void* dq, void* dk, void* dv, float* delta, int B, int H, int N_q, int N_k, int d, float scale,
-               int causal, const int32_t* seqlens_k, const int32_t* q_start, DenseMask dm, hipStream_t stream) {
+               int causal, const int32_t* seqlens_k, const int32_t* q_start, DenseMask dm, BlockMask bmk,
+               hipStream_t stream) {
   if (B < 0 || H < 0 || N_q < 0 || N_k < 0) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
@@ -701,19 +807,23 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
     e = attn_launch::launch(d == 128 ? attn_bwd_delta_kernel<128> : attn_bwd_delta_kernel<64>, dim3((unsigned)nb),
                             dim3(256), stream, op, gp, lse, stp, rows);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
-    const bool dense = dm.bits != nullptr;
-    auto kq = d == 128 ? (dense ? attn_bwd_dq_kernel<128, true> : attn_bwd_dq_kernel<128, false>)
-                       : (dense ? attn_bwd_dq_kernel<64, true> : attn_bwd_dq_kernel<64, false>);
+    const int mode = dm.bits ? 1 : bmk.flags ? 2 : 0;
+    auto kq = d == 128 ? (mode == 1 ? attn_bwd_dq_kernel<128, 1> : mode == 2 ? attn_bwd_dq_kernel<128, 2>
+                                                                             : attn_bwd_dq_kernel<128, 0>)
+                       : (mode == 1 ? attn_bwd_dq_kernel<64, 1> : mode == 2 ? attn_bwd_dq_kernel<64, 2>
+                                                                            : attn_bwd_dq_kernel<64, 0>);
     e = attn_launch::launch(kq, dim3((unsigned)(bh * n_qt)), dim3(kThreads), stream, qp, kp, vp, gp, (const f32x2*)stp,
-                            dqp, Hi, Nq, Nk, cc, sc, causal01, coff, seqlens_k, q_start, (int)n_qt, dm);
+                            dqp, Hi, Nq, Nk, cc, sc, causal01, coff, seqlens_k, q_start, (int)n_qt, dm, bmk);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
   }
   if (has_k) {
-    const bool dense = dm.bits != nullptr;
-    auto kk = d == 128 ? (dense ? attn_bwd_dkdv_kernel<128, true> : attn_bwd_dkdv_kernel<128, false>)
-                       : (dense ? attn_bwd_dkdv_kernel<64, true> : attn_bwd_dkdv_kernel<64, false>);
+    const int mode = dm.bits ? 1 : bmk.flags ? 2 : 0;
+    auto kk = d == 128 ? (mode == 1 ? attn_bwd_dkdv_kernel<128, 1> : mode == 2 ? attn_bwd_dkdv_kernel<128, 2>
+                                                                               : attn_bwd_dkdv_kernel<128, 0>)
+                       : (mode == 1 ? attn_bwd_dkdv_kernel<64, 1> : mode == 2 ? attn_bwd_dkdv_kernel<64, 2>
+                                                                              : attn_bwd_dkdv_kernel<64, 0>);
     e = attn_launch::launch(kk, dim3((unsigned)(bh * n_kt)), dim3(kThreads), stream, qp, kp, vp, gp, (const f32x2*)stp,
-                            dkp, dvp, Hi, Nq, Nk, cc, sc, causal01, coff, seqlens_k, q_start, (int)n_kt, dm);
+                            dkp, dvp, Hi, Nq, Nk, cc, sc, causal01, coff, seqlens_k, q_start, (int)n_kt, dm, bmk);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
   }
   return ATTN_OK;
@@ -726,7 +836,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
                         int N_k, int d, float scale, int causal, const int32_t* seqlens_k,
                         const int32_t* q_start, hipStream_t stream) {
   return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N_q, N_k, d, scale, causal, seqlens_k, q_start,
-                    DenseMask{nullptr, 0, 0, 0}, stream);
+                    DenseMask{nullptr, 0, 0, 0}, BlockMask{nullptr, 0, 0, 0}, stream);
 }
 
 extern "C" int attn_bwd_masked(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -742,5 +852,21 @@ extern "C" int attn_bwd_masked(const void* q, const void* k, const void* v, cons
     return ATTN_ERR_MASK;
   if ((long long)(N_q + kTile) * mask_row_words * 4 > 0x7fffffffLL) return ATTN_ERR_SHAPE;   // 32-bit offsets
   return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N_q, N_k, d, scale, causal, seqlens_k, q_start,
-                    DenseMask{mask_bits, mask_stride_b, mask_stride_h, mask_row_words}, stream);
+                    DenseMask{mask_bits, mask_stride_b, mask_stride_h, mask_row_words}, BlockMask{nullptr, 0, 0, 0},
+                    stream);
+}
+
+extern "C" int attn_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                     const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H,
+                                     int N_q, int N_k, int d, float scale, int causal, const int32_t* seqlens_k,
+                                     const int32_t* q_start, const uint8_t* block_mask, long long block_stride_b,
+                                     long long block_stride_h, hipStream_t stream) {
+  if (B < 0 || H < 0 || N_q < 0 || N_k < 0) return ATTN_ERR_SHAPE;
+  const bool work = (long long)B * H > 0 && (N_q > 0 || N_k > 0);
+  if (!block_mask) return work ? ATTN_ERR_NULL : ATTN_OK;
+  if (block_stride_b < 0 || block_stride_h < 0) return ATTN_ERR_MASK;
+  const int n_ks = (N_k + kBlk - 1) / kBlk;
+  if (n_ks > kMaxSparse || (N_q + kBlk - 1) / kBlk > kMaxSparse) return ATTN_ERR_SHAPE;   // the lists' capacity
+  return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N_q, N_k, d, scale, causal, seqlens_k, q_start,
+                    DenseMask{nullptr, 0, 0, 0}, BlockMask{block_mask, block_stride_b, block_stride_h, n_ks}, stream);
 }
