@@ -134,7 +134,7 @@ def main():
                     help="forward with a dense boolean mask (attn_fwd_masked): key j visible to row i iff "
                          "i - W < j <= i, one mask shared by all heads, packed once before the timed region")
     ap.add_argument("--block-density", type=float, default=0.0, metavar="P",
-                    help="block-sparse forward (attn_fwd_block_sparse): each (256-row tile, 32-key slice) block "
+                    help="block-sparse forward (attn_fwd_block_sparse): each (256-row, 128-key) block "
                          "kept with probability P (seeded, shared by all heads); value counts the kept blocks' work")
     ap.add_argument("--backward", action="store_true",
                     help="time attn_bwd (dQ, dK, dV; its three launches) instead of the forward; O and LSE come "
@@ -174,21 +174,22 @@ def main():
             sets.append(tuple(t.clone() for t in sets[0][:3]) + (torch.empty_like(q), torch.empty_like(sets[0][4])))
     stream = torch.cuda.current_stream(dev)
     n_step = [0]
-    if args.backward:
-        return bench_backward(args, torch, ta, w, inp, sets[0], sl, qs, stream, dev)
-
     packed = None
     bmask = None
     if args.block_density:
-        nqb, nkb = -(-w.N_q // 256), -(-w.N_k // 32)
+        nqb, nkb = -(-w.N_q // 256), -(-w.N_k // 128)
         keep = np.random.default_rng(w.seed + 700).random((1, 1, nqb, nkb)) < args.block_density
         bmask = torch.from_numpy(keep).to(dev)
         # counted flops of the kept blocks: allowed (row, key) pairs inside kept blocks
         i = np.arange(w.N_q)[:, None]
         j = np.arange(w.N_k)[None, :]
         allowed = (j <= i) if w.causal else np.ones((w.N_q, w.N_k), bool)
-        kept = keep[0, 0][np.arange(w.N_q) // 256][:, np.arange(w.N_k) // 32]
+        kept = keep[0, 0][np.arange(w.N_q) // 256][:, np.arange(w.N_k) // 128]
         sparse_frac = float((allowed & kept).sum()) / float(allowed.sum())
+    if args.backward:
+        return bench_backward(args, torch, ta, w, inp, sets[0], sl, qs, stream, dev, bmask,
+                              sparse_frac if args.block_density else 1.0)
+
     if args.window:
         i = torch.arange(w.N_q, device=dev)[:, None]
         j = torch.arange(w.N_k, device=dev)[None, :]
@@ -266,7 +267,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def bench_backward(args, torch, ta, w, inp, tensors, sl, qs, stream, dev):
+def bench_backward(args, torch, ta, w, inp, tensors, sl, qs, stream, dev, bmask=None, kept=1.0):
     """Time the backward pass: a step is one attn_bwd call (Delta, dQ, dK/dV kernels)."""
     from workloads import make_dout
 
@@ -274,13 +275,13 @@ def bench_backward(args, torch, ta, w, inp, tensors, sl, qs, stream, dev):
     g = torch.from_numpy(make_dout((w.B, w.H, w.N_q, w.d), seed=w.seed + 500).view(np.int16)).to(dev).view(
         torch.bfloat16)
     ta.attn_fwd(q, k, v, causal=w.causal, scale=float(inp.scale), seqlens_k=sl, q_start=qs, out=o, lse=lse,
-                stream=stream)
+                stream=stream, block_mask=bmask)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty((w.B, w.H, w.N_q, 2), dtype=torch.float32, device=dev)
 
     def step():
         ta.attn_bwd(q, k, v, o, lse, g, causal=w.causal, scale=float(inp.scale), seqlens_k=sl, q_start=qs, dq=dq,
-                    dk=dk, dv=dv, delta=delta, stream=stream)
+                    dk=dk, dv=dv, delta=delta, stream=stream, block_mask=bmask)
 
     for _ in range(args.warmup):
         step()
@@ -294,16 +295,19 @@ def bench_backward(args, torch, ta, w, inp, tensors, sl, qs, stream, dev):
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
     ms = e_start.elapsed_time(e_end) / args.steps
-    flops = 2.5 * w.flops()   # five N_q x N_k x d products (S, dP, dV, dK, dQ) against the forward's two
+    flops = 2.5 * w.flops() * kept   # five N_q x N_k x d products (S, dP, dV, dK, dQ) against the forward's two
     tflops = flops / (ms * 1e-3) / 1e12
     result = {
         "metric": BWD_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.N_q, "N_k": w.N_k, "d": w.d, "causal": w.causal,
-                   "varlen": inp.seqlens_k is not None, "pass": "backward"},
+                   "varlen": inp.seqlens_k is not None, "pass": "backward",
+                   **({"block_sparse": f"density {args.block_density}, kept fraction {kept:.3f}"}
+                      if bmask is not None else {})},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_bwd_traffic(w.name)},
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_bwd_traffic(w.name) if bmask is None else None},
         "launch_ms": {"mean": round(ms, 5)},
         "wall_s_timed": round(wall, 4),
     }

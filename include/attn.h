@@ -128,10 +128,10 @@ int attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float*
  * neither loaded nor computed, and their keys get probability 0.
  *
  *   block_mask       uint8 device array, read only: for batch b, head h, query
- *                    tile t (rows 256*t .. 256*t+255) and key slice s (keys
- *                    32*s .. 32*s+31) the byte block_mask[b*block_stride_b +
- *                    h*block_stride_h + t*ceil(N_k/32) + s]; nonzero = compute
- *                    the block. Rows of ceil(N_k/32) bytes, ceil(N_q/256) rows
+ *                    tile t (rows 256*t .. 256*t+255) and key block s (keys
+ *                    128*s .. 128*s+127) the byte block_mask[b*block_stride_b +
+ *                    h*block_stride_h + t*ceil(N_k/128) + s]; nonzero = compute
+ *                    the block. Rows of ceil(N_k/128) bytes, ceil(N_q/256) rows
  *                    per (b, h).
  *   block_stride_b,  byte strides between batches and heads (>= 0; 0 broadcasts).
  *   block_stride_h

@@ -248,8 +248,8 @@ def test_bwd_block_sparse(case):
     q, k, v = make_random(B, H, nq, nk, d, seed=nq + 19 * nk + d)
     g = make_dout((B, H, nq, d), seed=nq + 23 * nk)
     rng = np.random.default_rng(nq + 29 * nk)
-    bm = rng.random((mb, mh, -(-nq // 256), -(-nk // 32))) < dens
-    bm[..., 1] = False                          # keys 32..63 in no kept block: dK = dV = 0
+    bm = rng.random((mb, mh, -(-nq // 256), -(-nk // 128))) < dens
+    bm[..., 1] = False                          # keys 128..255 in no kept block: dK = dV = 0
     scale = np.float32(d ** -0.5)
     print(f"  block-sparse bwd {case}", flush=True)
     tq, tk, tv, tg = to_dev(q), to_dev(k), to_dev(v), to_dev(g)
@@ -259,8 +259,8 @@ def test_bwd_block_sparse(case):
     torch.cuda.synchronize()
     dq, dk, dv = f64(dq), f64(dk), f64(dv)
     rq, rk, rv = attention_bwd(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), bf16_bits_to_f64(g),
-                               float(scale), causal, attn_mask=expand_block_mask(bm, nq, nk, 256, 32))
+                               float(scale), causal, attn_mask=expand_block_mask(bm, nq, nk, 256, 128))
     r = check_grads({"dq": dq, "dk": dk, "dv": dv}, {"dq": rq, "dk": rk, "dv": rv})
     print("  ", r, flush=True)
     assert r.ok, str(r)
-    assert np.all(dk[:, :, 32:64] == 0) and np.all(dv[:, :, 32:64] == 0)
+    assert np.all(dk[:, :, 128:256] == 0) and np.all(dv[:, :, 128:256] == 0)

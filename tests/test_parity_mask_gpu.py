@@ -156,7 +156,7 @@ def test_block_sparse(case):
     B, H, nq, nk, d, causal, (mb, mh), dens, sl, qs = case
     q, k, v = make_random(B, H, nq, nk, d, seed=nq + 13 * nk + d)
     rng = np.random.default_rng(nq + 17 * nk)
-    nqb, nkb = -(-nq // 256), -(-nk // 32)
+    nqb, nkb = -(-nq // 256), -(-nk // 128)
     bm = rng.random((mb, mh, nqb, nkb)) < dens
     bm[0, 0, 0, :] = False                    # a tile with no block at all: its rows output 0
     scale = np.float32(d ** -0.5)
@@ -169,7 +169,7 @@ def test_block_sparse(case):
     o, lse = f64(o), lse.cpu().numpy().astype(np.float64)
     ro, rl = attention(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), float(scale), causal,
                        seqlens_k=None if sl is None else np.array(sl), q_start=None if qs is None else np.array(qs),
-                       attn_mask=expand_block_mask(bm, nq, nk, 256, 32))
+                       attn_mask=expand_block_mask(bm, nq, nk, 256, 128))
     r = check(o, ro, lse, rl)
     print("  ", r, flush=True)
     assert r.ok, str(r)
@@ -180,7 +180,7 @@ def test_block_sparse_all_kept_equals_plain():
     import tiled_attention_16_amd as ta
     q, k, v = make_random(1, 2, 700, 700, 128, seed=111)
     tq, tk, tv = to_dev(q), to_dev(k), to_dev(v)
-    bm = torch.ones((1, 1, 3, 22), dtype=torch.bool, device="cuda")
+    bm = torch.ones((1, 1, 3, 6), dtype=torch.bool, device="cuda")
     o1, l1 = ta.attn_fwd(tq, tk, tv, causal=True)
     o2, l2 = ta.attn_fwd(tq, tk, tv, causal=True, block_mask=bm)
     torch.cuda.synchronize()
@@ -193,13 +193,13 @@ def test_block_sparse_full_size_sampled():
     from oracle import expand_block_mask
     w = WORKLOADS["causal_n4096_d128"]
     inp = make_inputs(w)
-    bm = np.random.default_rng(7).random((1, 1, 16, 128)) < 0.5
+    bm = np.random.default_rng(7).random((1, 1, 16, 32)) < 0.5
     o, lse = ta.attn_fwd(to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), causal=True, scale=float(inp.scale),
                          block_mask=torch.from_numpy(bm).cuda())
     torch.cuda.synchronize()
     o, lse = f64(o), lse.cpu().numpy().astype(np.float64)
     rows = np.unique(np.concatenate([[0, 255, 256, 2047, 4095], np.random.default_rng(8).choice(4096, 40, replace=False)]))
-    full = expand_block_mask(bm, 4096, 4096, 256, 32)
+    full = expand_block_mask(bm, 4096, 4096, 256, 128)
     for b, h in [(0, 0), (0, 31)]:
         ro, rl = attention(bf16_bits_to_f64(inp.q[b:b + 1, h:h + 1]), bf16_bits_to_f64(inp.k[b:b + 1, h:h + 1]),
                            bf16_bits_to_f64(inp.v[b:b + 1, h:h + 1]), float(inp.scale), True, rows=rows, attn_mask=full)

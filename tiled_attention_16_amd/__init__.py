@@ -42,7 +42,7 @@ EXPORTS = ("attn_bwd", "attn_bwd_block_sparse", "attn_bwd_masked", "attn_fwd", "
            "attn_fwd_masked", "attn_mask_pack", "attn_status_str", "attn_version")
 
 SPARSE_BLOCK_Q = 256   # query rows per block of attn_fwd_block_sparse's block mask
-SPARSE_BLOCK_K = 32    # keys per block
+SPARSE_BLOCK_K = 128   # keys per block
 
 _lib = None
 
@@ -168,7 +168,7 @@ def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None, se
     bool GPU tensor ``[B or 1, H or 1, N_q, N_k]``, True = may attend,
     intersected with the other rules (packed by the library on each call;
     pass ``packed_mask=pack_mask(m)`` to pack once). ``block_mask``: optional
-    bool/uint8 GPU tensor ``[B or 1, H or 1, ceil(N_q/256), ceil(N_k/32)]``;
+    bool/uint8 GPU tensor ``[B or 1, H or 1, ceil(N_q/256), ceil(N_k/128)]``;
     only the blocks it keeps are computed (``attn_fwd_block_sparse``).
     Returns ``(o, lse)``; ``lse`` is None unless ``return_lse``. ``scale``
     defaults to ``d ** -0.5``. ``seqlens_k`` / ``q_start`` are optional int32

@@ -174,7 +174,7 @@ struct DenseMask {
 };
 
 // Block mask of attn_fwd_block_sparse: a byte per (256-row query tile,
-// 32-key slice), rows of n_ks bytes, matrix (b, h) at byte b*sb + h*sh.
+// 128-key block), rows of n_ks bytes, matrix (b, h) at byte b*sb + h*sh.
 struct BlockMask {
   const uint8_t* flags;
   long long sb, sh;
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int sl = 16 * lane + i;
-        if (sl < nblk && fl[sl] != 0) bits |= 1u << i;
+        if (sl < nblk && fl[sl >> 2] != 0) bits |= 1u << i;   // a flag covers 4 slices (128 keys)
       }
       const int cnt = __builtin_popcount(bits);
       int incl = cnt;
@@ -453,10 +453,10 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
 // ---------------------------------------------------------------- dk, dv
 // Dense: as in the dQ kernel; each wave copies, per block, the words of the
 // block's 32 rows that hold its own 32 keys.
-// Mode 2 (Sparse): the WG walks the 32-row query blocks of every 256-row
-// block-mask tile that keeps the slice of at least one of its waves; each
-// list entry carries the block and a 4-bit mask of the waves whose slice the
-// tile keeps (the others take no part in that block).
+// Mode 2 (Sparse): the WG's 128 keys are one key block of the mask; it walks
+// the 32-row query blocks of the 256-row tiles that keep that block. Each
+// list entry carries the query block and a mask of the waves that take part
+// (all of them: the key block is the WG's).
 template <int D, int Mode>   // 0: rules only; 1: dense mask (Dense); 2: block-sparse (Sparse)
 __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -501,14 +501,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
       int base = 0;
       for (int t0 = blk0 / 8; t0 * 8 < nbq && nblk > 0; t0 += 64) {   // 256-row tiles, one per lane
         const int t = t0 + lane;
+        // the WG's 128 keys are one block of the mask: all its waves take part or none
         uint32_t wm = 0;
-        if (t * 8 < nbq) {
-#pragma unroll
-          for (int w = 0; w < kWaves; ++w) {
-            const int sl = (k0 >> 5) + w;
-            if (sl < bmk.n_ks && fl[(size_t)t * bmk.n_ks + sl] != 0) wm |= 1u << w;
-          }
-        }
+        if (t * 8 < nbq && fl[(size_t)t * bmk.n_ks + kt] != 0) wm = (1u << kWaves) - 1;
         const int lo = max(8 * t, blk0), hi = min(8 * t + 8, nbq);
         const int cnt = (wm != 0 && hi > lo) ? hi - lo : 0;
         int incl = cnt;
@@ -865,8 +860,8 @@ extern "C" int attn_bwd_block_sparse(const void* q, const void* k, const void* v
   const bool work = (long long)B * H > 0 && (N_q > 0 || N_k > 0);
   if (!block_mask) return work ? ATTN_ERR_NULL : ATTN_OK;
   if (block_stride_b < 0 || block_stride_h < 0) return ATTN_ERR_MASK;
-  const int n_ks = (N_k + kBlk - 1) / kBlk;
-  if (n_ks > kMaxSparse || (N_q + kBlk - 1) / kBlk > kMaxSparse) return ATTN_ERR_SHAPE;   // the lists' capacity
+  if ((N_k + kBlk - 1) / kBlk > kMaxSparse || (N_q + kBlk - 1) / kBlk > kMaxSparse) return ATTN_ERR_SHAPE;   // lists
+  const int n_ks = (N_k + kTile - 1) / kTile;   // 128-key blocks per row of the block mask
   return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N_q, N_k, d, scale, causal, seqlens_k, q_start,
                     DenseMask{nullptr, 0, 0, 0}, BlockMask{block_mask, block_stride_b, block_stride_h, n_ks}, stream);
 }

@@ -198,8 +198,9 @@ __device__ __forceinline__ void wait_copies() {
 // Each wave copies its rows' words for the next 8 slices into LDS with one
 // buffer_load ... lds per 8 steps; every slice is masked.
 // Sparse (block-sparse attention, [MEMWALL] §7): a byte per (256-row query
-// tile, 32-key slice) says whether the slice is computed for that tile at
-// all (rows of n_ks bytes, matrix (b, h) at byte b*bsb + h*bsh). At each tile
+// tile, 128-key block, i.e. 4 slices) says whether the block is computed for
+// that tile at all (rows of n_ks bytes, n_ks = ceil(N_k / 128), matrix (b, h)
+// at byte b*bsb + h*bsh). At each tile
 // start wave 0 compacts the tile's set flags into a list of slice indices in
 // LDS; the ring walks that list, so unset slices cost neither copies nor
 // arithmetic. The rules still mask inside the slices that are computed.
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int sl = 16 * lane + i;
-        if (sl < nsl && fl[sl] != 0) bits |= 1u << i;
+        if (sl < nsl && fl[sl >> 2] != 0) bits |= 1u << i;   // a flag covers 4 slices (128 keys)
       }
       const int cnt = __builtin_popcount(bits);
       int incl = cnt;   // inclusive prefix sum over the wave
@@ -973,12 +974,12 @@ extern "C" int attn_fwd_block_sparse(const void* q, const void* k, const void* v
                                      const int32_t* q_start, const uint8_t* block_mask, long long block_stride_b,
                                      long long block_stride_h, hipStream_t stream) {
   if (B < 0 || H < 0 || N_q < 0 || N_k < 0) return ATTN_ERR_SHAPE;
-  const int n_ks = (N_k + kSlice - 1) / kSlice;
+  const int n_ks = (N_k + 4 * kSlice - 1) / (4 * kSlice);   // 128-key blocks per row of the block mask
   if ((long long)B * H * N_q == 0)
     return fwd_launch(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, seqlens_k, q_start, nullptr, 0, 0, 0, nullptr,
                       0, 0, 0, stream);
   if (!block_mask) return ATTN_ERR_NULL;
-  if (n_ks > kMaxSparseSlices) return ATTN_ERR_SHAPE;
+  if ((N_k + kSlice - 1) / kSlice > kMaxSparseSlices) return ATTN_ERR_SHAPE;
   if (block_stride_b < 0 || block_stride_h < 0) return ATTN_ERR_MASK;
   return fwd_launch(q, k, v, o, lse, B, H, N_q, N_k, d, scale, causal, seqlens_k, q_start, nullptr, 0, 0, 0,
                     block_mask, block_stride_b, block_stride_h, n_ks, stream);
