@@ -598,22 +598,25 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
   f32x16 adk[D / 32], adv[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) adk[db] = adv[db] = (f32x16){};
-  // S = Q K^T and dP = dO V^T of the block in stage qb
-  auto sdp = [&](const char* qb, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
+  // S = Q K^T and dP = dO V^T of the block in stage qb: all A operands are
+  // read first (before the full/masked branch of the loop, so the MFMAs in
+  // either branch only count the reads down), then the products
+  using Rows = bf16x8[D / 16];
+  auto sdp_read = [&](const char* qb, Rows& qa, Rows& ga) __attribute__((always_inline)) {
     const char* gb = qb + R::kBlkBytes;
-    s = (f32x16){};
-    dp = (f32x16){};
-    bf16x8 qa[2], ga[2];   // operands read one step ahead of their MFMAs
-    qa[0] = read_row<D>(qb, off, 0);
-    ga[0] = read_row<D>(gb, off, 0);
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) {
-      if (kc + 1 < D / 16) {
-        qa[(kc + 1) & 1] = read_row<D>(qb, off, kc + 1);
-        ga[(kc + 1) & 1] = read_row<D>(gb, off, kc + 1);
-      }
-      s = mfma(qa[kc & 1], kr[kc], s);
-      dp = mfma(ga[kc & 1], vr[kc], dp);
+      qa[kc] = read_row<D>(qb, off, kc);
+      ga[kc] = read_row<D>(gb, off, kc);
+    }
+  };
+  auto sdp = [&](const Rows& qa, const Rows& ga, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
+    s = (f32x16){};
+    dp = (f32x16){};
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) {
+      s = mfma(qa[kc], kr[kc], s);
+      dp = mfma(ga[kc], vr[kc], dp);
     }
   };
   // P and dS of block n from its S and dP, packed as the B operands of the
@@ -623,7 +626,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
   // after the wave's last key
   auto block_full = [&](int n) {
     const int r0 = row0_of(n);
-    return wkey_live && r0 + kBlk <= N_q && r0 >= qs && (!causal || r0 + coff >= wkey0 + kBlk - 1) && wave_in(n);
+    // one condition (bitwise, not short-circuit): a single branch lets the
+    // operand reads placed before it stay there
+    return wkey_live & (r0 + kBlk <= N_q) & (r0 >= qs) & (!causal | (r0 + coff >= wkey0 + kBlk - 1)) & wave_in(n);
   };
   auto softmax_grad = [&](auto full_t, int n, const f32x16& s, const f32x16& dp, uint32_t (&wp)[8],
                           uint32_t (&wd)[8]) __attribute__((always_inline)) {
@@ -706,7 +711,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
     for (int n = 0; n < kDepthKV - 1; ++n) issue(n);
     wait_block(std::integral_constant<int, kDepthKV - 2>{});   // block 0
     __syncthreads();
-    sdp(stage_of(0), s_cur, dp_cur);
+    Rows qa, ga;
+    sdp_read(stage_of(0), qa, ga);
+    sdp(qa, ga, s_cur, dp_cur);
   }
   for (int n = 0; n < nblk; ++n) {
     wait_block(std::integral_constant<int, kDepthKV - 3>{});   // block n+1
@@ -716,12 +723,14 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
     // fetched nothing: finite values, discarded)
     f32x16 s_nxt, dp_nxt;
     uint32_t wp[8], wd[8];
+    Rows qa, ga;
+    sdp_read(stage_of(n + 1), qa, ga);
     if (!Dense && block_full(n)) {
-      sdp(stage_of(n + 1), s_nxt, dp_nxt);
+      sdp(qa, ga, s_nxt, dp_nxt);
       softmax_grad(std::true_type{}, n, s_cur, dp_cur, wp, wd);
       interleave(std::integral_constant<int, 6>{});
     } else {
-      sdp(stage_of(n + 1), s_nxt, dp_nxt);
+      sdp(qa, ga, s_nxt, dp_nxt);
       softmax_grad(std::false_type{}, n, s_cur, dp_cur, wp, wd);
       interleave(std::integral_constant<int, 10>{});
     }
