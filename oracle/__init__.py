@@ -17,8 +17,13 @@ Parity status of each function (what pins it, all in ``tests/test_oracle.py``):
                     zero gradients for dO = 0 and for V with equal rows, the
                     Q = 0 closed form of dV, torch CPU fp64 autograd cross-check.
   check_grads       pinned by planted mistakes (NaN, out of band).
+  e4m3_decode       pinned (tests/test_oracle_fp8.py): the format's defining
+                    values, monotonicity, torch float8_e4m3fn cross-check.
+  attention_fp8     pinned: pure-Python brute force on tiny inputs, closed
+                    forms (Q = 0, equal V rows), descale invariances.
 """
 from .attention import (allowed_mask, attention, attention_online, bf16_bits_to_f64, causal_offset,  # noqa: F401
                         expand_block_mask)
 from .backward import attention_bwd  # noqa: F401
+from .fp8 import attention_fp8, e4m3_decode  # noqa: F401
 from .checker import check, check_grads, CheckResult, GradCheckResult  # noqa: F401

@@ -43,6 +43,7 @@ def test_pins_catch_planted_mistake(tmp_path, desc, old, new):
     (tmp_path / "tests").mkdir()
     shutil.copy(os.path.join(HERE, "test_oracle.py"), tmp_path / "tests")
     shutil.copytree(os.path.join(HERE, "golden"), tmp_path / "tests" / "golden")
+    shutil.copy(os.path.join(ROOT, "workloads.py"), tmp_path)
     (tmp_path / "tests" / "conftest.py").write_text(
         "import os, sys\nsys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))\n")
     # only the pins of the two-pass definition; the online recurrence is a separate function
@@ -82,14 +83,49 @@ def test_backward_pins_catch_planted_mistake(tmp_path, desc, old, new):
     assert res.returncode != 0, f"no pin caught the planted mistake '{desc}'"
 
 
+# (description, literal text in oracle/fp8.py, replacement)
+FP8_MUTANTS = [
+    ("exponent bias 8", "np.ldexp(1.0 + m / 8.0, e - 7)", "np.ldexp(1.0 + m / 8.0, e - 8)"),
+    ("no implicit leading one", "np.ldexp(1.0 + m / 8.0, e - 7)", "np.ldexp(m / 8.0, e - 7)"),
+    ("subnormal scale of a normal", "np.ldexp(m / 8.0, -6)", "np.ldexp(m / 8.0, -7)"),
+    ("sign ignored", "out = np.where(s == 1, -mag, mag)", "out = mag"),
+    ("S.1111.xxx all NaN", "(e == 15) & (m == 7)", "(e == 15)"),
+    ("V not transposed", "v = np.swapaxes(e4m3_decode(vt8), -1, -2) * np.float64(v_descale)",
+     "v = e4m3_decode(vt8).reshape(vt8.shape[:2] + (vt8.shape[3], vt8.shape[2])) * np.float64(v_descale)"),
+    ("v_descale dropped", "v = np.swapaxes(e4m3_decode(vt8), -1, -2) * np.float64(v_descale)",
+     "v = np.swapaxes(e4m3_decode(vt8), -1, -2)"),
+    ("k_descale as q_descale", "k = e4m3_decode(k8) * np.float64(k_descale)",
+     "k = e4m3_decode(k8) * np.float64(q_descale)"),
+]
+
+
+@pytest.mark.parametrize("desc,old,new", FP8_MUTANTS, ids=[m[0] for m in FP8_MUTANTS])
+def test_fp8_pins_catch_planted_mistake(tmp_path, desc, old, new):
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle")
+    shutil.copy(os.path.join(ROOT, "workloads.py"), tmp_path)
+    src = (tmp_path / "oracle" / "fp8.py").read_text(encoding="utf-8")
+    assert old in src, f"mutation site for '{desc}' not found"
+    (tmp_path / "oracle" / "fp8.py").write_text(src.replace(old, new, 1), encoding="utf-8")
+    (tmp_path / "tests").mkdir()
+    shutil.copy(os.path.join(HERE, "test_oracle_fp8.py"), tmp_path / "tests")
+    (tmp_path / "tests" / "conftest.py").write_text(
+        "import os, sys\nsys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))\n")
+    res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                          "tests/test_oracle_fp8.py", "-k", "not torch and not generator"],
+                         cwd=tmp_path, capture_output=True, text=True, timeout=300)
+    assert res.returncode != 0, f"no pin caught the planted mistake '{desc}'"
+
+
 @pytest.mark.parametrize("module,test_file,select", [("attention.py", "test_oracle.py", "not online"),
-                                                      ("backward.py", "test_oracle_bwd.py", "not checker")])
+                                                      ("backward.py", "test_oracle_bwd.py", "not checker"),
+                                                      ("fp8.py", "test_oracle_fp8.py", "not torch and not generator")])
 def test_unmutated_copy_passes(tmp_path, module, test_file, select):
     """Control for the two tests above: the same harness passes the oracle as it is."""
     shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle")
     (tmp_path / "tests").mkdir()
     shutil.copy(os.path.join(HERE, test_file), tmp_path / "tests")
     shutil.copytree(os.path.join(HERE, "golden"), tmp_path / "tests" / "golden")
+    shutil.copy(os.path.join(ROOT, "workloads.py"), tmp_path)
     (tmp_path / "tests" / "conftest.py").write_text(
         "import os, sys\nsys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))\n")
     res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",

@@ -166,3 +166,37 @@ def make_dout(shape, seed: int, sigma: float = 1.0):
     backward pass's extra input): iid N(0, sigma^2), drawn after nothing else."""
     g = np.random.Generator(np.random.PCG64(seed))
     return f32_to_bf16_bits(g.standard_normal(tuple(shape), dtype=np.float32) * np.float32(sigma))
+
+
+@dataclass
+class Fp8Inputs:
+    q8: np.ndarray          # uint8 E4M3 codes [B, H, N_q, d]
+    k8: np.ndarray          # [B, H, N_k, d]
+    vt8: np.ndarray         # V transposed: [B, H, d, N_k]
+    q_descale: float
+    k_descale: float
+    v_descale: float
+
+
+def make_fp8(B: int, H: int, N_q: int, N_k: int, d: int, seed: int, sigma=(1.0, 1.0, 1.0)) -> Fp8Inputs:
+    """Seeded OCP E4M3 Q, K, V codes with one descale per tensor.
+
+    Same draws as ``make_random`` (float32 normals times sigma, Q then K then
+    V); each tensor is divided by amax / 448 (448 = the largest E4M3 value) and
+    rounded to E4M3 by torch's float8_e4m3fn conversion; its descale is
+    amax / 448. V is returned transposed, key index fastest.
+    """
+    import torch
+
+    g = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for shape, s in (((B, H, N_q, d), sigma[0]), ((B, H, N_k, d), sigma[1]), ((B, H, N_k, d), sigma[2])):
+        x = g.standard_normal(shape, dtype=np.float32) * np.float32(s)
+        amax = float(np.abs(x).max()) if x.size else 1.0
+        ds = amax / 448.0 if amax > 0 else 1.0
+        y = np.clip(x.astype(np.float64) / ds, -448.0, 448.0).astype(np.float32)
+        codes = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        out.append((codes, ds))
+    (q8, qd), (k8, kd), (v8, vd) = out
+    vt8 = np.ascontiguousarray(np.swapaxes(v8, -1, -2))
+    return Fp8Inputs(q8=q8, k8=k8, vt8=vt8, q_descale=qd, k_descale=kd, v_descale=vd)
