@@ -223,6 +223,38 @@ int attn_bwd_block_sparse(const void* q, const void* k, const void* v, const voi
                           const uint8_t* block_mask, long long block_stride_b, long long block_stride_h,
                           hipStream_t stream);
 
+/*
+ * attn_fwd_fp8 - attention forward with FP8 (OCP E4M3) operands.
+ *
+ * The mixed-precision item of section 9 (future directions) of the
+ * codechina.net "GPU memory wall ... FlashAttention" article: both matrix
+ * products in FP8, accumulated in fp32 (the page names a 16-bit accumulator;
+ * fp32 is at least as precise). Computes, per (b, h) and query row i,
+ *   S_ij = scale * (q_descale * Q8_i) . (k_descale * K8_j),
+ *   O_i  = sum_j softmax_j(S_i) * v_descale * V8_j,   LSE_i = ln sum_j exp(S_ij),
+ * with the causal rules of attn_fwd (0 none, 1 top-left j <= i, 2 bottom-right
+ * j <= i + N_k - N_q); X8 is the tensor of decoded E4M3 codes. The
+ * probabilities are rounded to E4M3 (after multiplying by 2^8) before the
+ * second product; the sum that normalises them is the exact fp32 one.
+ *
+ *   q   device, [B, H, N_q, d] E4M3 bytes, 16-byte aligned.
+ *   k   device, [B, H, N_k, d] E4M3 bytes, 16-byte aligned.
+ *   vt  device, V transposed: [B, H, d, vt_row_stride] E4M3 bytes, 16-byte
+ *       aligned; row (b, h, c) holds V[b, h, j, c] for keys j = 0 .. N_k-1 at
+ *       byte j. vt_row_stride is a multiple of 16 and >= N_k rounded up to 16
+ *       (else ATTN_ERR_SHAPE); the bytes past N_k in a row are never used.
+ *   o   device, [B, H, N_q, d] bf16 output, 16-byte aligned.
+ *   lse device, [B, H, N_q] fp32 output, natural log, or NULL.
+ *   d   64 or 128. scale and the three descales must be finite (any sign).
+ * A row with no visible key outputs O = 0 and LSE = -inf. The library
+ * allocates nothing; one kernel launch on `stream`; argument errors are
+ * returned before any HIP call, as for attn_fwd (NULL, alignment, overlap of
+ * o or lse with an input or each other).
+ */
+int attn_fwd_fp8(const void* q, const void* k, const void* vt, long long vt_row_stride, void* o, float* lse,
+                 int B, int H, int N_q, int N_k, int d, float scale, float q_descale, float k_descale,
+                 float v_descale, int causal, hipStream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* attn_status_str(int status);
 

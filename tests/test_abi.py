@@ -200,3 +200,43 @@ def test_bwd_block_sparse_argument_errors(lib):
     assert lib.attn_bwd_block_sparse(*p, A16 * 40, 0, -2, None) == ta.ATTN_ERR_MASK
     p_long = p[:12] + [40000] + p[13:]
     assert lib.attn_bwd_block_sparse(*p_long, A16 * 40, 0, 0, None) == ta.ATTN_ERR_SHAPE
+
+
+def call_fp8(**kw):
+    args = dict(q=A16, k=A16 * 2, vt=A16 * 3, vt_row_stride=16, o=A16 * 4, lse=A16 * 5, B=1, H=2, N_q=8, N_k=8, d=64,
+                scale=0.125, q_descale=0.01, k_descale=0.02, v_descale=0.03, causal=False, stream=0)
+    args.update(kw)
+    return ta.attn_fwd_fp8_raw(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), ta.ATTN_ERR_SHAPE),
+    (dict(N_k=-1), ta.ATTN_ERR_SHAPE),
+    (dict(d=32), ta.ATTN_ERR_HEAD_DIM),
+    (dict(scale=float("nan")), ta.ATTN_ERR_SCALE),
+    (dict(q_descale=float("inf")), ta.ATTN_ERR_SCALE),
+    (dict(v_descale=float("nan")), ta.ATTN_ERR_SCALE),
+    (dict(scale=1e30, q_descale=1e30), ta.ATTN_ERR_SCALE),   # the product overflows
+    (dict(causal=3), ta.ATTN_ERR_MASK),
+    (dict(q=0), ta.ATTN_ERR_NULL),
+    (dict(vt=0), ta.ATTN_ERR_NULL),
+    (dict(o=0), ta.ATTN_ERR_NULL),
+    (dict(vt_row_stride=8), ta.ATTN_ERR_SHAPE),     # not a multiple of 16
+    (dict(N_k=17, vt_row_stride=16), ta.ATTN_ERR_SHAPE),   # shorter than N_k rounded up to 16
+    (dict(k=A16 * 2 + 4), ta.ATTN_ERR_ALIGN),
+    (dict(lse=A16 * 5 + 1), ta.ATTN_ERR_ALIGN),
+    (dict(o=A16 * 3), ta.ATTN_ERR_ALIAS),            # o on top of vt
+    (dict(lse=A16 * 4 + 32), ta.ATTN_ERR_ALIAS),     # lse inside o
+    (dict(B=1 << 20, H=1 << 12, N_q=1 << 12), ta.ATTN_ERR_SHAPE),
+])
+def test_fp8_argument_errors_return_before_any_hip_call(lib, kw, status):
+    assert call_fp8(**kw) == status
+
+
+def test_fp8_empty_problem_is_a_noop(lib):
+    assert call_fp8(N_q=0, q=0, o=0, lse=0, k=0, vt=0) == ta.ATTN_OK
+    assert call_fp8(B=0, q=0, o=0) == ta.ATTN_OK
+
+
+def test_fp8_vt_stride():
+    assert [ta.fp8_vt_stride(n) for n in (0, 1, 16, 17, 4096)] == [16, 16, 16, 32, 4096]

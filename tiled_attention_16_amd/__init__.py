@@ -39,7 +39,7 @@ def causal_mode(causal) -> int:
 
 # every symbol include/attn.h declares
 EXPORTS = ("attn_bwd", "attn_bwd_block_sparse", "attn_bwd_masked", "attn_fwd", "attn_fwd_block_sparse",
-           "attn_fwd_masked", "attn_mask_pack", "attn_status_str", "attn_version")
+           "attn_fwd_fp8", "attn_fwd_masked", "attn_mask_pack", "attn_status_str", "attn_version")
 
 SPARSE_BLOCK_Q = 256   # query rows per block of attn_fwd_block_sparse's block mask
 SPARSE_BLOCK_K = 128   # keys per block
@@ -79,6 +79,9 @@ def load_library() -> ctypes.CDLL:
     lib.attn_bwd_block_sparse.restype = ctypes.c_int
     lib.attn_bwd_block_sparse.argtypes = lib.attn_bwd.argtypes[:19] + [ctypes.c_void_p, ctypes.c_longlong,
                                                                        ctypes.c_longlong, ctypes.c_void_p]
+    lib.attn_fwd_fp8.restype = ctypes.c_int
+    lib.attn_fwd_fp8.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_longlong] + [ctypes.c_void_p] * 2 + \
+        [ctypes.c_int] * 5 + [ctypes.c_float] * 4 + [ctypes.c_int, ctypes.c_void_p]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_version.restype = ctypes.c_int
@@ -309,3 +312,66 @@ def attn_fwd_masked_raw(q: int, k: int, v: int, o: int, lse: int, B: int, H: int
                                               seqlens_k or None, q_start or None, mask_bits or None,
                                               int(mask_stride_b), int(mask_stride_h), int(mask_row_words),
                                               stream or None))
+
+
+def fp8_vt_stride(N_k: int) -> int:
+    """Smallest row stride (bytes) of the transposed V that ``attn_fwd_fp8`` accepts."""
+    return max(16, -(-N_k // 16) * 16)
+
+
+def attn_fwd_fp8_raw(q: int, k: int, vt: int, vt_row_stride: int, o: int, lse: int, B: int, H: int, N_q: int,
+                     N_k: int, d: int, scale: float, q_descale: float, k_descale: float, v_descale: float,
+                     causal, stream: int) -> int:
+    """The C entry point with plain integers for pointers; returns the status code."""
+    return int(load_library().attn_fwd_fp8(q or None, k or None, vt or None, int(vt_row_stride), o or None,
+                                           lse or None, int(B), int(H), int(N_q), int(N_k), int(d),
+                                           ctypes.c_float(scale), ctypes.c_float(q_descale),
+                                           ctypes.c_float(k_descale), ctypes.c_float(v_descale),
+                                           causal_mode(causal), stream or None))
+
+
+def attn_fwd_fp8(q8, k8, vt8, *, q_descale: float, k_descale: float, v_descale: float, causal=False,
+                 scale: Optional[float] = None, return_lse: bool = True, out=None, lse=None,
+                 stream=None) -> Tuple[object, Optional[object]]:
+    """FP8 (OCP E4M3) attention forward on GPU tensors of E4M3 codes.
+
+    ``q8`` ``[B, H, N_q, d]`` and ``k8`` ``[B, H, N_k, d]`` are uint8 or
+    float8_e4m3fn tensors; ``vt8`` is V transposed, ``[B, H, d, S]`` with the
+    row stride S a multiple of 16 and at least ``fp8_vt_stride(N_k)`` (bytes
+    past N_k are ignored). The real tensors are codes times their descale.
+    Returns ``(o, lse)``: bf16 ``[B, H, N_q, d]`` and fp32 ``[B, H, N_q]`` (None
+    unless ``return_lse``). ``causal`` as in ``attn_fwd``; ``scale`` defaults
+    to ``d ** -0.5``.
+    """
+    import torch
+
+    lib = load_library()
+    codes = []
+    for name, t in (("q8", q8), ("k8", k8), ("vt8", vt8)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise ValueError(f"{name} must be a uint8 or float8_e4m3fn GPU tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-d tensor")
+        codes.append(t)
+    B, H, N_q, d = q8.shape
+    N_k = k8.shape[2]
+    if k8.shape[:2] != (B, H) or k8.shape[3] != d or vt8.shape[:3] != (B, H, d):
+        raise ValueError(f"shape mismatch: q8 {tuple(q8.shape)} k8 {tuple(k8.shape)} vt8 {tuple(vt8.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N_q, d), dtype=torch.bfloat16, device=q8.device)
+    elif out.shape != (B, H, N_q, d) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor [B, H, N_q, d]")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q8.device)
+    if lse is not None and (lse.shape != (B, H, N_q) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, N_q]")
+    st = stream if stream is not None else torch.cuda.current_stream(q8.device)
+    status = lib.attn_fwd_fp8(q8.data_ptr() or None, k8.data_ptr() or None, vt8.data_ptr() or None, vt8.shape[3],
+                              out.data_ptr() or None, lse.data_ptr() if lse is not None else None, B, H, N_q, N_k, d,
+                              ctypes.c_float(scale), ctypes.c_float(q_descale), ctypes.c_float(k_descale),
+                              ctypes.c_float(v_descale), causal_mode(causal), ctypes.c_void_p(st.cuda_stream))
+    if status != ATTN_OK:
+        raise AttnError(status, "attn_fwd_fp8")
+    return out, (lse if return_lse else None)

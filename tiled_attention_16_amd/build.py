@@ -10,7 +10,8 @@ import sys
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 REPO_DIR = os.path.dirname(PKG_DIR)
-SRCS = [os.path.join(PKG_DIR, "csrc", "attn_fwd.hip"), os.path.join(PKG_DIR, "csrc", "attn_bwd.hip")]
+SRCS = [os.path.join(PKG_DIR, "csrc", "attn_fwd.hip"), os.path.join(PKG_DIR, "csrc", "attn_bwd.hip"),
+        os.path.join(PKG_DIR, "csrc", "attn_fwd_fp8.hip")]
 LIB = os.path.join(PKG_DIR, "libattn.so")
 
 HIPCC_FLAGS = [
