@@ -44,9 +44,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, published
 METRIC = "attention fwd TFLOP/s (bf16, causal, N=4096, d=128) + % of MFMA bf16 peak"
 HBM_METRIC = "attention fwd achieved HBM GB/s (bf16, short sequences) + % of HBM peak"
+FP8_METRIC = "attention fwd TFLOP/s (FP8 E4M3 operands, causal, N=4096, d=128) + % of MFMA fp8 peak"
+MFMA_FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, published
 BWD_METRIC = "attention bwd TFLOP/s (bf16, dQ dK dV, counted 10*B*H*N_q*N_k*d, halved when causal) + % of MFMA bf16 peak"
 KERNEL_SRC = os.path.join(ROOT, "tiled_attention_16_amd", "csrc", "attn_fwd.hip")
 BWD_SRC = os.path.join(ROOT, "tiled_attention_16_amd", "csrc", "attn_bwd.hip")
+FP8_SRC = os.path.join(ROOT, "tiled_attention_16_amd", "csrc", "attn_fwd_fp8.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -66,6 +69,20 @@ def measured_bwd_traffic(workload: str):
     if not src or src.group(1) != kernel_source_hash(BWD_SRC):
         return None
     m = re.search(rf"traffic_bytes_per_call\[{re.escape(workload)}\]:\s*([0-9.eE+]+)", text)
+    return float(m.group(1)) if m else None
+
+
+def measured_fp8_traffic(workload: str):
+    """HBM bytes per attn_fwd_fp8 launch from the committed counter summary, or
+    None when it is missing or covers an older kernel source."""
+    path = os.path.join(PROFILES, f"attn_fwd_fp8_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path, encoding="utf-8").read()
+    src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not src or src.group(1) != kernel_source_hash(FP8_SRC):
+        return None
+    m = re.search(rf"traffic_bytes_per_launch\[{re.escape(workload)}\]:\s*([0-9.eE+]+)", text)
     return float(m.group(1)) if m else None
 
 
@@ -139,6 +156,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time attn_bwd (dQ, dK, dV; its three launches) instead of the forward; O and LSE come "
                          "from one attn_fwd call before the timed region")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time attn_fwd_fp8 on E4M3 inputs of the workload's shape (per-tensor scales, V "
+                         "transposed) instead of the bf16 forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device copies of MIB MiB each (the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
@@ -186,6 +206,8 @@ def main():
         allowed = (j <= i) if w.causal else np.ones((w.N_q, w.N_k), bool)
         kept = keep[0, 0][np.arange(w.N_q) // 256][:, np.arange(w.N_k) // 128]
         sparse_frac = float((allowed & kept).sum()) / float(allowed.sum())
+    if args.fp8:
+        return bench_fp8(args, torch, ta, w, dev)
     if args.backward:
         return bench_backward(args, torch, ta, w, inp, sets[0], sl, qs, stream, dev, bmask,
                               sparse_frac if args.block_density else 1.0)
@@ -265,6 +287,78 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(result), flush=True)
+
+
+def bench_fp8(args, torch, ta, w, dev):
+    """One step = one attn_fwd_fp8 launch over the workload's shape."""
+    from workloads import make_fp8
+
+    if w.seqlens_range is not None or w.q_start_batches:
+        raise SystemExit("--fp8 takes a workload without variable lengths")
+    x = make_fp8(w.B, w.H, w.N_q, w.N_k, w.d, seed=w.seed)
+    S = ta.fp8_vt_stride(w.N_k)
+    vt = np.zeros((w.B, w.H, w.d, S), dtype=np.uint8)
+    vt[..., :w.N_k] = x.vt8
+    q, k, vtd = (torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in (x.q8, x.k8, vt))
+    o = torch.empty((w.B, w.H, w.N_q, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.N_q), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    scale = float(w.scale)
+
+    def step():
+        ta.attn_fwd_fp8(q, k, vtd, q_descale=x.q_descale, k_descale=x.k_descale, v_descale=x.v_descale,
+                        causal=w.causal, scale=scale, out=o, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    e_end.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ms_per_step = e_start.elapsed_time(e_end) / args.steps
+    tflops = w.flops() / (ms_per_step * 1e-3) / 1e12
+    result = {
+        "metric": FP8_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": w.name + "_fp8", "B": w.B, "H": w.H, "N_q": w.N_q, "N_k": w.N_k, "d": w.d,
+                   "causal": w.causal, "inputs": "E4M3 codes, one descale per tensor, V transposed"},
+        "pct_of_mfma_fp8_peak": round(100.0 * tflops / MFMA_FP8_PEAK_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": measured_fp8_traffic(w.name)},
+        "launch_ms": {"mean": round(ms_per_step, 5)},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_fp8(w, x)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_fp8(w, x, budget_s: float = 12.0):
+    """Time the fp64 FP8 oracle on whole heads of the workload until the budget is spent."""
+    import threadpoolctl
+
+    from oracle import attention_fp8
+
+    heads_done = 0
+    t0 = time.perf_counter()
+    for h in range(w.H):
+        attention_fp8(x.q8[:1, h:h + 1], x.k8[:1, h:h + 1], x.vt8[:1, h:h + 1], float(w.scale), x.q_descale,
+                      x.k_descale, x.v_descale, w.causal)
+        heads_done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = w.flops() / (w.B * w.H) * heads_done
+    blas = [d.get("num_threads", 1) for d in threadpoolctl.threadpool_info() if d.get("user_api") == "blas"]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(max(blas) if blas else 1), "kind": "oracle",
+            "sample": f"fp64 FP8 oracle (decode, then attention) on {heads_done} of {w.B * w.H} (batch, head) "
+                      f"pairs of {w.name}, all {w.N_q} rows each, {dt:.1f} s wall", "seconds": dt}
 
 
 def bench_backward(args, torch, ta, w, inp, tensors, sl, qs, stream, dev, bmask=None, kept=1.0):

@@ -21,7 +21,7 @@
 // (half, byte) works if both operands use it. A row of the S^T tile is chosen
 // to be key sigma(m) = 16*((m>>2)&1) + 4*(m>>3) + (m&3) of the 32-key slice:
 // then accumulator register r of half h holds key 16h + r, and lane half h
-// needs V^T bytes of keys [16h, 16h+16) and [32+16h, 32+16h+16) of a 64-key
+// needs V^T bytes of keys [16h, 16h+16) and [32+16h, 32+16h+16) of each 64 keys of a
 // step: two 16-byte LDS reads.
 #include <hip/hip_runtime.h>
 #include <float.h>
@@ -42,9 +42,10 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 constexpr int kWaves = 4;            // waves per workgroup, 32 query rows each
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsWG = 32 * kWaves;
-constexpr int kStep = 64;            // keys per step (k of the P V product)
+constexpr int kStep = 128;           // keys per step: 4 slices of 32 for S^T, 2 MFMAs of 64 for P V
+constexpr int kSlices = kStep / 32, kVRowChunks = kStep / 16;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kPScale = 256.f;     // P is rounded to E4M3 as P * 2^8
+constexpr float kPLog2 = 8.f;        // P is rounded to E4M3 as P * 2^8
 
 __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f32x16& c) {
   // operand formats 0 = E4M3 for A and B; block scales 127 = 2^0 (E8M0)
@@ -62,8 +63,11 @@ __device__ __forceinline__ int k_chunk(int r, int c) {
   if constexpr (D == 128) return c ^ (((r >> 1) & 3) | (((r >> 4) & 1) << 2));
   else return c ^ (((r >> 2) & 1) | (((r >> 4) & 1) << 1));
 }
-// 16-byte chunk c (of 4) of V^T tile row d
-__device__ __forceinline__ int v_chunk(int d, int c) { return c ^ ((d >> 2) & 3); }
+// 16-byte chunk c of V^T tile row d (kStep bytes), XOR-swizzled likewise
+__device__ __forceinline__ int v_chunk(int d, int c) {
+  if constexpr (kVRowChunks == 8) return c ^ ((d >> 1) & 7);
+  else return c ^ ((d >> 2) & 3);
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   auto rn = [](float x) {
@@ -74,11 +78,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
+// two workgroups (eight waves) per CU: one wave's softmax runs while another's MFMAs do
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ Vt,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int H, int N_q, int N_k, long long ldv, float c,
     float o_scale, uint32_t q_sign, int causal, int coff, int n_qt) {
-  constexpr int kKBytes = kStep * D, kStage = 2 * kKBytes;   // [K tile 64 x D][V^T tile D x 64]
+  constexpr int kKBytes = kStep * D, kStage = 2 * kKBytes;   // [K tile kStep x D][V^T tile D x kStep]
   constexpr int kKChunks = kKBytes / 16 / kThreads;          // 16-byte K chunks per thread per step
   constexpr int kVChunks = kKChunks;                         // same count for V^T
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
@@ -128,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
     }
 #pragma unroll
     for (int j = 0; j < kVChunks; ++j) {
-      const int i = tid + kThreads * j, d = i >> 2, cc = i & 3;
+      const int i = tid + kThreads * j, d = i / kVRowChunks, cc = i % kVRowChunks;
       const int kk = k0 + 16 * cc;
       u32x4 x = {0u, 0u, 0u, 0u};
       if (kk < N_k) {
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
     }
 #pragma unroll
     for (int j = 0; j < kVChunks; ++j) {
-      const int i = tid + kThreads * j, d = i >> 2, cc = i & 3;
+      const int i = tid + kThreads * j, d = i / kVRowChunks, cc = i % kVRowChunks;
       *(lds_u32x4*)(sv + d * kStep + 16 * v_chunk(d, cc)) = vbuf[j];
     }
   };
@@ -164,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = (f32x16){};
-  float m_run = -INFINITY, l_run = 0.f;   // running max (log2 units) and this half's sum
+  float m_run = -INFINITY, l_run = 0.f;   // running max (log2 units) and this half's sum of 2^8 p
   const int sig = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);   // key of S^T row m in its slice
 
   if (n_steps > 0) {
@@ -180,9 +185,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
     if (!causal || k0 <= min(q0w + 31, N_q - 1) + coff) {
       const uint8_t* sk = smem + stage * kStage;
       const uint8_t* sv = sk + kKBytes;
-      f32x16 s[2];
+      f32x16 s[kSlices];
 #pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
+      for (int sl = 0; sl < kSlices; ++sl) {
         const int r = 32 * sl + sig;
         s[sl] = (f32x16){};
 #pragma unroll
@@ -196,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
       const bool full = k0 + kStep <= N_k && (!causal || k0 + kStep - 1 <= q0w + coff);
       if (!full) {
 #pragma unroll
-        for (int sl = 0; sl < 2; ++sl)
+        for (int sl = 0; sl < kSlices; ++sl)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + 32 * sl + 16 * h + r;
@@ -206,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
       }
       float mx = -INFINITY;
 #pragma unroll
-      for (int sl = 0; sl < 2; ++sl)
+      for (int sl = 0; sl < kSlices; ++sl)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sl][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -221,10 +226,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
           for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         m_run = m_new;
       }
-      const float msub = m_run == -INFINITY ? 0.f : m_run;   // a row with no key yet: every p is 0
-      int pw[8];
+      // p * 2^8 straight from the exponent; a row with no key yet: every p is 0
+      const float msub = (m_run == -INFINITY ? 0.f : m_run) - kPLog2;
+      int pw[4 * kSlices];
 #pragma unroll
-      for (int sl = 0; sl < 2; ++sl)
+      for (int sl = 0; sl < kSlices; ++sl)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float p[4];
@@ -233,16 +239,21 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
             p[e] = __builtin_amdgcn_exp2f(s[sl][4 * j + e] * c - msub);
             l_run += p[e];
           }
-          int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * kPScale, p[1] * kPScale, 0, false);
-          pw[4 * sl + j] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * kPScale, p[3] * kPScale, w, true);
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+          pw[4 * sl + j] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
         }
-      const i32x8 pop = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+      // keys [64kh, 64kh + 64) of the step: slices 2kh and 2kh + 1
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int d = 32 * db + m;
-        const u32x4 lo = *(const lds_u32x4*)(sv + d * kStep + 16 * v_chunk(d, h));
-        const u32x4 hi = *(const lds_u32x4*)(sv + d * kStep + 16 * v_chunk(d, 2 + h));
-        oacc[db] = mfma8(join(lo, hi), pop, oacc[db]);
+      for (int kh = 0; kh < kSlices / 2; ++kh) {
+        const i32x8 pop = {pw[8 * kh], pw[8 * kh + 1], pw[8 * kh + 2], pw[8 * kh + 3],
+                           pw[8 * kh + 4], pw[8 * kh + 5], pw[8 * kh + 6], pw[8 * kh + 7]};
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int d = 32 * db + m;
+          const u32x4 lo = *(const lds_u32x4*)(sv + d * kStep + 16 * v_chunk(d, 4 * kh + h));
+          const u32x4 hi = *(const lds_u32x4*)(sv + d * kStep + 16 * v_chunk(d, 4 * kh + 2 + h));
+          oacc[db] = mfma8(join(lo, hi), pop, oacc[db]);
+        }
       }
     }
     if (st + 1 < n_steps) {
@@ -267,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
         const uint32_t b = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
         *(uint2*)(orow + d) = make_uint2(a, b);
       }
-    if (LSE && h == 0) LSE[(size_t)bh * N_q + qrow] = l > 0.f ? (m_run + __log2f(l)) / kLog2e : -INFINITY;
+    if (LSE && h == 0) LSE[(size_t)bh * N_q + qrow] = l > 0.f ? (m_run + __log2f(l) - kPLog2) / kLog2e : -INFINITY;
   }
 }
 
@@ -313,7 +324,7 @@ extern "C" int attn_fwd_fp8(const void* q, const void* k, const void* vt, long l
   c = fabsf(c);
   if (c < FLT_MIN) c = FLT_MIN;
   if (!std::isfinite(c)) return ATTN_ERR_SCALE;
-  const float o_scale = v_descale / kPScale;
+  const float o_scale = v_descale;   // the sum l carries the same 2^8 as the rounded P
   const int coff = causal == 2 ? N_k - N_q : 0, causal01 = causal ? 1 : 0, nqt = (int)n_qt;
   const dim3 grid((unsigned)(bh * n_qt)), block(kThreads);
   const uint8_t *qp = (const uint8_t*)q, *kp = (const uint8_t*)k, *vp = (const uint8_t*)vt;
