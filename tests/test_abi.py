@@ -240,3 +240,13 @@ def test_fp8_empty_problem_is_a_noop(lib):
 
 def test_fp8_vt_stride():
     assert [ta.fp8_vt_stride(n) for n in (0, 1, 16, 17, 4096)] == [16, 16, 16, 32, 4096]
+
+
+def test_fp8_binding_rejects_bad_tensors(lib):
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.uint8)
+    vt = torch.zeros(1, 1, 64, 16, dtype=torch.uint8)
+    with pytest.raises(ValueError):   # CPU tensors
+        ta.attn_fwd_fp8(q, q, vt, q_descale=1.0, k_descale=1.0, v_descale=1.0)
+    with pytest.raises(ValueError):   # bf16 is not an FP8 code tensor
+        ta.attn_fwd_fp8(q.to(torch.bfloat16), q, vt, q_descale=1.0, k_descale=1.0, v_descale=1.0)

@@ -58,3 +58,19 @@ def test_hbm_probes_sit_below_the_ridge():
     for w in HBM_PROBES.values():
         assert w.flops() / w.algorithmic_bytes() < 2500.0 / 8.0
         assert 3 * 2 * w.B * w.H * w.N_k * w.d > 256 << 20
+
+
+def test_fp8_inputs_are_deterministic_and_scaled():
+    import numpy as np
+
+    from oracle.fp8 import e4m3_decode
+    from workloads import make_fp8
+
+    a, b = make_fp8(1, 2, 30, 40, 64, seed=9), make_fp8(1, 2, 30, 40, 64, seed=9)
+    for x, y in ((a.q8, b.q8), (a.k8, b.k8), (a.vt8, b.vt8)):
+        np.testing.assert_array_equal(x, y)
+    assert (a.q_descale, a.k_descale, a.v_descale) == (b.q_descale, b.k_descale, b.v_descale)
+    assert not np.array_equal(make_fp8(1, 2, 30, 40, 64, seed=10).q8, a.q8)
+    # each tensor's largest magnitude maps to 448 (the largest E4M3 value)
+    for codes, ds in ((a.q8, a.q_descale), (a.k8, a.k_descale), (a.vt8, a.v_descale)):
+        assert np.abs(e4m3_decode(codes)).max() == 448.0 and ds > 0
