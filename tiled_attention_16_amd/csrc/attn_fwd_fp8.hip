@@ -197,17 +197,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(
           s[sl] = mfma8(join(lo, hi), qop[cq], s[sl]);
         }
       }
-      // register r of slice sl, half h: key k0 + 32*sl + 16*h + r of row qrow
+      // register r of slice sl, half h: key k0 + 32*sl + 16*h + r of row qrow,
+      // visible iff key <= lim (the last key, or the row's diagonal): one
+      // compare against a per-slice threshold per score
       const bool full = k0 + kStep <= N_k && (!causal || k0 + kStep - 1 <= q0w + coff);
       if (!full) {
+        const int lim = causal ? min(N_k - 1, qrow + coff) : N_k - 1;
 #pragma unroll
-        for (int sl = 0; sl < kSlices; ++sl)
+        for (int sl = 0; sl < kSlices; ++sl) {
+          const int thr = lim - (k0 + 32 * sl + 16 * h);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * sl + 16 * h + r;
-            const bool ok = key < N_k && (!causal || key <= qrow + coff);
-            s[sl][r] = ok ? s[sl][r] : -INFINITY;
-          }
+          for (int r = 0; r < 16; ++r) s[sl][r] = r <= thr ? s[sl][r] : -INFINITY;
+        }
       }
       float mx = -INFINITY;
 #pragma unroll
