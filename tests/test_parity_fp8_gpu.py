@@ -157,3 +157,13 @@ def test_fp8_full_size_sampled_rows():
     o, lse = run_gpu(x, 128 ** -0.5, 1)
     rows = [0, 1, 127, 128, 1000, 2047, 2048, 3333, 4095]
     check(o, lse, x, 128 ** -0.5, 1, rows=rows)
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [(1, 8, 16384, 128, 1), (1, 32, 4096, 64, 0), (2, 4, 3000, 128, 2)])
+def test_fp8_large_sampled_rows(B, H, N, d, causal):
+    """Long sequences and the other head dim at full size; sampled rows."""
+    x = make_fp8(B, H, N, N, d, seed=22 + d)
+    print(f"fp8 large {(B, H, N, d, causal)}", flush=True)
+    o, lse = run_gpu(x, d ** -0.5, causal)
+    rows = sorted({0, 1, 127, 128, 255, N // 2, N - 129, N - 1})
+    check(o, lse, x, d ** -0.5, causal, rows=rows)
