@@ -39,7 +39,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-constexpr int kWaves = 4;            // waves per workgroup, 32 query rows each
+constexpr int kWaves = 8;            // waves per workgroup, 32 query rows each
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsWG = 32 * kWaves;
 constexpr int kStep = 128;           // keys per step: 4 slices of 32 for S^T, 2 MFMAs of 64 for P V
@@ -78,8 +78,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 template <int D>
-// two workgroups (eight waves) per CU: one wave's softmax runs while another's MFMAs do
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(
+// one workgroup of eight waves per CU, two per SIMD: one wave's softmax runs while the
+// other's MFMAs do, and each K / V^T tile staged in LDS serves 256 query rows
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ Vt,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int H, int N_q, int N_k, long long ldv, float c,
     float o_scale, uint32_t q_sign, int causal, int coff, int n_qt) {
