@@ -11,11 +11,17 @@ short, bandwidth-bound shapes instead: the line then reports achieved GB/s
 (algorithmic bytes: Q, K, V read once, O and LSE written once) against the
 8 TB/s HBM peak, and successive launches rotate over three copies of the
 inputs at different addresses so that no launch finds its inputs in cache. Inputs are synthetic seeded bf16 tensors already resident in HBM
-when the timed region starts. W untimed warmup steps (enough that the GPU
-clock has settled under load), then exactly K timed steps launched back to
-back and bracketed by a device synchronisation on both sides; the timed
-region is measured with two HIP events recorded on the stream the kernel is
-launched on, and the average launch duration is that time / K.
+when the timed region starts. Warm-up: at least W untimed steps and, whatever
+W is, at least WARMUP_MIN_S seconds of back-to-back launches, because the
+GPU's clock needs that long to settle under this load (the first ~10 launches
+run at a high clock, the next ~100 dip, then it holds); the JSON records how
+many warm-up launches ran. Then exactly K timed steps launched back to back,
+bracketed by a device synchronisation on both sides; the timed region is
+measured with two HIP events recorded on the stream the kernel is launched
+on, and the average launch duration is that time / K. A second pass of K
+launches outside the timed region, with an event after each, gives the
+per-launch median, min and max (events between launches add ~2.5 % to each,
+which is why they stay out of the timed region).
 
 Prints ONE JSON line on stdout. ``value`` is TFLOP/s with the counted flops
 4*B*H*N_q*N_k*d (halved when causal). ``roofline`` prices the kernel against
@@ -41,6 +47,7 @@ from workloads import HBM_PROBES, HEADLINE, WORKLOADS, make_inputs  # noqa: E402
 ALL_WORKLOADS = {**WORKLOADS, **HBM_PROBES}
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+WARMUP_MIN_S = 0.5                # minimum warm-up time, whatever --warmup says
 HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, published
 METRIC = "attention fwd TFLOP/s (bf16, causal, N=4096, d=128) + % of MFMA bf16 peak"
 HBM_METRIC = "attention fwd achieved HBM GB/s (bf16, short sequences) + % of HBM peak"
@@ -51,6 +58,77 @@ KERNEL_SRC = os.path.join(ROOT, "tiled_attention_16_amd", "csrc", "attn_fwd.hip"
 BWD_SRC = os.path.join(ROOT, "tiled_attention_16_amd", "csrc", "attn_bwd.hip")
 FP8_SRC = os.path.join(ROOT, "tiled_attention_16_amd", "csrc", "attn_fwd_fp8.hip")
 PROFILES = os.path.join(ROOT, "profiles")
+
+
+def metric_of(w) -> str:
+    """The metric string of a forward workload (the headline's is METRIC)."""
+    if w.name == HEADLINE:
+        return METRIC
+    mask = "causal" if w.causal else ("varlen" if w.seqlens_range is not None else "non-causal")
+    return f"attention fwd TFLOP/s (bf16, {mask}, B={w.B}, H={w.H}, N={w.N_q}, d={w.d}) + % of MFMA bf16 peak"
+
+
+def effective_flops(w, inp) -> float:
+    """4*d flops per (query, key) pair that a mask allows, summed exactly over
+    every (batch, head): keys below seqlens_k[b], rows at or after q_start[b],
+    and j <= i under a causal mask. For square causal shapes this is the
+    counted N*(N+1)/2 pairs rather than the metric's N*N/2."""
+    total = 0
+    for b in range(w.B):
+        kv = w.N_k if inp.seqlens_k is None else min(max(int(inp.seqlens_k[b]), 0), w.N_k)
+        qs = 0 if inp.q_start is None else min(max(int(inp.q_start[b]), 0), w.N_q)
+        i = np.arange(qs, w.N_q, dtype=np.int64)
+        keys = np.minimum(kv, i + 1) if w.causal else np.full(i.shape, kv, dtype=np.int64)
+        total += int(keys.sum())
+    return 4.0 * w.d * w.H * total
+
+
+def warm_up(step, torch, dev, n_min: int):
+    """At least n_min launches and at least WARMUP_MIN_S seconds of them; returns (launches, seconds)."""
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(max(1, min(50, n_min - n)) if n < n_min else 50):
+            step()
+            n += 1
+        torch.cuda.synchronize(dev)
+        dt = time.perf_counter() - t0
+        if n >= n_min and dt >= WARMUP_MIN_S:
+            return n, dt
+
+
+def timed(step, torch, stream, dev, steps: int):
+    """The timed region: exactly `steps` launches back to back on `stream`
+    between two events, synchronised on both sides. Then, outside it, the same
+    number of launches with an event after each, for the per-launch median,
+    min and max (an event between launches lengthens them by ~2.5 %, so those
+    events stay out of the timed region). Returns (bracket ms, per-launch ms
+    array, wall s of the timed region)."""
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize(dev)
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    return e0.elapsed_time(e1), per, wall
+
+
+def launch_stats(total_ms: float, per, steps: int) -> dict:
+    """mean: the timed region / K; median, min, max: per-launch durations from
+    the second pass (one event after each launch, outside the timed region)."""
+    return {"mean": round(total_ms / steps, 5), "median": round(float(np.median(per)), 5),
+            "min": round(float(per.min()), 5), "max": round(float(per.max()), 5),
+            "per_launch_pass": f"{steps} more launches, an event after each"}
 
 
 def kernel_source_hash(path: str = KERNEL_SRC) -> str:
@@ -144,7 +222,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(ALL_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--window", type=int, default=0, metavar="W",
@@ -223,25 +301,19 @@ def main():
         ta.attn_fwd(sq, sk, sv, causal=w.causal, scale=float(inp.scale), seqlens_k=sl, q_start=qs, out=so,
                     lse=slse, stream=stream, packed_mask=packed, block_mask=bmask)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize(dev)
+    n_warm, warm_s = warm_up(step, torch, dev, args.warmup)
     # The timed region: exactly `steps` launches back to back on one stream,
-    # bracketed by two events (and a synchronisation on both sides). The
-    # average launch duration used for the roofline is the same bracket / K.
-    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e_start.record(stream)
-    for i in range(args.steps):
-        step()
-    e_end.record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    total_ms = e_start.elapsed_time(e_end)
+    # bracketed by events (and a synchronisation on both sides). The average
+    # launch duration used for the roofline is the bracket / K.
+    total_ms, per, wall = timed(step, torch, stream, dev, args.steps)
     ms_per_step = total_ms / args.steps
     flops = w.flops() * (sparse_frac if args.block_density else 1.0)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = tflops
+    varlen = inp.seqlens_k is not None or inp.q_start is not None
+    eff = effective_flops(w, inp) if varlen and not (args.window or args.block_density) else None
+    # the roofline prices the work the kernel has to do: for a varlen
+    # workload that is the allowed pairs, not the nominal square
+    achieved = eff / (ms_per_step * 1e-3) / 1e12 if eff is not None else tflops
     traffic = measured_traffic(w.name) if not (args.window or args.block_density) else None
     if hbm_probe:
         gbs = w.algorithmic_bytes() / (ms_per_step * 1e-3) / 1e9
@@ -254,13 +326,14 @@ def main():
             "tflops": round(tflops, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
-            "launch_ms": {"mean": round(ms_per_step, 5)},
+            "launch_ms": launch_stats(total_ms, per, args.steps),
+            "warmup_run": {"launches": n_warm, "seconds": round(warm_s, 3), "min_seconds": WARMUP_MIN_S},
             "wall_s_timed": round(wall, 4),
         }
         print(json.dumps(result), flush=True)
         return
     result = {
-        "metric": METRIC,
+        "metric": metric_of(w),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -278,10 +351,15 @@ def main():
                    **({"block_sparse": f"density {args.block_density}, kept fraction of the counted work "
                                        f"{sparse_frac:.3f}"} if args.block_density else {})},
         "pct_of_mfma_bf16_peak": round(100.0 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
+        **({"effective": {"flops": eff, "tflops": round(achieved, 2),
+                          "fraction_of_nominal": round(eff / w.flops(), 4),
+                          "note": "4*d flops per allowed (query, key) pair: keys below seqlens_k[b], "
+                                  "rows at or after q_start[b]"}} if eff is not None else {}),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic},
-        "launch_ms": {"mean": round(ms_per_step, 5)},
+        "launch_ms": launch_stats(total_ms, per, args.steps),
+        "warmup_run": {"launches": n_warm, "seconds": round(warm_s, 3), "min_seconds": WARMUP_MIN_S},
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:
@@ -309,18 +387,9 @@ def bench_fp8(args, torch, ta, w, dev):
         ta.attn_fwd_fp8(q, k, vtd, q_descale=x.q_descale, k_descale=x.k_descale, v_descale=x.v_descale,
                         causal=w.causal, scale=scale, out=o, lse=lse, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize(dev)
-    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e_start.record(stream)
-    for _ in range(args.steps):
-        step()
-    e_end.record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    ms_per_step = e_start.elapsed_time(e_end) / args.steps
+    n_warm, warm_s = warm_up(step, torch, dev, args.warmup)
+    total_ms, per, wall = timed(step, torch, stream, dev, args.steps)
+    ms_per_step = total_ms / args.steps
     tflops = w.flops() / (ms_per_step * 1e-3) / 1e12
     result = {
         "metric": FP8_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -331,7 +400,8 @@ def bench_fp8(args, torch, ta, w, dev):
         "pct_of_mfma_fp8_peak": round(100.0 * tflops / MFMA_FP8_PEAK_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": measured_fp8_traffic(w.name)},
-        "launch_ms": {"mean": round(ms_per_step, 5)},
+        "launch_ms": launch_stats(total_ms, per, args.steps),
+        "warmup_run": {"launches": n_warm, "seconds": round(warm_s, 3), "min_seconds": WARMUP_MIN_S},
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:
@@ -377,18 +447,9 @@ def bench_backward(args, torch, ta, w, inp, tensors, sl, qs, stream, dev, bmask=
         ta.attn_bwd(q, k, v, o, lse, g, causal=w.causal, scale=float(inp.scale), seqlens_k=sl, q_start=qs, dq=dq,
                     dk=dk, dv=dv, delta=delta, stream=stream, block_mask=bmask)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize(dev)
-    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e_start.record(stream)
-    for _ in range(args.steps):
-        step()
-    e_end.record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    ms = e_start.elapsed_time(e_end) / args.steps
+    n_warm, warm_s = warm_up(step, torch, dev, args.warmup)
+    total_ms, per, wall = timed(step, torch, stream, dev, args.steps)
+    ms = total_ms / args.steps
     flops = 2.5 * w.flops() * kept   # five N_q x N_k x d products (S, dP, dV, dK, dQ) against the forward's two
     tflops = flops / (ms * 1e-3) / 1e12
     result = {
@@ -402,7 +463,8 @@ def bench_backward(args, torch, ta, w, inp, tensors, sl, qs, stream, dev, bmask=
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_bwd_traffic(w.name) if bmask is None else None},
-        "launch_ms": {"mean": round(ms, 5)},
+        "launch_ms": launch_stats(total_ms, per, args.steps),
+        "warmup_run": {"launches": n_warm, "seconds": round(warm_s, 3), "min_seconds": WARMUP_MIN_S},
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:

@@ -26,4 +26,4 @@ from .attention import (allowed_mask, attention, attention_online, bf16_bits_to_
                         expand_block_mask)
 from .backward import attention_bwd  # noqa: F401
 from .fp8 import attention_fp8, e4m3_decode  # noqa: F401
-from .checker import check, check_grads, CheckResult, GradCheckResult  # noqa: F401
+from .checker import check, check_grads, merge, CheckResult, GradCheckResult  # noqa: F401

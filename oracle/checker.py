@@ -30,6 +30,8 @@ class CheckResult:
     o_mean_abs: float
     lse_max_abs: float
     reasons: list
+    o_abs_sum: float = 0.0     # sum of |dO| over the compared elements (for merging slices)
+    o_count: int = 0           # number of compared O elements
 
     def __str__(self) -> str:
         state = "PASS" if self.ok else "FAIL"
@@ -38,11 +40,13 @@ class CheckResult:
 
 
 def check(o_test: np.ndarray, o_ref: np.ndarray, lse_test: Optional[np.ndarray] = None,
-          lse_ref: Optional[np.ndarray] = None) -> CheckResult:
+          lse_ref: Optional[np.ndarray] = None, mean_bar: bool = True) -> CheckResult:
     """Compare float64 views of the tested outputs with the oracle's.
 
     ``o_test``/``o_ref``: [..., R, d]; ``lse_test``/``lse_ref``: [..., R].
     A row is fully masked when its oracle LSE is -inf (the oracle's O is 0 there).
+    ``mean_bar=False`` leaves the mean-abs bar to ``merge`` (one slice of a
+    larger output, whose mean is taken over all slices together).
     """
     o_test = np.asarray(o_test, dtype=np.float64)
     o_ref = np.asarray(o_ref, dtype=np.float64)
@@ -57,8 +61,9 @@ def check(o_test: np.ndarray, o_ref: np.ndarray, lse_test: Optional[np.ndarray] 
     o_mean = float(diff.mean()) if diff.size else 0.0
     if o_max > O_MAX_ABS:
         reasons.append(f"O max abs {o_max:.3e} > {O_MAX_ABS}")
-    if o_mean > O_MEAN_ABS:
+    if mean_bar and o_mean > O_MEAN_ABS:
         reasons.append(f"O mean abs {o_mean:.3e} > {O_MEAN_ABS}")
+    o_sum = float(diff.sum()) if diff.size else 0.0
     lse_max = 0.0
     if lse_ref is not None:
         lse_ref = np.asarray(lse_ref, dtype=np.float64)
@@ -82,7 +87,23 @@ def check(o_test: np.ndarray, o_ref: np.ndarray, lse_test: Optional[np.ndarray] 
                 lse_max = float(d.max())
                 if lse_max > LSE_MAX_ABS:
                     reasons.append(f"LSE max abs {lse_max:.3e} > {LSE_MAX_ABS}")
-    return CheckResult(not reasons, o_max, o_mean, lse_max, reasons)
+    return CheckResult(not reasons, o_max, o_mean, lse_max, reasons, o_sum, int(diff.size))
+
+
+def merge(parts) -> CheckResult:
+    """One verdict for a whole output checked slice by slice (``check(...,
+    mean_bar=False)`` on each): the max bars are the slices' maxima, the
+    mean-abs bar is applied to the mean over every element of every slice."""
+    parts = list(parts)
+    reasons = [r for p in parts for r in p.reasons]
+    o_max = max((p.o_max_abs for p in parts), default=0.0)
+    lse_max = max((p.lse_max_abs for p in parts), default=0.0)
+    total = sum(p.o_abs_sum for p in parts)
+    count = sum(p.o_count for p in parts)
+    o_mean = total / count if count else 0.0
+    if o_mean > O_MEAN_ABS:
+        reasons.append(f"O mean abs {o_mean:.3e} > {O_MEAN_ABS} over {count} elements")
+    return CheckResult(not reasons, o_max, o_mean, lse_max, reasons, total, count)
 
 
 # Gradients (the backward pass). The benchmark statement fixes no tolerance for

@@ -78,3 +78,37 @@ def test_spurious_minus_inf_fails():
     l2 = lse.copy()
     l2[1, 1, 2] = -np.inf
     assert not check(o, o, l2, lse).ok
+
+
+def test_merge_equals_whole_check():
+    # slice-by-slice checking with the mean bar left to merge() gives the same
+    # verdict and statistics as checking the whole output at once
+    from oracle.checker import merge
+    o, lse = ref()
+    rng = np.random.default_rng(7)
+    o2 = o + rng.uniform(-1.5e-3, 3.0e-3, o.shape)
+    o2[0, 1, 3] = 0.0
+    whole = check(o2, o, lse, lse)
+    parts = [check(o2[b, h], o[b, h], lse[b, h], lse[b, h], mean_bar=False) for b in range(2) for h in range(3)]
+    m = merge(parts)
+    assert m.ok == whole.ok
+    assert np.isclose(m.o_mean_abs, whole.o_mean_abs) and m.o_max_abs == whole.o_max_abs
+    assert m.lse_max_abs == whole.lse_max_abs
+
+
+def test_merge_applies_mean_bar_over_all_slices():
+    # every slice alone would pass a per-slice max bar; the merged mean is over
+    # the bar, so the merged verdict fails even though no slice tested its mean
+    from oracle.checker import O_MEAN_ABS, merge
+    o, lse = ref()
+    o2 = o + 1.5 * O_MEAN_ABS
+    o2[0, 1, 3] = 0.0
+    parts = [check(o2[b, h], o[b, h], lse[b, h], lse[b, h], mean_bar=False) for b in range(2) for h in range(3)]
+    assert all(p.ok for p in parts)
+    m = merge(parts)
+    assert not m.ok and any("mean" in r for r in m.reasons)
+    # a structural failure in one slice survives the merge
+    o3 = o.copy()
+    o3[1, 2, 0, 0] = np.nan
+    parts = [check(o3[b, h], o[b, h], lse[b, h], lse[b, h], mean_bar=False) for b in range(2) for h in range(3)]
+    assert not merge(parts).ok

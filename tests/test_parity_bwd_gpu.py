@@ -130,7 +130,8 @@ def test_bwd_repeatable_bitwise():
 @pytest.mark.parametrize("name", ["causal_n4096_d128", "varlen_n1024_d64"])
 def test_bwd_full_size_heads(name):
     """The workload at full size, launched as the benchmark launches it; the
-    oracle checks two whole (batch, head) slices."""
+    oracle checks whole (batch, head) slices: eight heads spread over the head
+    axis (headline shape), two heads of every batch (varlen shape)."""
     import tiled_attention_16_amd as ta
     w = WORKLOADS[name]
     inp = make_inputs(w)
@@ -145,7 +146,13 @@ def test_bwd_full_size_heads(name):
     dq, dk, dv = f64(dq), f64(dk), f64(dv)
     for t in (dq, dk, dv):
         assert np.all(np.isfinite(t))
-    for b, h in [(0, 0), (w.B - 1, w.H - 1)]:
+    if w.B == 1:
+        pairs = [(0, h) for h in range(0, w.H, max(1, w.H // 8))][:8] + [(0, w.H - 1)]
+    else:
+        pairs = [(b, (5 * b) % w.H) for b in range(w.B)] + [(b, w.H - 1 - (3 * b) % w.H) for b in range(w.B)]
+    pairs = sorted(set(pairs))
+    assert len(pairs) >= 8
+    for b, h in pairs:
         sb = None if inp.seqlens_k is None else inp.seqlens_k[b:b + 1]
         qb = None if inp.q_start is None else inp.q_start[b:b + 1]
         rq, rk, rv = attention_bwd(bf16_bits_to_f64(inp.q[b:b + 1, h:h + 1]), bf16_bits_to_f64(inp.k[b:b + 1, h:h + 1]),

@@ -4,9 +4,10 @@ Every case calls the C-ABI entry point through the Python binding and compares
 element by element with ``oracle.attention`` on the same seeded bf16 inputs:
   * small shapes (several tiles plus ragged tails): every output element;
   * the benchmark workloads at full size, launched exactly as bench.py launches
-    them: sampled (batch, head, row) outputs computed one by one by the oracle,
-    plus properties of the whole output (finite, fully masked rows exactly 0
-    with LSE = -inf, every element written).
+    them: every element of O and LSE, the mean-abs bar taken over the whole
+    output, plus properties of the whole output (finite, fully masked rows
+    exactly 0 with LSE = -inf);
+  * grids whose workgroup count is a multiple of 8 (regrouped over the XCDs).
 Bars: O max |d| <= 2e-2 and mean |d| <= 2e-3; LSE |d| <= 1e-3.
 """
 import sys
@@ -14,7 +15,7 @@ import sys
 import numpy as np
 import pytest
 
-from oracle import attention, bf16_bits_to_f64, check
+from oracle import attention, bf16_bits_to_f64, check, merge
 from workloads import HBM_PROBES, WORKLOADS, Workload, make_inputs, make_random, make_rising
 
 pytestmark = pytest.mark.gpu
@@ -224,37 +225,39 @@ def test_repeatable_bitwise():
     np.testing.assert_array_equal(l1, l2)
 
 
-# ------------------------------------------------------------------ full-size workloads, sampled rows
+# ------------------------------------------------------------------ full-size workloads, every element
 FULL = ["causal_n2048_d128", "causal_n4096_d128", "noncausal_n4096_d128", "varlen_n1024_d64",
         "causal_n16384_d128_stress", *HBM_PROBES]
 
 
-def sample_rows(n, rng, count=48):
-    fixed = [0, 1, 31, 32, 63, 64, 127, 128, 129, n // 2, n - 129, n - 128, n - 65, n - 64, n - 2, n - 1]
-    rest = rng.choice(n, size=count, replace=False)
-    return np.unique(np.clip(np.concatenate([fixed, rest]), 0, n - 1))
+def compare_whole(w: Workload, inp, o, lse):
+    """Every element of O and LSE against the oracle, one batch at a time (to
+    bound host memory); the mean-abs bar is taken over the whole output."""
+    parts = []
+    for b in range(w.B):
+        sl = None if inp.seqlens_k is None else inp.seqlens_k[b:b + 1]
+        qs = None if inp.q_start is None else inp.q_start[b:b + 1]
+        ro, rl = attention(bf16_bits_to_f64(inp.q[b:b + 1]), bf16_bits_to_f64(inp.k[b:b + 1]),
+                           bf16_bits_to_f64(inp.v[b:b + 1]), float(inp.scale), w.causal, seqlens_k=sl, q_start=qs,
+                           row_block=2048)
+        parts.append(check(o[b:b + 1], ro, lse[b:b + 1], rl, mean_bar=False))
+        if not parts[-1].ok:
+            print(f"  {w.name} b={b}: {parts[-1]}", flush=True)
+    r = merge(parts)
+    print(f"  {w.name} whole output ({w.B}x{w.H}x{w.N_q} rows): {r}", flush=True)
+    return r
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_workload_sampled(name):
+def test_full_size_workload_every_element(name):
+    """The workload at full size, launched as bench.py launches it (one call,
+    the whole grid: 256 or 512 workgroups, so the XCD regrouping of the
+    workgroup order is in play); every output element is compared."""
     w: Workload = {**WORKLOADS, **HBM_PROBES}[name]
     inp = make_inputs(w)
     o, lse = run(inp.q, inp.k, inp.v, inp.scale, w.causal, inp.seqlens_k, inp.q_start)
-    # properties of the whole output
-    assert np.all(np.isfinite(o)), "non-finite O"
-    assert not np.any(np.isnan(lse)), "NaN LSE"
-    rng = np.random.default_rng(w.seed)
-    bh = [(0, 0), (w.B - 1, w.H - 1)] + [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(4)]
-    q64, k64, v64 = bf16_bits_to_f64(inp.q), bf16_bits_to_f64(inp.k), bf16_bits_to_f64(inp.v)
-    for b, h in bh:
-        rows = sample_rows(w.N_q, rng)
-        sl = None if inp.seqlens_k is None else inp.seqlens_k[b:b + 1]
-        qs = None if inp.q_start is None else inp.q_start[b:b + 1]
-        ro, rl = attention(q64[b:b + 1, h:h + 1], k64[b:b + 1, h:h + 1], v64[b:b + 1, h:h + 1], float(inp.scale),
-                           w.causal, seqlens_k=sl, q_start=qs, rows=rows)
-        r = check(o[b:b + 1, h:h + 1, rows], ro, lse[b:b + 1, h:h + 1, rows], rl)
-        print(f"  {name} b={b} h={h} rows={len(rows)}: {r}", flush=True)
-        assert r.ok, f"{name} b={b} h={h}: {r}"
+    r = compare_whole(w, inp, o, lse)
+    assert r.ok, f"{name}: {r}"
     if inp.q_start is not None:
         for b in range(w.B):
             qs = int(inp.q_start[b])
@@ -262,6 +265,53 @@ def test_full_size_workload_sampled(name):
             assert np.all(np.isfinite(lse[b, :, qs:]))
     else:
         assert np.all(np.isfinite(lse))
+
+
+# Grids whose workgroup count is a multiple of 8 take the XCD regrouping of the
+# workgroup order (consecutive ids go to different XCDs; each XCD is given a
+# contiguous range of (head, tile pair) indices). Small enough to compare whole.
+XCD = [
+    # B, H, N, d, causal   (workgroups = B*H*ceil(ceil(N/256)/2))
+    (1, 8, 512, 128, True),       # 8
+    (1, 8, 512, 64, False),       # 8
+    (2, 4, 1000, 128, True),      # 16, ragged tail
+    (2, 4, 1000, 64, False),      # 16
+    (3, 8, 700, 128, False),      # 48, three tiles: one workgroup pairs tile 1 with itself
+    (1, 16, 1536, 64, True),      # 48
+]
+
+
+@pytest.mark.parametrize("case", XCD, ids=[f"{c[0]}x{c[1]}x{c[2]}_d{c[3]}_{'c' if c[4] else 'n'}" for c in XCD])
+def test_xcd_regrouped_grid_every_element(case):
+    B, H, n, d, causal = case
+    n_wg = B * H * ((-(-n // 256) + 1) // 2)
+    assert n_wg % 8 == 0
+    q, k, v = make_random(B, H, n, n, d, seed=3 * n + d + B + H)
+    compare_full(q, k, v, np.float32(d ** -0.5), causal)
+
+
+def test_xcd_regrouped_grid_writes_exactly_its_outputs():
+    # every element of O and LSE written, nothing around them, on a regrouped grid
+    import tiled_attention_16_amd as ta
+    B, H, n, d = 2, 4, 1000, 128
+    q, k, v = make_random(B, H, n, n, d, seed=31)
+    numel = B * H * n * d
+    guard = 4096
+    buf = torch.full((numel + 2 * guard,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lbuf = torch.full((B * H * n + 2 * guard,), float("nan"), dtype=torch.float32, device="cuda")
+    out = buf[guard:guard + numel].view(B, H, n, d)
+    lse = lbuf[guard:guard + B * H * n].view(B, H, n)
+    seqlens = torch.tensor([1000, 613], dtype=torch.int32, device="cuda")
+    qstart = torch.tensor([0, 300], dtype=torch.int32, device="cuda")
+    ta.attn_fwd(to_dev(q), to_dev(k), to_dev(v), causal=True, seqlens_k=seqlens, q_start=qstart, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any().item() and not torch.isnan(lse).any().item()
+    assert torch.isnan(buf[:guard]).all().item() and torch.isnan(buf[guard + numel:]).all().item()
+    assert torch.isnan(lbuf[:guard]).all().item() and torch.isnan(lbuf[guard + B * H * n:]).all().item()
+    ro, rl = attention(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), float(np.float32(d ** -0.5)),
+                       True, seqlens_k=np.array([1000, 613]), q_start=np.array([0, 300]))
+    r = check(bf16_bits_to_f64(bits_of(out)), ro, lse.cpu().numpy(), rl)
+    assert r.ok, str(r)
 
 
 # Bottom-right causal (causal = 2): key j visible to row i iff j <= i + N_k - N_q.
