@@ -56,7 +56,8 @@ typedef enum {
   ATTN_ERR_ALIGN = 5,     /* a bf16 tensor not 16-byte aligned, lse/delta 4-byte */
   ATTN_ERR_ALIAS = 6,     /* an output overlaps an input or another output       */
   ATTN_ERR_LAUNCH = 7,    /* the kernel launch failed (hipGetLastError)          */
-  ATTN_ERR_MASK = 8       /* causal not 0/1/2, or a bad mask layout              */
+  ATTN_ERR_MASK = 8,      /* causal not 0/1/2, or a bad mask layout              */
+  ATTN_ERR_SCRATCH = 9    /* attn_bwd_noalloc: B*H*N_q above its 2^20-row limit  */
 } attn_status;
 
 /*
@@ -195,6 +196,27 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              const float* lse, void* dq, void* dk, void* dv, float* delta,
              int B, int H, int N_q, int N_k, int d, float scale, int causal,
              const int32_t* seqlens_k, const int32_t* q_start, hipStream_t stream);
+
+/*
+ * attn_bwd_noalloc - attn_bwd without the delta workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Computes exactly what attn_bwd computes, with the same kernels; the per-row
+ * (LSE * log2 e, Delta) pairs go to a workspace the library owns: a static
+ * device array of 2^20 float pairs (8 MiB) on each GPU it runs on, held until
+ * the process ends. The call allocates nothing and frees nothing; on its first
+ * use on a device it looks up that array's device address (a HIP call that
+ * does not allocate) and keeps it. Limit: B * H * N_q <= 1048576 rows, else
+ * ATTN_ERR_SCRATCH before any HIP call. Every call on one GPU uses the same
+ * array: calls that overlap in time on one GPU (two streams) race and must
+ * be serialised by the caller. Other arguments, errors and launches as in
+ * attn_bwd.
+ */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv,
+                     int B, int H, int N_q, int N_k, int d, float scale, int causal,
+                     const int32_t* seqlens_k, const int32_t* q_start, hipStream_t stream);
 
 /*
  * attn_bwd_masked - attn_bwd for attn_fwd_masked: the same gradients with the

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert ta.attn_version() == 10100
-    for code in range(9):
+    for code in range(10):
         s = ta.attn_status_str(code)
         assert s and s != "unknown status"
     assert ta.attn_status_str(99) == "unknown status"
@@ -250,3 +250,38 @@ def test_fp8_binding_rejects_bad_tensors(lib):
         ta.attn_fwd_fp8(q, q, vt, q_descale=1.0, k_descale=1.0, v_descale=1.0)
     with pytest.raises(ValueError):   # bf16 is not an FP8 code tensor
         ta.attn_fwd_fp8(q.to(torch.bfloat16), q, vt, q_descale=1.0, k_descale=1.0, v_descale=1.0)
+
+
+def call_bwd_noalloc(**kw):
+    args = dict(q=A16, k=A16 * 2, v=A16 * 3, o=A16 * 4, dout=A16 * 5, lse=A16 * 6, dq=A16 * 7, dk=A16 * 8,
+                dv=A16 * 9, B=1, H=2, N_q=8, N_k=8, d=64, scale=0.125, causal=False, seqlens_k=0, q_start=0, stream=0)
+    args.update(kw)
+    return ta.attn_bwd_noalloc_raw(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=-1), ta.ATTN_ERR_SHAPE),
+    (dict(B=1, H=16, N_q=65537), ta.ATTN_ERR_SCRATCH),        # 1048592 rows > 2^20
+    (dict(B=1024, H=1024, N_q=2), ta.ATTN_ERR_SCRATCH),
+    (dict(d=32), ta.ATTN_ERR_HEAD_DIM),
+    (dict(scale=float("nan")), ta.ATTN_ERR_SCALE),
+    (dict(dout=0), ta.ATTN_ERR_NULL),
+    (dict(lse=0), ta.ATTN_ERR_NULL),
+    (dict(dq=A16 * 7 + 8), ta.ATTN_ERR_ALIGN),
+    (dict(dq=A16 * 5 + 16), ta.ATTN_ERR_ALIAS),
+    (dict(causal=3), ta.ATTN_ERR_MASK),
+])
+def test_bwd_noalloc_argument_errors_return_before_any_hip_call(lib, kw, status):
+    assert call_bwd_noalloc(**kw) == status
+
+
+def test_bwd_noalloc_limit_is_exactly_2_pow_20_rows(lib):
+    # exactly 2^20 rows passes the size check (and then fails on a later
+    # argument check, still before any HIP call); one more row does not
+    assert call_bwd_noalloc(B=1, H=16, N_q=65536, dout=0) == ta.ATTN_ERR_NULL
+    assert call_bwd_noalloc(B=1, H=16, N_q=65537, dout=0) == ta.ATTN_ERR_SCRATCH
+
+
+def test_bwd_noalloc_empty_problem_is_a_noop(lib):
+    assert call_bwd_noalloc(B=0, q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0) == ta.ATTN_OK
+    assert call_bwd_noalloc(N_q=0, N_k=0, q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0) == ta.ATTN_OK

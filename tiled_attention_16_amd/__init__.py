@@ -23,6 +23,7 @@ ATTN_ERR_ALIGN = 5
 ATTN_ERR_ALIAS = 6
 ATTN_ERR_LAUNCH = 7
 ATTN_ERR_MASK = 8
+ATTN_ERR_SCRATCH = 9
 
 # causal modes of the C ABI
 CAUSAL_NONE, CAUSAL_TOP_LEFT, CAUSAL_BOTTOM_RIGHT = 0, 1, 2
@@ -38,7 +39,7 @@ def causal_mode(causal) -> int:
     return int(causal)
 
 # every symbol include/attn.h declares
-EXPORTS = ("attn_bwd", "attn_bwd_block_sparse", "attn_bwd_masked", "attn_fwd", "attn_fwd_block_sparse",
+EXPORTS = ("attn_bwd", "attn_bwd_block_sparse", "attn_bwd_masked", "attn_bwd_noalloc", "attn_fwd", "attn_fwd_block_sparse",
            "attn_fwd_fp8", "attn_fwd_masked", "attn_mask_pack", "attn_status_str", "attn_version")
 
 SPARSE_BLOCK_Q = 256   # query rows per block of attn_fwd_block_sparse's block mask
@@ -72,6 +73,9 @@ def load_library() -> ctypes.CDLL:
                                    ctypes.c_void_p]
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int] + \
+        [ctypes.c_void_p] * 3
+    lib.attn_bwd_noalloc.restype = ctypes.c_int
+    lib.attn_bwd_noalloc.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int] + \
         [ctypes.c_void_p] * 3
     lib.attn_bwd_masked.restype = ctypes.c_int
     lib.attn_bwd_masked.argtypes = lib.attn_bwd.argtypes[:19] + [ctypes.c_void_p, ctypes.c_longlong,
@@ -300,6 +304,56 @@ def attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[flo
         status = lib.attn_bwd(*args, ctypes.c_void_p(st.cuda_stream))
     if status != ATTN_OK:
         raise AttnError(status, "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc_raw(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int, B: int,
+                         H: int, N_q: int, N_k: int, d: int, scale: float, causal, seqlens_k: int, q_start: int,
+                         stream: int) -> int:
+    """The C entry point ``attn_bwd_noalloc`` with plain integers for pointers; returns the status code."""
+    p = [x or None for x in (q, k, v, o, dout, lse, dq, dk, dv)]
+    return int(load_library().attn_bwd_noalloc(*p, int(B), int(H), int(N_q), int(N_k), int(d), ctypes.c_float(scale),
+                                               causal_mode(causal), seqlens_k or None, q_start or None,
+                                               stream or None))
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, *, causal: bool = False, scale: Optional[float] = None,
+                     seqlens_k=None, q_start=None, stream=None):
+    """``attn_bwd`` through the allocation-free entry point: the caller passes
+    every output (``dq``, ``dk``, ``dv``), there is no ``delta`` workspace (the
+    library keeps the row statistics in its own per-GPU array) and nothing is
+    allocated. B*H*N_q is limited to 2**20 rows; calls that overlap in time on
+    one GPU race. Returns ``(dq, dk, dv)``."""
+    import torch
+
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise ValueError(f"{name} must be a bfloat16 GPU tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+    B, H, N_q, d = q.shape
+    N_k = k.shape[2]
+    if k.shape[:2] != (B, H) or k.shape[3] != d or v.shape != k.shape or dk.shape != k.shape or \
+            dv.shape != k.shape or o.shape != q.shape or dout.shape != q.shape or dq.shape != q.shape:
+        raise ValueError("shape mismatch among q, k, v, o, dout, dq, dk, dv")
+    if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or not lse.is_cuda or \
+            lse.shape != (B, H, N_q) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N_q] GPU tensor")
+    for name, t in (("seqlens_k", seqlens_k), ("q_start", q_start)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_cuda or t.numel() != B or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 GPU tensor of {B} elements")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    ptr = lambda t: t.data_ptr() or None  # noqa: E731
+    status = lib.attn_bwd_noalloc(ptr(q), ptr(k), ptr(v), ptr(o), ptr(dout), ptr(lse), ptr(dq), ptr(dk), ptr(dv),
+                                  B, H, N_q, N_k, d, ctypes.c_float(scale), causal_mode(causal),
+                                  seqlens_k.data_ptr() if seqlens_k is not None else None,
+                                  q_start.data_ptr() if q_start is not None else None,
+                                  ctypes.c_void_p(st.cuda_stream))
+    if status != ATTN_OK:
+        raise AttnError(status, "attn_bwd_noalloc")
     return dq, dk, dv
 
 

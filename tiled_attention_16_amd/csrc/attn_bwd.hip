@@ -36,6 +36,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
+#include <mutex>
 #include <type_traits>
 
 #include "attn.h"
@@ -761,10 +762,16 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// Device address of the allocation-free entry point's row-statistics array
+// on the device of `stream` (declared below); looked up once per device.
+int scratch_address(hipStream_t stream, float** out);
+
+// delta == nullptr with own_delta: the row statistics go to the library's own
+// array (attn_bwd_noalloc); its address is taken after every argument check.
 int bwd_launch(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                void* dq, void* dk, void* dv, float* delta, int B, int H, int N_q, int N_k, int d, float scale,
                int causal, const int32_t* seqlens_k, const int32_t* q_start, DenseMask dm, BlockMask bmk,
-               hipStream_t stream) {
+               hipStream_t stream, bool own_delta = false) {
   if (B < 0 || H < 0 || N_q < 0 || N_k < 0) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
@@ -772,7 +779,7 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
   const long long bh = (long long)B * H;
   if (bh == 0 || (N_q == 0 && N_k == 0)) return ATTN_OK;
   const bool has_q = N_q > 0, has_k = N_k > 0;
-  if (has_q && (!q || !o || !dout || !lse || !dq || !delta)) return ATTN_ERR_NULL;
+  if (has_q && (!q || !o || !dout || !lse || !dq || (!delta && !own_delta))) return ATTN_ERR_NULL;
   if (has_k && (!k || !v || !dk || !dv)) return ATTN_ERR_NULL;
   if (bh > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   const long long n_qt = (N_q + kTile - 1) / kTile, n_kt = (N_k + kTile - 1) / kTile;
@@ -793,6 +800,11 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
       if (overlaps(outs[i], out_n[i], ins[j], in_n[j])) return ATTN_ERR_ALIAS;
     for (int j = i + 1; j < 4; ++j)
       if (overlaps(outs[i], out_n[i], outs[j], out_n[j])) return ATTN_ERR_ALIAS;
+  }
+
+  if (own_delta && has_q) {
+    const int st = scratch_address(stream, &delta);
+    if (st != ATTN_OK) return st;
   }
 
   const float c = scale * kLog2e;
@@ -873,4 +885,55 @@ extern "C" int attn_bwd_block_sparse(const void* q, const void* k, const void* v
   const int n_ks = (N_k + kTile - 1) / kTile;   // 128-key blocks per row of the block mask
   return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N_q, N_k, d, scale, causal, seqlens_k, q_start,
                     DenseMask{nullptr, 0, 0, 0}, BlockMask{block_mask, block_stride_b, block_stride_h, n_ks}, stream);
+}
+
+// ---------------------------------------------------- allocation-free backward
+// attn_bwd_noalloc is attn_bwd with the per-row (LSE * log2 e, Delta) pairs
+// kept in `scratch`, a library-owned array of this size (one copy on every GPU
+// the library runs on, resident until the process ends), for callers that
+// cannot allocate device memory. On the host the array's name only stands in
+// for the symbol: its device address is looked up once per device with
+// hipGetSymbolAddress (that device current) and only that address is ever
+// handed to a kernel. The delta kernel writes every row it covers before the
+// dQ and dK/dV kernels read them, so nothing has to be cleared between calls.
+// Two calls that overlap in time on one GPU share the array and race.
+namespace {
+constexpr long long kNoAllocRows = 1LL << 20;   // B * H * N_q at most: 8 MiB of float pairs
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) float scratch[2 * kNoAllocRows];
+
+namespace {
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices];   // device address of `scratch` per device, null until looked up
+
+int scratch_address(hipStream_t stream, float** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return ATTN_ERR_LAUNCH;
+  int dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return ATTN_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return ATTN_ERR_LAUNCH;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) return ATTN_ERR_LAUNCH;
+    g_scratch[dev] = (float*)p;
+  }
+  *out = g_scratch[dev];
+  return ATTN_OK;
+}
+}  // namespace
+
+extern "C" int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                const float* lse, void* dq, void* dk, void* dv, int B, int H, int N_q, int N_k,
+                                int d, float scale, int causal, const int32_t* seqlens_k, const int32_t* q_start,
+                                hipStream_t stream) {
+  if (B < 0 || H < 0 || N_q < 0 || N_k < 0) return ATTN_ERR_SHAPE;
+  if ((long long)B * H * N_q > kNoAllocRows) return ATTN_ERR_SCRATCH;
+  return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, nullptr, B, H, N_q, N_k, d, scale, causal, seqlens_k, q_start,
+                    DenseMask{nullptr, 0, 0, 0}, BlockMask{nullptr, 0, 0, 0}, stream, true);
 }

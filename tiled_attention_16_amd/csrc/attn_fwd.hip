@@ -1009,6 +1009,7 @@ extern "C" const char* attn_status_str(int status) {
     case ATTN_ERR_ALIAS: return "output overlaps an input or the other output";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
     case ATTN_ERR_MASK: return "causal must be 0, 1 or 2; mask rows need >= ceil(N_k/32) words, a multiple of 8";
+    case ATTN_ERR_SCRATCH: return "B*H*N_q exceeds the 1048576 rows of the allocation-free backward's own workspace";
     default: return "unknown status";
   }
 }
