@@ -218,6 +218,69 @@ def copy_calibration(torch, mib: int):
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
+def run_probes(torch):
+    """Instruction-rate microbenchmarks (``libattn_probe.so``): the MFMA-only
+    rate and clock, VALU work hidden under MFMAs, v_exp_f32 against v_fma_f32,
+    and LDS read rates. Each probe kernel records per-workgroup shader-clock
+    cycles (s_memtime) and the 100 MHz real-time counter (s_memrealtime)."""
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "tiled_attention_16_amd", "libattn_probe.so"))
+    lib.attn_probe.restype = ctypes.c_int
+    lib.attn_probe.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = torch.cuda.current_stream(dev)
+    sink = torch.zeros(512, dtype=torch.float32, device=dev)
+
+    def one(kind, op, nv, threads, iters, blocks=None):
+        blocks = blocks or n_cu
+        t = torch.zeros(4 * blocks, dtype=torch.int64, device=dev)
+        for _ in range(2):   # the first launch warms the clock and loads the code
+            rc = lib.attn_probe(kind, op, nv, blocks, threads, iters, t.data_ptr(), sink.data_ptr(),
+                                ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"attn_probe({kind}, {op}, {nv}) failed: {rc}")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        lib.attn_probe(kind, op, nv, blocks, threads, iters, t.data_ptr(), sink.data_ptr(),
+                       ctypes.c_void_p(stream.cuda_stream))
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        ms = e0.elapsed_time(e1)
+        a = t.cpu().numpy().astype(np.float64).reshape(blocks, 4)
+        cyc = np.median(a[:, 2] - a[:, 0])
+        rt = np.median(a[:, 3] - a[:, 1])
+        return ms, cyc, cyc / rt * 100e6   # ms, cycles per workgroup, clock in Hz
+
+    out = {"probe": "gfx950 instruction rates", "compute_units": n_cu,
+           "note": "cycles are shader-clock cycles (s_memtime); per SIMD means summed over the waves of a SIMD"}
+    iters = 40000
+    valu = ((0, "v_fma_f32"), (1, "v_exp_f32"), (2, "v_cvt_pk_bf16_f32"), (3, "v_add_f32"))
+    for waves in (1, 2):
+        ms, cyc, clk = one(0, 0, 0, 256 * waves, iters)
+        flops = n_cu * 4 * waves * iters * 4 * 32768.0
+        out[f"mfma_only_{waves}wave_per_simd"] = {
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1), "clock_ghz": round(clk / 1e9, 3),
+            "cycles_per_mfma_per_simd": round(cyc / (iters * 4 * waves), 2)}
+        for op, name in valu:
+            row = {}
+            for nv in (2, 4, 6, 8):
+                ms, cyc, clk = one(0, op, nv, 256 * waves, iters // 2)
+                row[str(nv)] = round(cyc / (iters // 2 * 4 * waves), 2)
+            out[f"cycles_per_mfma_per_simd_with_n_{name}_after_each_{waves}wave_per_simd"] = row
+    for op, name in valu:
+        ms, cyc, clk = one(1, op, 32, 256, iters // 4)
+        c1 = cyc / (iters // 4 * 32)
+        ms, cyc, clk = one(1, op, 32, 512, iters // 4)
+        out[f"{name}_cycles_per_instruction"] = {"1wave_per_simd": round(c1, 2),
+                                                 "2waves_per_simd_per_simd": round(cyc / (iters // 4 * 32 * 2), 2)}
+    for op, name, nbytes in ((0, "ds_read_b128", 1024), (1, "ds_read_b64_tr_b16", 512)):
+        ms, cyc, clk = one(2, op, 0, 512, iters // 8)
+        out[f"{name}_bytes_per_clock_per_cu_8waves"] = round(8 * (iters // 8) * 8 * nbytes / cyc, 1)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,6 +300,9 @@ def main():
     ap.add_argument("--fp8", action="store_true",
                     help="time attn_fwd_fp8 on E4M3 inputs of the workload's shape (per-tensor scales, V "
                          "transposed) instead of the bf16 forward")
+    ap.add_argument("--probe", action="store_true",
+                    help="instead of the benchmark, run the instruction-rate microbenchmarks (MFMA-only rate and "
+                         "clock, VALU work hidden under MFMAs, v_exp_f32 cost, LDS read rates) and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 5 plain device copies of MIB MiB each (the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
@@ -250,6 +316,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration)
+        return
+    if args.probe:
+        run_probes(torch)
         return
 
     import tiled_attention_16_amd as ta

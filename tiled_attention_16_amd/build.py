@@ -1,4 +1,5 @@
-"""Compile the HIP library ``libattn.so`` (forward and backward kernels) for gfx950 in-tree.
+"""Compile the HIP library ``libattn.so`` (forward and backward kernels) for gfx950 in-tree,
+and the instruction-rate probes ``libattn_probe.so`` that ``bench.py --probe`` runs.
 
 Usage: ``python -m tiled_attention_16_amd.build`` (or ``build_library()``).
 """
@@ -13,6 +14,9 @@ REPO_DIR = os.path.dirname(PKG_DIR)
 SRCS = [os.path.join(PKG_DIR, "csrc", "attn_fwd.hip"), os.path.join(PKG_DIR, "csrc", "attn_bwd.hip"),
         os.path.join(PKG_DIR, "csrc", "attn_fwd_fp8.hip")]
 LIB = os.path.join(PKG_DIR, "libattn.so")
+# instruction-rate microbenchmarks (bench.py --probe); not part of the attention C ABI
+PROBE_SRC = os.path.join(PKG_DIR, "csrc", "probes.hip")
+PROBE_LIB = os.path.join(PKG_DIR, "libattn_probe.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -42,9 +46,12 @@ def build_library(verbose: bool = False) -> str:
     flags_s = [f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
     # the forward kernel's hand-placed MFMAs are the ones the hazard check is for
     cmd_s = [hipcc, *flags_s, *inc, "--cuda-device-only", "-S", SRCS[0], "-o", asm]
-    procs = [subprocess.Popen(c, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True) for c in (cmd, cmd_s)]
+    probe_tmp = PROBE_LIB + ".tmp"
+    cmd_p = [hipcc, *HIPCC_FLAGS, PROBE_SRC, "-o", probe_tmp]
+    cmds = (cmd, cmd_s, cmd_p)
+    procs = [subprocess.Popen(c, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True) for c in cmds]
     outs = [p.communicate() for p in procs]
-    for c, p, (out, err) in zip((cmd, cmd_s), procs, outs):
+    for c, p, (out, err) in zip(cmds, procs, outs):
         if p.returncode != 0:
             raise RuntimeError(f"hipcc failed ({p.returncode}):\n{' '.join(c)}\n{out}\n{err}")
     if verbose and outs[0][1]:
@@ -56,6 +63,7 @@ def build_library(verbose: bool = False) -> str:
         os.remove(tmp)
         raise RuntimeError("MFMA hazard in the compiled kernel:\n" + "\n".join(problems))
     os.replace(tmp, LIB)
+    os.replace(probe_tmp, PROBE_LIB)
     return LIB
 
 
