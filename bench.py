@@ -83,8 +83,8 @@ def effective_flops(w, inp) -> float:
     return 4.0 * w.d * w.H * total
 
 
-def warm_up(step, torch, dev, n_min: int):
-    """At least n_min launches and at least WARMUP_MIN_S seconds of them; returns (launches, seconds)."""
+def warm_up(step, torch, dev, n_min: int, min_s: float = WARMUP_MIN_S):
+    """At least n_min launches and at least min_s seconds of them; returns (launches, seconds)."""
     n = 0
     t0 = time.perf_counter()
     while True:
@@ -93,7 +93,7 @@ def warm_up(step, torch, dev, n_min: int):
             n += 1
         torch.cuda.synchronize(dev)
         dt = time.perf_counter() - t0
-        if n >= n_min and dt >= WARMUP_MIN_S:
+        if n >= n_min and dt >= min_s:
             return n, dt
 
 
@@ -167,7 +167,7 @@ def measured_fp8_traffic(workload: str):
 def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when the summary is missing, covers another workload or an older kernel."""
-    path = os.path.join(PROFILES, f"attn_fwd_{workload}_hbm_traffic.md")
+    path = os.path.join(PROFILES, f"attn_fwd_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path, encoding="utf-8").read()
@@ -286,6 +286,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-min-s", type=float, default=WARMUP_MIN_S, metavar="S",
+                    help="minimum warm-up time in seconds, whatever --warmup is (default %(default)s: the clock "
+                         "settles under this load after ~0.05 s); 0 for counter runs under a profiler")
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(ALL_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--window", type=int, default=0, metavar="W",
@@ -370,7 +373,7 @@ def main():
         ta.attn_fwd(sq, sk, sv, causal=w.causal, scale=float(inp.scale), seqlens_k=sl, q_start=qs, out=so,
                     lse=slse, stream=stream, packed_mask=packed, block_mask=bmask)
 
-    n_warm, warm_s = warm_up(step, torch, dev, args.warmup)
+    n_warm, warm_s = warm_up(step, torch, dev, args.warmup, args.warmup_min_s)
     # The timed region: exactly `steps` launches back to back on one stream,
     # bracketed by events (and a synchronisation on both sides). The average
     # launch duration used for the roofline is the bracket / K.
@@ -396,7 +399,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
             "launch_ms": launch_stats(total_ms, per, args.steps),
-            "warmup_run": {"launches": n_warm, "seconds": round(warm_s, 3), "min_seconds": WARMUP_MIN_S},
+            "warmup_run": {"launches": n_warm, "seconds": round(warm_s, 3), "min_seconds": args.warmup_min_s},
             "wall_s_timed": round(wall, 4),
         }
         print(json.dumps(result), flush=True)
@@ -428,7 +431,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic},
         "launch_ms": launch_stats(total_ms, per, args.steps),
-        "warmup_run": {"launches": n_warm, "seconds": round(warm_s, 3), "min_seconds": WARMUP_MIN_S},
+        "warmup_run": {"launches": n_warm, "seconds": round(warm_s, 3), "min_seconds": args.warmup_min_s},
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:
@@ -456,7 +459,7 @@ def bench_fp8(args, torch, ta, w, dev):
         ta.attn_fwd_fp8(q, k, vtd, q_descale=x.q_descale, k_descale=x.k_descale, v_descale=x.v_descale,
                         causal=w.causal, scale=scale, out=o, lse=lse, stream=stream)
 
-    n_warm, warm_s = warm_up(step, torch, dev, args.warmup)
+    n_warm, warm_s = warm_up(step, torch, dev, args.warmup, args.warmup_min_s)
     total_ms, per, wall = timed(step, torch, stream, dev, args.steps)
     ms_per_step = total_ms / args.steps
     tflops = w.flops() / (ms_per_step * 1e-3) / 1e12
@@ -470,7 +473,7 @@ def bench_fp8(args, torch, ta, w, dev):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": measured_fp8_traffic(w.name)},
         "launch_ms": launch_stats(total_ms, per, args.steps),
-        "warmup_run": {"launches": n_warm, "seconds": round(warm_s, 3), "min_seconds": WARMUP_MIN_S},
+        "warmup_run": {"launches": n_warm, "seconds": round(warm_s, 3), "min_seconds": args.warmup_min_s},
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:
@@ -516,7 +519,7 @@ def bench_backward(args, torch, ta, w, inp, tensors, sl, qs, stream, dev, bmask=
         ta.attn_bwd(q, k, v, o, lse, g, causal=w.causal, scale=float(inp.scale), seqlens_k=sl, q_start=qs, dq=dq,
                     dk=dk, dv=dv, delta=delta, stream=stream, block_mask=bmask)
 
-    n_warm, warm_s = warm_up(step, torch, dev, args.warmup)
+    n_warm, warm_s = warm_up(step, torch, dev, args.warmup, args.warmup_min_s)
     total_ms, per, wall = timed(step, torch, stream, dev, args.steps)
     ms = total_ms / args.steps
     flops = 2.5 * w.flops() * kept   # five N_q x N_k x d products (S, dP, dV, dK, dQ) against the forward's two
@@ -533,7 +536,7 @@ def bench_backward(args, torch, ta, w, inp, tensors, sl, qs, stream, dev, bmask=
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_bwd_traffic(w.name) if bmask is None else None},
         "launch_ms": launch_stats(total_ms, per, args.steps),
-        "warmup_run": {"launches": n_warm, "seconds": round(warm_s, 3), "min_seconds": WARMUP_MIN_S},
+        "warmup_run": {"launches": n_warm, "seconds": round(warm_s, 3), "min_seconds": args.warmup_min_s},
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:

@@ -89,17 +89,26 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr int kSlice = 32;     // keys per K/V slice (one LDS stage, one pipeline step)
-constexpr int kStages = 8;     // LDS ring depth in slices
 constexpr int kRB = 1;         // 32-row MFMA blocks (query rows / 32) per wave
 constexpr int kRows = 32 * kRB;           // query rows per wave
-constexpr int kWaves = 8 / kRB;           // wave64s per workgroup: 256 rows per workgroup
-constexpr int kBM = kRows * kWaves;
-constexpr int kThreads = 64 * kWaves;
 constexpr float kSumCap = 256.f;   // bound on a lane's 16 exponentials of one slice (2^8)
 constexpr float kLn2 = 0.69314718055994530942f;
 
-template <int D>
+// Workgroup shape. W = 8: one workgroup of 8 waves (256 query rows) per CU,
+// the two waves of each SIMD from the same workgroup. W = 4: 4 waves (128
+// query rows) per workgroup and two workgroups per CU, each with its own ring
+// in half the LDS: the two waves of a SIMD then belong to different
+// workgroups and do not meet at the same barriers, so one workgroup's barrier
+// and LDS waits, and its tile prologue and epilogue, run under the other's
+// MFMAs. The ring is 8 slices deep either way, so W = 4 needs d = 64 (64 KB of
+// stages per workgroup); at d = 128 the 80 KB per workgroup would allow only
+// 5 stages, too shallow to cover the copy latency.
+template <int D, int W>
 struct Slice {
+  static constexpr int kWaves = W;                           // wave64s per workgroup
+  static constexpr int kBM = kRows * W;                      // query rows per workgroup (one tile)
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kStages = 8;                          // LDS ring depth in slices
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kBytes = kSlice * kRowBytes;          // one K or V stage
   static constexpr int kLds = 2 * kStages * kBytes;          // K stages, then V stages
@@ -109,8 +118,14 @@ struct Slice {
   static constexpr int kRowsPerCopy = 1024 / kRowBytes;
   static constexpr int kLanesPerRow = 64 / kRowsPerCopy;
   static_assert(kCopies % kCopyWaves == 0, "copies must split evenly over the copying waves");
-  static_assert(kLds <= 160 * 1024, "the stages must fit the 160 KB LDS of a CU");
+  static_assert(kLds * (W == 4 ? 2 : 1) <= 160 * 1024, "the workgroups' stages must fit the 160 KB LDS of a CU");
 };
+
+// Workgroup shape of each kernel instance (see Slice): the rules-only forward
+// at d = 64 runs two 4-wave workgroups per CU; the others keep 8-wave
+// workgroups (the dense-mask and block-sparse instances lay out their mask
+// words and block flags per 256-row tile).
+constexpr int waves_of(int mode, int d) { return mode == 0 && d == 64 ? 4 : 8; }
 
 // Chunk position of 16-byte chunk c of row r is c ^ swz(r). The banks sweep
 // 256 bytes. Two read patterns must stay conflict-free:
@@ -208,14 +223,15 @@ constexpr int kMaxSparseSlices = 1024;   // keys per head up to 32768 on the spa
 constexpr int kListPad = 80;             // sentinel entries past the list (the copies look 7 ahead)
 
 template <int D, int Mode>   // Mode 0: rules only; 1: dense mask (Dense); 2: block-sparse (Sparse)
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
+__global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 : 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int H, int N_q, int N_k, float c, int neg_scale,
     int causal, int coff, const int32_t* __restrict__ seqlens_k, const int32_t* __restrict__ q_start, int n_qt,
     int n_wg, const uint32_t* __restrict__ mbits, long long msb, long long msh, int mrw,
     const uint8_t* __restrict__ bmask, long long bsb, long long bsh, int n_ks) {
   constexpr bool Dense = Mode == 1, Sparse = Mode == 2;
-  using T = Slice<D>;
+  using T = Slice<D, waves_of(Mode, D)>;
+  constexpr int kWaves = T::kWaves, kBM = T::kBM, kThreads = T::kThreads, kStages = T::kStages;
   constexpr int kMaskLds = Dense ? 2 * kWaves * 1024                              // two 8-slice blocks of mask words per wave
                                  : Sparse ? 4 * (kMaxSparseSlices + kListPad + 16)   // the slice list
                                           : 0;
@@ -903,7 +919,9 @@ int fwd_launch(const void* q, const void* k, const void* v, void* o, float* lse,
   if ((long long)B * H * N_q == 0) return ATTN_OK;
   if (!q || !o) return ATTN_ERR_NULL;
   if (N_k > 0 && (!k || !v)) return ATTN_ERR_NULL;
-  const long long n_qt = (N_q + kBM - 1) / kBM;
+  const int mode = mbits ? 1 : bmask ? 2 : 0;
+  const int waves = waves_of(mode, d), bm = kRows * waves;      // workgroup shape of the instance
+  const long long n_qt = (N_q + bm - 1) / bm;
   const long long n_wg = (long long)B * H * ((n_qt + 1) / 2);   // one workgroup per pair of query tiles
   if (n_wg > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   if ((long long)B * H > 0x7fffffffLL) return ATTN_ERR_SHAPE;
@@ -933,10 +951,9 @@ int fwd_launch(const void* q, const void* k, const void* v, void* o, float* lse,
   uint16_t* op = (uint16_t*)o;
   // causal mode 1: key j visible to row i iff j <= i; mode 2: iff j <= i + N_k - N_q
   int causal01 = causal ? 1 : 0, coff = causal == 2 ? N_k - N_q : 0, n_qt_i = (int)n_qt, n_wg_i = (int)n_wg;
-  const int mode = mbits ? 1 : bmask ? 2 : 0;
   auto kern = d == 128 ? (mode == 1 ? attn_fwd_kernel<128, 1> : mode == 2 ? attn_fwd_kernel<128, 2> : attn_fwd_kernel<128, 0>)
                        : (mode == 1 ? attn_fwd_kernel<64, 1> : mode == 2 ? attn_fwd_kernel<64, 2> : attn_fwd_kernel<64, 0>);
-  const hipError_t e = attn_launch::launch(kern, dim3((unsigned)n_wg), dim3(kThreads), stream, qp, kp, vp, op, lse, H, N_q,
+  const hipError_t e = attn_launch::launch(kern, dim3((unsigned)n_wg), dim3(64 * waves), stream, qp, kp, vp, op, lse, H, N_q,
                                            N_k, c, neg, causal01, coff, seqlens_k, q_start, n_qt_i, n_wg_i, mbits, msb,
                                            msh, mrw, bmask, bsb, bsh, n_ks);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
