@@ -42,9 +42,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import HBM_PROBES, HEADLINE, WORKLOADS, make_inputs  # noqa: E402
+from workloads import HBM_PROBES, HEADLINE, REFERENCE, WORKLOADS, make_inputs  # noqa: E402
 
-ALL_WORKLOADS = {**WORKLOADS, **HBM_PROBES}
+ALL_WORKLOADS = {**WORKLOADS, **HBM_PROBES, **REFERENCE}
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 WARMUP_MIN_S = 0.5                # minimum warm-up time, whatever --warmup says

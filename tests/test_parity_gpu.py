@@ -108,6 +108,28 @@ def test_out_of_range_mask_values_are_clamped():
                  np.array([-3, 0, 1000], np.int32))
 
 
+# Non-causal launches with per-batch lengths hand out their workgroups heaviest
+# batch first (batches ranked by valid keys times attending rows, one lane per
+# batch, up to 64 batches; more batches take the plain order).
+RANKED = [
+    # B, H, N, d, seqlens (None: random with ties), q_start
+    (64, 1, 70, 64, None, None),
+    (65, 1, 40, 128, None, None),
+    (7, 3, 600, 128, [600, 17, 600, 0, 333, 600, 17], [0, 0, 500, 0, 0, 599, 3]),
+    (5, 2, 300, 64, [300, 300, 300, 300, 300], [0, 64, 0, 64, 300]),
+]
+
+
+@pytest.mark.parametrize("case", RANKED, ids=[f"B{c[0]}_H{c[1]}_N{c[2]}_d{c[3]}" for c in RANKED])
+def test_heaviest_batch_first_order(case):
+    B, H, n, d, sl, qs = case
+    q, k, v = make_random(B, H, n, n, d, seed=B * 7 + n + d)
+    rng = np.random.default_rng(B + n)
+    seqlens = np.array(sl, np.int32) if sl is not None else rng.choice([1, n // 3, n // 2, n], size=B).astype(np.int32)
+    qstart = np.array(qs, np.int32) if qs is not None else None
+    compare_full(q, k, v, np.float32(d ** -0.5), False, seqlens, qstart)
+
+
 def test_padding_contents_never_used():
     B, H, n, d = 2, 2, 150, 128
     q, k, v = make_random(B, H, n, n, d, seed=11)

@@ -220,6 +220,7 @@ __device__ __forceinline__ void wait_copies() {
 // LDS; the ring walks that list, so unset slices cost neither copies nor
 // arithmetic. The rules still mask inside the slices that are computed.
 constexpr int kMaxSparseSlices = 1024;   // keys per head up to 32768 on the sparse path
+constexpr int kMaxRankedBatches = 64;    // batches ranked by work (one per lane) for the launch order
 constexpr int kListPad = 80;             // sentinel entries past the list (the copies look 7 ahead)
 
 template <int D, int Mode>   // Mode 0: rules only; 1: dense mask (Dense); 2: block-sparse (Sparse)
@@ -243,22 +244,58 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
   const int hf = lane >> 5;
 
   // ---- work decomposition: blockIdx -> (batch*head, pair of query tiles) ----
-  // Consecutive workgroup ids are dealt round-robin over the 8 XCDs; regroup so
-  // that each XCD gets a contiguous range of (head, tile) pairs and the K/V of a
-  // head stay in one XCD's L2.
-  int lin = blockIdx.x;
-  if ((n_wg & 7) == 0) lin = (lin & 7) * (n_wg >> 3) + (lin >> 3);
   const int n_pairs = (n_qt + 1) / 2;
-  const int bh = lin / n_pairs;
-  const int pr = lin - bh * n_pairs;
+  const int per_b = H * n_pairs;   // workgroups of one batch
+  const int n_b = n_wg / per_b;    // the batch count
+  int bh, pr;
+  int kv = N_k, qs = 0;   // the batch's valid keys and masked leading rows, clamped
+  bool have_kv_qs = false;
+  if (!causal && (seqlens_k || q_start) && n_b <= kMaxRankedBatches) {
+    // Per-batch valid lengths make batches unequal; the workgroups of one
+    // batch are equal. Rank the batches by their work, valid keys times rows
+    // that attend (ties by index), and hand out the workgroups heaviest batch
+    // first: the dispatcher starts workgroups in id order and refills free
+    // slots in the same order, so this is a longest-first schedule. Ids stay
+    // dealt round-robin over the XCDs, which then all get a mix of batches.
+    long long wl = -1;   // lane l: the work of batch l
+    int kv_l = N_k, qs_l = 0;
+    if (lane < n_b) {
+      kv_l = seqlens_k ? min(max(seqlens_k[lane], 0), N_k) : N_k;
+      qs_l = q_start ? min(max(q_start[lane], 0), N_q) : 0;
+      wl = (long long)kv_l * (N_q - qs_l);
+    }
+    int rank = 0;
+    for (int j = 0; j < n_b; ++j) {
+      const long long wj = ((long long)__builtin_amdgcn_readlane((int)(wl >> 32), j) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)wl, j);
+      rank += (wj > wl || (wj == wl && j < lane)) ? 1 : 0;
+    }
+    const int r0 = blockIdx.x / per_b;                 // this workgroup's batch rank
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < n_b && rank == r0);
+    const int b_r = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+    const int rem = blockIdx.x - r0 * per_b;
+    bh = b_r * H + rem / n_pairs;
+    pr = rem % n_pairs;
+    kv = __builtin_amdgcn_readlane(kv_l, b_r);
+    qs = __builtin_amdgcn_readlane(qs_l, b_r);
+    have_kv_qs = true;
+  } else {
+    // Consecutive workgroup ids are dealt round-robin over the 8 XCDs; regroup
+    // so that each XCD gets a contiguous range of (head, tile) pairs and the
+    // K/V of a head stay in one XCD's L2.
+    int lin = blockIdx.x;
+    if ((n_wg & 7) == 0) lin = (lin & 7) * (n_wg >> 3) + (lin >> 3);
+    bh = lin / n_pairs;
+    pr = lin - bh * n_pairs;
+  }
   const int b = bh / H;
   const char* kg = (const char*)(K + (size_t)bh * N_k * D);
   const char* vg = (const char*)(V + (size_t)bh * N_k * D);
 
-  int kv = N_k;
-  if (seqlens_k) kv = min(max(seqlens_k[b], 0), N_k);
-  int qs = 0;
-  if (q_start) qs = min(max(q_start[b], 0), N_q);
+  if (!have_kv_qs) {
+    if (seqlens_k) kv = min(max(seqlens_k[b], 0), N_k);
+    if (q_start) qs = min(max(q_start[b], 0), N_q);
+  }
 
   // ---- K/V slice copies: global -> LDS, 1 KB per wave instruction ----
   // Copy q of this wave fills LDS bytes [1024*qi, 1024*qi + 1024) of a stage,

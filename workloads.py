@@ -97,6 +97,12 @@ HBM_PROBES = {
                                         causal=False, seed=1007),
 }
 
+# The varlen workload's shape with every key valid and no masked rows: the
+# reference its effective throughput is compared against (benchmark only).
+REFERENCE = {
+    "dense_n1024_d64": Workload("dense_n1024_d64", B=8, H=32, N_q=1024, N_k=1024, d=64, causal=False, seed=1004),
+}
+
 HEADLINE = "causal_n4096_d128"
 
 
