@@ -524,6 +524,9 @@ def bench_backward(args, torch, ta, w, inp, tensors, sl, qs, stream, dev, bmask=
     ms = total_ms / args.steps
     flops = 2.5 * w.flops() * kept   # five N_q x N_k x d products (S, dP, dV, dK, dQ) against the forward's two
     tflops = flops / (ms * 1e-3) / 1e12
+    varlen = inp.seqlens_k is not None or inp.q_start is not None
+    eff = 2.5 * effective_flops(w, inp) if varlen and bmask is None else None
+    achieved = eff / (ms * 1e-3) / 1e12 if eff is not None else tflops
     result = {
         "metric": BWD_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
@@ -532,8 +535,10 @@ def bench_backward(args, torch, ta, w, inp, tensors, sl, qs, stream, dev, bmask=
                    "varlen": inp.seqlens_k is not None, "pass": "backward",
                    **({"block_sparse": f"density {args.block_density}, kept fraction {kept:.3f}"}
                       if bmask is not None else {})},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        **({"effective": {"flops": eff, "tflops": round(achieved, 2), "fraction_of_nominal": round(eff / (2.5 * w.flops()), 4),
+                          "note": "10*d flops per allowed (query, key) pair"}} if eff is not None else {}),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_bwd_traffic(w.name) if bmask is None else None},
         "launch_ms": launch_stats(total_ms, per, args.steps),
         "warmup_run": {"launches": n_warm, "seconds": round(warm_s, 3), "min_seconds": args.warmup_min_s},

@@ -101,7 +101,9 @@ CASES = [
     (1, 2, 130, 17, 64, 0, 4),       # fewer keys than one step
     (1, 1, 150, 100, 64, 2, 5),      # bottom-right with N_q > N_k: the first 50 rows see nothing
     (1, 2, 64, 1, 128, 1, 6),
-    (2, 1, 129, 128, 128, 1, 7),     # a 129th row in its own workgroup
+    (2, 1, 129, 128, 128, 1, 7),     # 129 rows in one 256-row workgroup: wave 4 holds one row, waves 5-7 none
+    (1, 2, 520, 520, 128, 1, 8),     # causal d=128 over three 256-row workgroups (the last of 8 rows)
+    (1, 2, 600, 400, 128, 2, 9),     # bottom-right causal d=128, three workgroups, 200 rows see nothing
 ]
 
 
@@ -155,7 +157,7 @@ def test_fp8_full_size_sampled_rows():
     """B=1, H=32, N=4096, d=128 causal, the benchmark's launch; sampled rows."""
     x = make_fp8(1, 32, 4096, 4096, 128, seed=21)
     o, lse = run_gpu(x, 128 ** -0.5, 1)
-    rows = [0, 1, 127, 128, 1000, 2047, 2048, 3333, 4095]
+    rows = [0, 1, 127, 128, 255, 256, 511, 512, 1000, 2047, 2048, 3333, 4095]
     check(o, lse, x, 128 ** -0.5, 1, rows=rows)
 
 
@@ -165,5 +167,5 @@ def test_fp8_large_sampled_rows(B, H, N, d, causal):
     x = make_fp8(B, H, N, N, d, seed=22 + d)
     print(f"fp8 large {(B, H, N, d, causal)}", flush=True)
     o, lse = run_gpu(x, d ** -0.5, causal)
-    rows = sorted({0, 1, 127, 128, 255, N // 2, N - 129, N - 1})
+    rows = sorted({0, 1, 127, 128, 255, 256, 511, 512, N // 2, N - 257, N - 256, N - 129, N - 1})
     check(o, lse, x, d ** -0.5, causal, rows=rows)

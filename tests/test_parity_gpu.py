@@ -117,17 +117,36 @@ RANKED = [
     (65, 1, 40, 128, None, None),
     (7, 3, 600, 128, [600, 17, 600, 0, 333, 600, 17], [0, 0, 500, 0, 0, 599, 3]),
     (5, 2, 300, 64, [300, 300, 300, 300, 300], [0, 64, 0, 64, 300]),
+    # heads over all batches a multiple of 8: whole heads dealt over the XCDs,
+    # several tile pairs per head (4, 2 and 3)
+    (4, 2, 1000, 64, [1000, 333, 700, 1], [0, 0, 100, 0]),
+    (8, 4, 600, 128, None, None),
+    (2, 4, 700, 64, [650, 700], [0, 70]),
 ]
 
 
 @pytest.mark.parametrize("case", RANKED, ids=[f"B{c[0]}_H{c[1]}_N{c[2]}_d{c[3]}" for c in RANKED])
 def test_heaviest_batch_first_order(case):
+    # outputs pre-filled with NaN: a workgroup order that skipped or repeated
+    # a (batch, head, tile pair) would leave NaN behind
+    import tiled_attention_16_amd as ta
     B, H, n, d, sl, qs = case
     q, k, v = make_random(B, H, n, n, d, seed=B * 7 + n + d)
     rng = np.random.default_rng(B + n)
     seqlens = np.array(sl, np.int32) if sl is not None else rng.choice([1, n // 3, n // 2, n], size=B).astype(np.int32)
     qstart = np.array(qs, np.int32) if qs is not None else None
-    compare_full(q, k, v, np.float32(d ** -0.5), False, seqlens, qstart)
+    out = torch.full((B, H, n, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, n), float("nan"), dtype=torch.float32, device="cuda")
+    print(f"  ranked B,H,N,d={B},{H},{n},{d}", flush=True)
+    ta.attn_fwd(to_dev(q), to_dev(k), to_dev(v), causal=False, seqlens_k=torch.from_numpy(seqlens).cuda(),
+                q_start=torch.from_numpy(qstart).cuda() if qstart is not None else None, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any().item() and not torch.isnan(lse).any().item()
+    ro, rl = attention(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), float(np.float32(d ** -0.5)),
+                       False, seqlens_k=seqlens, q_start=qstart)
+    r = check(bf16_bits_to_f64(bits_of(out)), ro, lse.cpu().numpy(), rl)
+    print("  ", r, flush=True)
+    assert r.ok, str(r)
 
 
 def test_padding_contents_never_used():

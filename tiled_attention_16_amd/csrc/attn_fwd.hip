@@ -255,8 +255,11 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
     // batch are equal. Rank the batches by their work, valid keys times rows
     // that attend (ties by index), and hand out the workgroups heaviest batch
     // first: the dispatcher starts workgroups in id order and refills free
-    // slots in the same order, so this is a longest-first schedule. Ids stay
-    // dealt round-robin over the XCDs, which then all get a mix of batches.
+    // slots in the same order, so this is a longest-first schedule. Ids are
+    // dealt round-robin over the 8 XCDs; when the head count allows, whole
+    // heads are dealt that way (all n_pairs workgroups of a head on one XCD,
+    // one after another, so its K/V is fetched into one L2) while every XCD
+    // still gets the same mix of batches.
     long long wl = -1;   // lane l: the work of batch l
     int kv_l = N_k, qs_l = 0;
     if (lane < n_b) {
@@ -270,10 +273,17 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
                            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)wl, j);
       rank += (wj > wl || (wj == wl && j < lane)) ? 1 : 0;
     }
-    const int r0 = blockIdx.x / per_b;                 // this workgroup's batch rank
+    // j: position in the heaviest-first order (batch rank, head, tile pair)
+    int j = blockIdx.x;
+    if (((n_b * H) & 7) == 0) {
+      const int x = j & 7, sx = j >> 3;                 // XCD, position within it
+      const int gx = sx / n_pairs;
+      j = ((gx << 3) + x) * n_pairs + (sx - gx * n_pairs);
+    }
+    const int r0 = j / per_b;                          // this workgroup's batch rank
     const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < n_b && rank == r0);
     const int b_r = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
-    const int rem = blockIdx.x - r0 * per_b;
+    const int rem = j - r0 * per_b;
     bh = b_r * H + rem / n_pairs;
     pr = rem % n_pairs;
     kv = __builtin_amdgcn_readlane(kv_l, b_r);
@@ -432,8 +442,8 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
   k_rsrc[2] = v_rsrc[2] = __builtin_amdgcn_readfirstlane(kv_end * T::kRowBytes);
   asm volatile("" : "+s"(k_rsrc), "+s"(v_rsrc));
 
-  // This wave's rows: row_lo .. row_lo + 63, as MFMA blocks rb = 0, 1 of 32
-  // rows; lane L holds row row_lo + 32*rb + L%32 of block rb.
+  // This wave's rows: row_lo .. row_lo + 31, one MFMA block of 32 rows; lane L
+  // holds row row_lo + L%32 (lanes L and L+32 split that row's keys).
   const int row_lo = q0 + kRows * wave;
   const int row_hi = min(row_lo + kRows - 1, N_q - 1);
   const bool wave_live = row_lo < N_q && row_hi >= qs;
