@@ -269,6 +269,12 @@ def run_probes(torch):
                 ms, cyc, clk = one(0, op, nv, 256 * waves, iters // 2)
                 row[str(nv)] = round(cyc / (iters // 2 * 4 * waves), 2)
             out[f"cycles_per_mfma_per_simd_with_n_{name}_after_each_{waves}wave_per_simd"] = row
+    for waves in (1, 2):
+        ms, cyc, clk = one(3, 0, 0, 256 * waves, iters)
+        flops = n_cu * 4 * waves * iters * 4 * 16384.0
+        out[f"mfma16x16x32_only_{waves}wave_per_simd"] = {
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1), "clock_ghz": round(clk / 1e9, 3),
+            "cycles_per_mfma_per_simd": round(cyc / (iters * 4 * waves), 2)}
     for op, name in valu:
         ms, cyc, clk = one(1, op, 32, 256, iters // 4)
         c1 = cyc / (iters // 4 * 32)

@@ -10,8 +10,12 @@
 //            v_exp_f32, v_cvt_pk_bf16_f32 or v_add_f32) issued after each
 //            MFMA: the MFMA-only rate and how much VALU work an MFMA hides;
 //   valu     32 of one of those VALU instructions per loop step, no MFMA;
+//   mfma16   back-to-back v_mfma_f32_16x16x32_bf16 on four independent
+//            accumulators (half the flops of the 32x32x16 form per instruction);
 //   lds      ds_read_b128 or ds_read_b64_tr_b16 streams over a 64 KB LDS
-//            buffer, bank-conflict free, eight reads in flight per wave.
+//            buffer, bank-conflict free, eight reads in flight per wave; the
+//            buffer holds distinct words and the reads are summed, so no read
+//            can be dropped.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -83,6 +87,33 @@ __global__ __launch_bounds__(512) void probe_mfma_kernel(int iters, unsigned lon
   if (s == 12345.f) sink[threadIdx.x] = s;   // never true for these inputs; keeps the work alive
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(512) void probe_mfma16_kernel(int iters, unsigned long long* t, float* sink) {
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = (f32x4){};
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (threadIdx.x & 7));
+    b[i] = (__bf16)(0.002f * i);
+  }
+  __syncthreads();
+  stamp(t, 0);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc[j]) : "a"(a), "a"(b));
+  }
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __syncthreads();
+  stamp(t, 1);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) s += acc[j][threadIdx.x & 3];
+  if (s == 12345.f) sink[threadIdx.x] = s;   // never true for these inputs; keeps the work alive
+}
+
 template <int NV, int Op>
 __global__ __launch_bounds__(512) void probe_valu_kernel(int iters, unsigned long long* t, float* sink) {
   float x[8];
@@ -105,27 +136,28 @@ __global__ __launch_bounds__(512) void probe_valu_kernel(int iters, unsigned lon
 template <bool Tr>
 __global__ __launch_bounds__(512) void probe_lds_kernel(int iters, unsigned long long* t, float* sink) {
   __shared__ __attribute__((aligned(1024))) char buf[65536];
-  for (int i = threadIdx.x; i < 65536 / 16; i += blockDim.x) *(lds_u32x4*)(buf + 16 * i) = (u32x4){1u, 2u, 3u, 4u};
+  for (int i = threadIdx.x; i < 65536 / 16; i += blockDim.x)
+    *(lds_u32x4*)(buf + 16 * i) = (u32x4){4u * i + 1u, 4u * i + 2u, 4u * i + 3u, 4u * i + 4u};
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   u32x4 acc = {0u, 0u, 0u, 0u};
   stamp(t, 0);
   for (int it = 0; it < iters; ++it) {
-    const int base = ((it * 8 + wave) & 7) * 8192;
+    const int base = ((it + wave) & 7) * 8192;   // a different 8 KB block every step
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if constexpr (Tr) {
         const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + base + j * 1024 + 8 * lane));
-        acc[j & 3] ^= __builtin_bit_cast(uint2, v).x;
+        acc[j & 3] += __builtin_bit_cast(uint2, v).x;
       } else {
-        acc ^= *(const lds_u32x4*)(buf + base + j * 1024 + 16 * lane);
+        acc += *(const lds_u32x4*)(buf + base + j * 1024 + 16 * lane);
       }
     }
   }
   __syncthreads();
   stamp(t, 1);
-  if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x9e3779b9u) sink[threadIdx.x] = 1.f;
+  if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x9e3779b9u) sink[threadIdx.x] = 1.f;   // keeps every read
 }
 
 template <typename K>
@@ -137,7 +169,7 @@ int run(K kern, int blocks, int threads, int iters, unsigned long long* t, float
 
 }  // namespace
 
-// kind: 0 mfma, 1 valu, 2 lds. op (mfma, valu): 0 v_fma_f32, 1 v_exp_f32,
+// kind: 0 mfma, 1 valu, 2 lds, 3 mfma16 (op and nv 0). op (mfma, valu): 0 v_fma_f32, 1 v_exp_f32,
 // 2 v_cvt_pk_bf16_f32, 3 v_add_f32; (lds) 0 ds_read_b128, 1
 // ds_read_b64_tr_b16. nv: VALU instructions after each MFMA (mfma: 0, 2, 4,
 // 6, 8) or per loop step (valu: 32). t: device, 4 * blocks unsigned 64-bit
@@ -179,5 +211,6 @@ extern "C" int attn_probe(int kind, int op, int nv, int blocks, int threads, int
   }
   if (kind == 2) return run(op == 1 ? probe_lds_kernel<true> : probe_lds_kernel<false>, blocks, threads, iters, t, sink,
                             stream);
+  if (kind == 3) return run(probe_mfma16_kernel, blocks, threads, iters, t, sink, stream);
   return 1;
 }
