@@ -166,8 +166,10 @@ __device__ __forceinline__ float lane_swap_add(float x) {
 }
 
 // MFMA 32x32x16 bf16 -> fp32, issued as inline assembly so that each
-// operand's register class is fixed: the scores and the output accumulator
-// in VGPRs (the VALU reads them), the K, V and Q operands in AGPRs.
+// operand's register class is fixed: every operand and accumulator in VGPRs.
+// A kernel that uses no AGPRs gets the whole 256-register budget of two waves
+// per SIMD as VGPRs; with the K, V and Q operands in AGPRs the budget was
+// split 128/128 and spilled operand offsets cost a v_accvgpr_read each per step.
 // The compiler does not know these are MFMAs, so the code itself places the
 // wait states an MFMA result needs before anything else reads it
 // (mfma_result_wait). An MFMA must also not read a register in the 2 wait
@@ -177,16 +179,16 @@ __device__ __forceinline__ float lane_swap_add(float x) {
 // on the compiled code (tiled_attention_16_amd/hazards.py).
 template <bool Pad>
 __device__ __forceinline__ void mfma_v_init(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  if constexpr (Pad) asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "a"(a), "a"(b));
-  else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "a"(a), "a"(b));
+  if constexpr (Pad) asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
 template <bool Pad>
 __device__ __forceinline__ void mfma_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  if constexpr (Pad) asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "a"(a), "a"(b));
-  else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "a"(a), "a"(b));
+  if constexpr (Pad) asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_a(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "a"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 // 24 wait states: more than a 32x32 MFMA result needs before another
 // instruction may read it.
