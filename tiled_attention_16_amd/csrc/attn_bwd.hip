@@ -120,14 +120,14 @@ __device__ __forceinline__ bf16x8 read_row(const char* blk, const Offs<D>& o, in
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kDepth = 4;   // ring depth in blocks: copies run three blocks ahead
 
-template <int D>
+template <int D, int W = kWaves>   // W: waves of the workgroup that share the copies
 struct Ring {
   static constexpr int kBlkBytes = kBlk * 2 * D;
   static constexpr int kKB = kBlkBytes / 1024;        // copies per matrix block
   static constexpr int kRowsPerKB = 1024 / (2 * D);
   static constexpr int kLanesPerRow = 64 / kRowsPerKB;
-  static constexpr int kCpw = 2 * kKB / kWaves;       // copies per wave per block (two matrices)
-  static_assert((2 * kKB) % kWaves == 0, "copies must split evenly over the waves");
+  static constexpr int kCpw = 2 * kKB / W;            // copies per wave per block (two matrices)
+  static_assert((2 * kKB) % W == 0, "copies must split evenly over the waves");
 };
 
 // Raw buffer descriptor over [base, base + bytes): lanes whose offset is at
@@ -151,6 +151,15 @@ __device__ __forceinline__ void copy_kb(const i32x4& rs, uint32_t soff, uint32_t
   // (the add after the M0 write is the wait state the LDS copy needs)
   asm volatile("s_mov_b32 m0, %1\n\tv_add_u32 %0, %2, %3\n\tbuffer_load_dwordx4 %0, %4, 0 offen lds"
                : "=&v"(v) : "s"(lds), "s"(soff), "v"(off), "s"(rs) : "memory", "m0");
+}
+
+// copy_kb with lane offset 16*lane, computed from the lane id inside the
+// block, so that no register has to hold it across a loop.
+__device__ __forceinline__ void copy_kb_lane16(const i32x4& rs, uint32_t soff, uint32_t lds) {
+  uint32_t v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0\n\tv_lshlrev_b32 %0, 4, %0\n\t"
+               "s_mov_b32 m0, %1\n\tv_add_u32 %0, %2, %0\n\tbuffer_load_dwordx4 %0, %3, 0 offen lds"
+               : "=&v"(v) : "s"(lds), "s"(soff), "s"(rs) : "memory", "m0");
 }
 
 // vmcnt(0) as a builtin the compiler sees: the register loads issued before
@@ -451,7 +460,11 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
   }
 }
 
-// ---------------------------------------------------------------- dk, dv
+// ---------------------------------------------------------------- dk, dv (d = 64)
+// At d = 64 a block carries half the MFMA work of d = 128 but the same
+// softmax work, and this kernel's software pipeline (the next block's S and
+// dP on the MFMA unit while the VALU turns this block's into P and dS)
+// measured faster than two waves per SIMD without it (attn_bwd_dkdv_kernel).
 // Dense: as in the dQ kernel; each wave copies, per block, the words of the
 // block's 32 rows that hold its own 32 keys.
 // Mode 2 (Sparse): the WG's 128 keys are one key block of the mask; it walks
@@ -459,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
 // list entry carries the query block and a mask of the waves that take part
 // (all of them: the key block is the WG's).
 template <int D, int Mode>   // 0: rules only; 1: dense mask (Dense); 2: block-sparse (Sparse)
-__global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_pipe_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const f32x2* __restrict__ stats, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int H, int N_q, int N_k, float c, float scale, int causal, int coff,
@@ -756,6 +769,297 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(
   }
 }
 
+// ---------------------------------------------------------------- dk, dv
+// d = 128: one workgroup of 8 wave64s per 256 keys, 32 keys per wave. A wave keeps its
+// keys' K in registers as B operands and the dK, dV accumulators; its keys'
+// V stays in LDS (a 32-row block per wave, copied once) and is read as the B
+// operand of dP. That keeps a wave within the 256 registers of two waves per
+// SIMD, so one wave's softmax work and waits run under the other's MFMAs.
+// Dense: as in the dQ kernel; each wave copies, per block, the words of the
+// block's 32 rows that hold its own 32 keys.
+// Mode 2 (Sparse): each group of 4 waves (128 keys) is one key block of the
+// mask; the WG walks the 32-row query blocks of the 256-row tiles that keep
+// any of its blocks. Each list entry carries the query block and a mask of
+// the waves that take part.
+constexpr int kWavesKV = 8;
+constexpr int kTileKV = kBlk * kWavesKV;   // keys per dK/dV workgroup (d = 128)
+
+template <int D, int Mode>   // 0: rules only; 1: dense mask (Dense); 2: block-sparse (Sparse)
+__global__ __launch_bounds__(64 * kWavesKV) void attn_bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const f32x2* __restrict__ stats, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, int H, int N_q, int N_k, float c, float scale, int causal, int coff,
+    const int32_t* __restrict__ seqlens_k, const int32_t* __restrict__ q_start, int n_kt, DenseMask dm,
+    BlockMask bmk) {
+  constexpr bool Dense = Mode == 1, Sparse = Mode == 2;
+  static_assert(D == 128, "d = 64 runs attn_bwd_dkdv_pipe_kernel");
+  constexpr int kThreadsKV = 64 * kWavesKV;
+  using R = Ring<D, kWavesKV>;
+  constexpr int kMaskBytes = Dense ? kWavesKV * 256 : 0;
+  // [Q block][dO block][stats of the 32 rows][mask words of each wave]
+  constexpr int kStage = 2 * R::kBlkBytes + 1024 + kMaskBytes;
+  constexpr int kCpb = R::kCpw + (Dense ? 1 : 0);   // copies per wave per block (wave 0: one more)
+  constexpr int kVBytes = kWavesKV * R::kBlkBytes;   // the workgroup's V, a block per wave
+  constexpr int kListBytes = Sparse ? 4 * (kMaxSparse + kListPad + 4) : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[kDepth * kStage + kVBytes + kListBytes];
+  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  // Under a causal mask early key tiles have the most rows: tile-major order,
+  // heaviest first across all heads (see the dq kernel).
+  const int n_bh = (int)(gridDim.x / n_kt);
+  const int bh = causal ? (int)(blockIdx.x % n_bh) : (int)(blockIdx.x / n_kt);
+  const int kt = causal ? (int)(blockIdx.x / n_bh) : (int)(blockIdx.x % n_kt);
+  const int b = bh / H;
+  int kv = N_k;
+  if (seqlens_k) kv = min(max(seqlens_k[b], 0), N_k);
+  int qs = 0;
+  if (q_start) qs = min(max(q_start[b], 0), N_q);
+  const size_t q_base = (size_t)bh * N_q * D, k_base = (size_t)bh * N_k * D;
+  const int k0 = kt * kTileKV;
+  // query rows that can see a key of this tile: [r_begin, N_q)
+  int r_begin = max(qs, causal ? max(k0 - coff, 0) : 0);   // row i sees keys <= i + coff
+  if (k0 >= kv) r_begin = N_q;                  // every key of the tile is masked
+  const int blk0 = r_begin / kBlk;
+  int nblk = r_begin < N_q ? (N_q + kBlk - 1) / kBlk - blk0 : 0;
+  // Sparse: list entries blk | (wave mask << 24) of the kept query blocks,
+  // padded with the block past the last row (its copies fetch nothing)
+  [[maybe_unused]] int* lst = (int*)(smem + kDepth * kStage + kVBytes);
+  if constexpr (Sparse) {
+    const int nbq = (N_q + kBlk - 1) / kBlk;   // 32-row query blocks of the head
+    if (wave == 0) {
+      const uint8_t* fl = bmk.flags + (size_t)b * bmk.sb + (size_t)(bh - b * H) * bmk.sh;
+      const int kb0 = kt * (kWavesKV / 4);     // the tile's 128-key blocks of the mask: 4 waves each
+      int base = 0;
+      for (int t0 = blk0 / 8; t0 * 8 < nbq && nblk > 0; t0 += 64) {   // 256-row tiles, one per lane
+        const int t = t0 + lane;
+        uint32_t wm = 0;
+        if (t * 8 < nbq) {
+#pragma unroll
+          for (int kb = 0; kb < kWavesKV / 4; ++kb)
+            if (kb0 + kb < bmk.n_ks && fl[(size_t)t * bmk.n_ks + kb0 + kb] != 0) wm |= 0x0fu << (4 * kb);
+        }
+        const int lo = max(8 * t, blk0), hi = min(8 * t + 8, nbq);
+        const int cnt = (wm != 0 && hi > lo) ? hi - lo : 0;
+        int incl = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int x = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += x;
+        }
+        int pos = base + incl - cnt;
+        for (int q = lo; q < lo + cnt; ++q) lst[pos++] = q | (int)(wm << 24);
+        base += __shfl(incl, 63, 64);
+      }
+      if (lane < kListPad) lst[base + lane] = nbq;
+      if (lane == 0) lst[kMaxSparse + kListPad] = base;
+    }
+    __syncthreads();
+    nblk = __builtin_amdgcn_readfirstlane(lst[kMaxSparse + kListPad]);
+  }
+  // first query row of ring position n, and whether this wave's slice takes part
+  auto row0_of = [&](int n) __attribute__((always_inline)) {
+    if constexpr (Sparse) return (__builtin_amdgcn_readfirstlane(lst[n]) & 0xffffff) * kBlk;
+    else return (blk0 + n) * kBlk;
+  };
+  auto wave_in = [&](int n) __attribute__((always_inline)) {
+    if constexpr (Sparse) return ((__builtin_amdgcn_readfirstlane(lst[n]) >> (24 + wave)) & 1) != 0;
+    else return true;
+  };
+
+  const int wkey0 = k0 + kBlk * wave;   // this wave's first key
+  const int key = wkey0 + (lane & 31);
+  const bool key_ok = key < N_k, key_live = key < kv;
+  const bool wkey_live = wkey0 + kBlk <= kv;   // all 32 keys of the wave are valid
+  bf16x8 kr[D / 16];   // this key's K as B operands (zeros past the valid length)
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) {
+    u32x4 a = {0u, 0u, 0u, 0u};
+    if (key_live) a = *(const u32x4*)(K + k_base + (size_t)key * D + kc * 16 + hf * 8);
+    kr[kc] = __builtin_bit_cast(bf16x8, a);
+  }
+
+  wait_loads();
+  // Rows past N_q (and keys past kv) fetch nothing: zero the ring and the V
+  // blocks once, so such rows hold zeros or rows of an earlier block (finite)
+  // and are masked out below.
+  for (int i = tid; i < (kDepth * kStage + kVBytes) / 16; i += kThreadsKV)
+    *(lds_u32x4*)(smem + 16 * i) = (u32x4){0u, 0u, 0u, 0u};
+  __syncthreads();
+  const uint32_t rows_bytes = (uint32_t)N_q * 2 * D;
+  const i32x4 q_rs = rsrc(Q + q_base, rows_bytes), g_rs = rsrc(dO + q_base, rows_bytes);
+  const i32x4 s_rs = rsrc(stats + (size_t)bh * N_q, (uint32_t)N_q * 8);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  // this wave's 32 keys of V into its LDS block (keys past kv fetch nothing);
+  // awaited by the first block's wait below (copies complete in issue order)
+  const char* vblk = smem + kDepth * kStage + wave * R::kBlkBytes;
+  {
+    const i32x4 v_rs = rsrc(V + k_base, (uint32_t)kv * 2 * D);
+    const uint32_t vl = lds0 + kDepth * kStage + wave * R::kBlkBytes;
+#pragma unroll
+    for (int ci = 0; ci < R::kKB; ++ci)
+      copy_kb(v_rs, (uint32_t)wkey0 * 2 * D, copy_lane_off<D>(ci, lane), vl + ci * 1024);
+  }
+  int cpoff[R::kCpw];
+#pragma unroll
+  for (int i = 0; i < R::kCpw; ++i) cpoff[i] = copy_lane_off<D>(wave * R::kCpw + i, lane);
+  // the stats copy (wave 0): lane L brings bytes 16L .. 16L+15 from the
+  // block's first row on, into the stage's 1 KB stats area; the first 256
+  // bytes are the block's 32 rows, the rest (later rows, or nothing past N_q)
+  // is never read. Its lane offset is made inside the copy (kept in a
+  // register across the loop, it was spilled and reloaded with a full vmcnt
+  // wait).
+  // Dense: lane L < 32 brings, for row r0 + L, the word that holds this wave's keys
+  [[maybe_unused]] i32x4 m_rs = {0, 0, 0, 0};
+  [[maybe_unused]] uint32_t m_off = 0;
+  if constexpr (Dense) {
+    m_rs = rsrc(dm.bits + (size_t)b * dm.sb + (size_t)(bh - b * H) * dm.sh, (uint32_t)N_q * dm.rw * 4);
+    m_off = lane < 32 ? (uint32_t)lane * dm.rw * 4 + (uint32_t)(wkey0 >> 5) * 4 : 0x40000000u;
+  }
+  auto issue = [&](int n) {   // the block of ring position n into stage n % kDepth
+    const uint32_t st = lds0 + (uint32_t)(n % kDepth) * kStage;
+    const uint32_t r0 = (uint32_t)row0_of(n);
+#pragma unroll
+    for (int i = 0; i < R::kCpw; ++i) {
+      const int ci = wave * R::kCpw + i;
+      const bool is_g = ci >= R::kKB;
+      copy_kb(is_g ? g_rs : q_rs, r0 * 2 * D, cpoff[i], st + (uint32_t)ci * 1024);
+    }
+    if (wave == 0) copy_kb_lane16(s_rs, r0 * 8, st + 2 * R::kBlkBytes);
+    if constexpr (Dense) copy_dw(m_rs, r0 * dm.rw * 4, m_off, st + 2 * R::kBlkBytes + 1024 + wave * 256);
+  };
+  // Block n has landed once at most the `ahead` newest blocks' copies of this
+  // wave are in flight (wave 0 issues one copy more per block).
+  auto wait_block = [&](auto ahead) {
+    constexpr int A = decltype(ahead)::value;
+    if (wave == 0) wait_copies<A * (kCpb + 1)>();
+    else wait_copies<A * kCpb>();
+  };
+  auto stage_of = [&](int n) { return (const char*)smem + (n % kDepth) * kStage; };
+
+  const Offs<D> off(lane);
+  f32x16 adk[D / 32], adv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) adk[db] = adv[db] = (f32x16){};
+  // no mask anywhere in block n for this wave: all its keys are valid, all
+  // rows exist and are past q_start, and (causal) the block starts at or
+  // after the wave's last key
+  auto block_full = [&](int n) {
+    const int r0 = row0_of(n);
+    // one condition (bitwise, not short-circuit): a single branch
+    return wkey_live & (r0 + kBlk <= N_q) & (r0 >= qs) & (!causal | (r0 + coff >= wkey0 + kBlk - 1)) & wave_in(n);
+  };
+
+#pragma unroll
+  for (int n = 0; n < kDepth - 1; ++n) issue(n);
+  for (int n = 0; n < nblk; ++n) {
+    wait_block(std::integral_constant<int, kDepth - 2>{});   // block n (and, before block 0, the V blocks)
+    __syncthreads();   // everyone's copies of block n; block n-1's stage is free
+    issue(n + kDepth - 1);
+    const char* qb = stage_of(n);
+    const char* gb = qb + R::kBlkBytes;
+    // S = Q K^T, then dP = dO V^T (lane = key, 16 query rows per lane); the
+    // operands are read one step ahead of their MFMAs
+    f32x16 s = {}, dp = {};
+    {
+      bf16x8 qa[2];
+      qa[0] = read_row<D>(qb, off, 0);
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) {
+        if (kc + 1 < D / 16) qa[(kc + 1) & 1] = read_row<D>(qb, off, kc + 1);
+        s = mfma(qa[kc & 1], kr[kc], s);
+      }
+    }
+    {
+      bf16x8 ga[2], va[2];
+      ga[0] = read_row<D>(gb, off, 0);
+      va[0] = read_row<D>(vblk, off, 0);
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) {
+        if (kc + 1 < D / 16) {
+          ga[(kc + 1) & 1] = read_row<D>(gb, off, kc + 1);
+          va[(kc + 1) & 1] = read_row<D>(vblk, off, kc + 1);
+        }
+        dp = mfma(ga[kc & 1], va[kc & 1], dp);
+      }
+    }
+    // P and dS, packed as the B operands of the dV and dK products; register
+    // r holds query row r0 + 8*(r/4) + 4*hf + r%4
+    const int r0 = row0_of(n);
+    const char* sb = qb + 2 * R::kBlkBytes;
+    [[maybe_unused]] const bool in = wave_in(n);
+    [[maybe_unused]] const char* mb = sb + 1024 + wave * 256;   // Dense: word of row r0 + t at 4*t
+    uint32_t wp[8], wd[8];
+    const bool full = !Dense && block_full(n);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      // stats of rows 8g + 4hf .. +3: (lse2, D) pairs, 32 bytes
+      const f32x4 s01 = *(const lds_f32x4*)(sb + 8 * (8 * g + 4 * hf));
+      const f32x4 s23 = *(const lds_f32x4*)(sb + 8 * (8 * g + 4 * hf) + 16);
+      const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
+      const float dd[4] = {s01[1], s01[3], s23[1], s23[3]};
+      float p[4], ds[4];
+      if (full) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(s[4 * g + e] * c - l2[e]);
+          ds[e] = p[e] * (dp[4 * g + e] - dd[e]);
+        }
+      } else {
+        // Dense: the words of rows 8g + 4hf .. +3, one 16-byte read
+        [[maybe_unused]] u32x4 mw = {};
+        if constexpr (Dense) mw = *(const lds_u32x4*)(mb + 32 * g + 16 * hf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const int qrow = r0 + 8 * g + 4 * hf + e;
+          bool ok = key_live && qrow < N_q && qrow >= qs && (!causal || key <= qrow + coff);
+          if constexpr (Sparse) ok = ok && in;
+          if constexpr (Dense) ok = ok && ((mw[e] >> (lane & 31)) & 1u);
+          p[e] = ok ? __builtin_amdgcn_exp2f(s[r] * c - l2[e]) : 0.f;
+          ds[e] = ok ? p[e] * (dp[r] - dd[e]) : 0.f;
+        }
+      }
+      wp[2 * g] = pack2(p[0], p[1]);
+      wp[2 * g + 1] = pack2(p[2], p[3]);
+      wd[2 * g] = pack2(ds[0], ds[1]);
+      wd[2 * g + 1] = pack2(ds[2], ds[3]);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by the transposing read)
+    {
+      bf16x8 ta_g[2], ta_q[2];
+      ta_g[0] = read_tr<D>(gb, off, 0, 0);
+      ta_q[0] = read_tr<D>(qb, off, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * (D / 32); ++i) {   // i = cc * (D/32) + db
+        const int cc = i / (D / 32), db = i % (D / 32);
+        if (i + 1 < 2 * (D / 32)) {
+          ta_g[(i + 1) & 1] = read_tr<D>(gb, off, (i + 1) / (D / 32), (i + 1) % (D / 32));
+          ta_q[(i + 1) & 1] = read_tr<D>(qb, off, (i + 1) / (D / 32), (i + 1) % (D / 32));
+        }
+        const bf16x8 bp = __builtin_bit_cast(bf16x8, (u32x4){wp[4 * cc], wp[4 * cc + 1], wp[4 * cc + 2], wp[4 * cc + 3]});
+        const bf16x8 bd = __builtin_bit_cast(bf16x8, (u32x4){wd[4 * cc], wd[4 * cc + 1], wd[4 * cc + 2], wd[4 * cc + 3]});
+        adv[db] = mfma(ta_g[i & 1], bp, adv[db]);
+        adk[db] = mfma(ta_q[i & 1], bd, adk[db]);
+      }
+    }
+  }
+  wait_copies<0>();   // no copy may still be writing LDS when the workgroup ends
+  // register r of block db holds d = 32*db + 8*(r/4) + 4*hf + r%4 of this lane's key
+  if (key_ok) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const size_t at = k_base + (size_t)key * D + 32 * db + 8 * g + 4 * hf;
+        const u32x2 xk = {pack2(adk[db][4 * g] * scale, adk[db][4 * g + 1] * scale),
+                          pack2(adk[db][4 * g + 2] * scale, adk[db][4 * g + 3] * scale)};
+        const u32x2 xv = {pack2(adv[db][4 * g], adv[db][4 * g + 1]), pack2(adv[db][4 * g + 2], adv[db][4 * g + 3])};
+        *(u32x2*)(dK + at) = xk;
+        *(u32x2*)(dV + at) = xv;
+      }
+  }
+}
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   if (!a || !b || na == 0 || nb == 0) return false;
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
@@ -782,10 +1086,11 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
   if (has_q && (!q || !o || !dout || !lse || !dq || (!delta && !own_delta))) return ATTN_ERR_NULL;
   if (has_k && (!k || !v || !dk || !dv)) return ATTN_ERR_NULL;
   if (bh > 0x7fffffffLL) return ATTN_ERR_SHAPE;
-  const long long n_qt = (N_q + kTile - 1) / kTile, n_kt = (N_k + kTile - 1) / kTile;
+  const int tkv = d == 128 ? kTileKV : kTile;   // keys per dK/dV workgroup
+  const long long n_qt = (N_q + kTile - 1) / kTile, n_kt = (N_k + tkv - 1) / tkv;
   if (bh * n_qt > 0x7fffffffLL || bh * n_kt > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   // per-head byte offsets of the copies are 32-bit
-  if ((long long)(N_q + kTile) * d * 2 > 0x7fffffffLL || (long long)(N_k + kTile) * d * 2 > 0x7fffffffLL)
+  if ((long long)(N_q + kTile) * d * 2 > 0x7fffffffLL || (long long)(N_k + tkv) * d * 2 > 0x7fffffffLL)
     return ATTN_ERR_SHAPE;
   const size_t qb = (size_t)bh * N_q * d * 2, kb = (size_t)bh * N_k * d * 2, rb = (size_t)bh * N_q * 4;
   if (((uintptr_t)q | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq) & 15) return ATTN_ERR_ALIGN;
@@ -834,12 +1139,14 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
   }
   if (has_k) {
     const int mode = dm.bits ? 1 : bmk.flags ? 2 : 0;
+    // d = 128: 8-wave workgroups of 256 keys; d = 64: the pipelined 4-wave kernel, 128 keys
     auto kk = d == 128 ? (mode == 1 ? attn_bwd_dkdv_kernel<128, 1> : mode == 2 ? attn_bwd_dkdv_kernel<128, 2>
                                                                                : attn_bwd_dkdv_kernel<128, 0>)
-                       : (mode == 1 ? attn_bwd_dkdv_kernel<64, 1> : mode == 2 ? attn_bwd_dkdv_kernel<64, 2>
-                                                                              : attn_bwd_dkdv_kernel<64, 0>);
-    e = attn_launch::launch(kk, dim3((unsigned)(bh * n_kt)), dim3(kThreads), stream, qp, kp, vp, gp, (const f32x2*)stp,
-                            dkp, dvp, Hi, Nq, Nk, cc, sc, causal01, coff, seqlens_k, q_start, (int)n_kt, dm, bmk);
+                       : (mode == 1 ? attn_bwd_dkdv_pipe_kernel<64, 1> : mode == 2 ? attn_bwd_dkdv_pipe_kernel<64, 2>
+                                                                                   : attn_bwd_dkdv_pipe_kernel<64, 0>);
+    e = attn_launch::launch(kk, dim3((unsigned)(bh * n_kt)), dim3(d == 128 ? 64 * kWavesKV : kThreads), stream, qp, kp,
+                            vp, gp, (const f32x2*)stp, dkp, dvp, Hi, Nq, Nk, cc, sc, causal01, coff, seqlens_k, q_start,
+                            (int)n_kt, dm, bmk);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
   }
   return ATTN_OK;
