@@ -26,6 +26,10 @@ HIPCC_FLAGS = [
     "-shared",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results and operands of the compiler-scheduled (builtin) MFMAs in
+    # VGPRs: a kernel that uses no AGPRs gets the whole register budget as
+    # VGPRs instead of a fixed VGPR/AGPR split, and needs no v_accvgpr moves
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
 ]
 
 
