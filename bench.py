@@ -52,8 +52,25 @@ HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, published
 METRIC = "attention fwd TFLOP/s (bf16, causal, N=4096, d=128) + % of MFMA bf16 peak"
 HBM_METRIC = "attention fwd achieved HBM GB/s (bf16, short sequences) + % of HBM peak"
 FP8_METRIC = "attention fwd TFLOP/s (FP8 E4M3 operands, causal, N=4096, d=128) + % of MFMA fp8 peak"
+
+
+def fp8_metric_of(w) -> str:
+    """The metric string of an FP8 forward line (the headline shape's is FP8_METRIC)."""
+    if w.name == HEADLINE:
+        return FP8_METRIC
+    mask = "causal" if w.causal else "non-causal"
+    return f"attention fwd TFLOP/s (FP8 E4M3 operands, {mask}, B={w.B}, H={w.H}, N={w.N_q}, d={w.d}) + % of MFMA fp8 peak"
 MFMA_FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, published
 BWD_METRIC = "attention bwd TFLOP/s (bf16, dQ dK dV, counted 10*B*H*N_q*N_k*d, halved when causal) + % of MFMA bf16 peak"
+
+
+def bwd_metric_of(w) -> str:
+    """The metric string of a backward line (the headline shape's is BWD_METRIC)."""
+    if w.name == HEADLINE:
+        return BWD_METRIC
+    mask = "causal" if w.causal else ("varlen" if w.seqlens_range is not None else "non-causal")
+    return (f"attention bwd TFLOP/s (bf16, dQ dK dV, {mask}, B={w.B}, H={w.H}, N={w.N_q}, d={w.d}, "
+            f"counted 10*B*H*N_q*N_k*d, halved when causal) + % of MFMA bf16 peak")
 KERNEL_SRC = os.path.join(ROOT, "tiled_attention_16_amd", "csrc", "attn_fwd.hip")
 BWD_SRC = os.path.join(ROOT, "tiled_attention_16_amd", "csrc", "attn_bwd.hip")
 FP8_SRC = os.path.join(ROOT, "tiled_attention_16_amd", "csrc", "attn_fwd_fp8.hip")
@@ -470,7 +487,7 @@ def bench_fp8(args, torch, ta, w, dev):
     ms_per_step = total_ms / args.steps
     tflops = w.flops() / (ms_per_step * 1e-3) / 1e12
     result = {
-        "metric": FP8_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "metric": fp8_metric_of(w), "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
         "config": {"workload": w.name + "_fp8", "B": w.B, "H": w.H, "N_q": w.N_q, "N_k": w.N_k, "d": w.d,
@@ -534,7 +551,7 @@ def bench_backward(args, torch, ta, w, inp, tensors, sl, qs, stream, dev, bmask=
     eff = 2.5 * effective_flops(w, inp) if varlen and bmask is None else None
     achieved = eff / (ms * 1e-3) / 1e12 if eff is not None else tflops
     result = {
-        "metric": BWD_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "metric": bwd_metric_of(w), "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.N_q, "N_k": w.N_k, "d": w.d, "causal": w.causal,

@@ -39,3 +39,19 @@ def test_every_workload_has_its_own_metric():
     names = {bench.metric_of(w) for w in WORKLOADS.values()}
     assert len(names) == len(WORKLOADS)
     assert bench.metric_of(WORKLOADS[HEADLINE]) == bench.METRIC
+
+
+def test_every_fp8_workload_has_its_own_metric():
+    from workloads import HEADLINE, WORKLOADS
+    fixed = [w for w in WORKLOADS.values() if w.seqlens_range is None]
+    names = {bench.fp8_metric_of(w) for w in fixed}
+    assert len(names) == len(fixed)
+    assert bench.fp8_metric_of(WORKLOADS[HEADLINE]) == bench.FP8_METRIC
+    assert "non-causal" in bench.fp8_metric_of(WORKLOADS["noncausal_n4096_d128"])
+
+
+def test_every_backward_workload_has_its_own_metric():
+    from workloads import HEADLINE, WORKLOADS
+    names = {bench.bwd_metric_of(w) for w in WORKLOADS.values()}
+    assert len(names) == len(WORKLOADS)
+    assert bench.bwd_metric_of(WORKLOADS[HEADLINE]) == bench.BWD_METRIC
