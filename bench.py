@@ -286,6 +286,11 @@ def run_probes(torch):
                 ms, cyc, clk = one(0, op, nv, 256 * waves, iters // 2)
                 row[str(nv)] = round(cyc / (iters // 2 * 4 * waves), 2)
             out[f"cycles_per_mfma_per_simd_with_n_{name}_after_each_{waves}wave_per_simd"] = row
+    for chains in (1, 2):
+        for waves in (1, 2):
+            ms, cyc, clk = one(4, chains, 0, 256 * waves, iters)
+            out[f"mfma_{chains}_dependent_chain_{waves}wave_per_simd"] = {
+                "cycles_per_mfma_per_simd": round(cyc / (iters * 4 * waves), 2), "clock_ghz": round(clk / 1e9, 3)}
     for waves in (1, 2):
         ms, cyc, clk = one(3, 0, 0, 256 * waves, iters)
         flops = n_cu * 4 * waves * iters * 4 * 16384.0

@@ -10,6 +10,8 @@
 //            v_exp_f32, v_cvt_pk_bf16_f32 or v_add_f32) issued after each
 //            MFMA: the MFMA-only rate and how much VALU work an MFMA hides;
 //   valu     32 of one of those VALU instructions per loop step, no MFMA;
+//   chain    v_mfma_f32_32x32x16_bf16 accumulating into one accumulator (a
+//            dependent chain) or two in turn;
 //   mfma16   back-to-back v_mfma_f32_16x16x32_bf16 on four independent
 //            accumulators (half the flops of the 32x32x16 form per instruction);
 //   lds      ds_read_b128 or ds_read_b64_tr_b16 streams over a 64 KB LDS
@@ -84,6 +86,36 @@ __global__ __launch_bounds__(512) void probe_mfma_kernel(int iters, unsigned lon
   for (int j = 0; j < 4; ++j) s += acc[j][threadIdx.x & 15];
 #pragma unroll
   for (int i = 0; i < 8; ++i) s += x[i];
+  if (s == 12345.f) sink[threadIdx.x] = s;   // never true for these inputs; keeps the work alive
+}
+
+// iters steps of 4 MFMAs that all accumulate into `Acc` independent
+// accumulators in turn (Acc = 1: one dependent chain, each MFMA reads the
+// previous one's result as its C operand; Acc = 2: two interleaved chains).
+template <int Acc>
+__global__ __launch_bounds__(512) void probe_mfma_chain_kernel(int iters, unsigned long long* t, float* sink) {
+  f32x16 acc[Acc];
+#pragma unroll
+  for (int j = 0; j < Acc; ++j) acc[j] = (f32x16){};
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (threadIdx.x & 7));
+    b[i] = (__bf16)(0.002f * i);
+  }
+  __syncthreads();
+  stamp(t, 0);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc[j % Acc]) : "a"(a), "a"(b));
+  }
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __syncthreads();
+  stamp(t, 1);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < Acc; ++j) s += acc[j][threadIdx.x & 15];
   if (s == 12345.f) sink[threadIdx.x] = s;   // never true for these inputs; keeps the work alive
 }
 
@@ -169,7 +201,7 @@ int run(K kern, int blocks, int threads, int iters, unsigned long long* t, float
 
 }  // namespace
 
-// kind: 0 mfma, 1 valu, 2 lds, 3 mfma16 (op and nv 0). op (mfma, valu): 0 v_fma_f32, 1 v_exp_f32,
+// kind: 0 mfma, 1 valu, 2 lds, 3 mfma16 (op and nv 0), 4 dependent MFMA chains (op: 1 or 2 chains). op (mfma, valu): 0 v_fma_f32, 1 v_exp_f32,
 // 2 v_cvt_pk_bf16_f32, 3 v_add_f32; (lds) 0 ds_read_b128, 1
 // ds_read_b64_tr_b16. nv: VALU instructions after each MFMA (mfma: 0, 2, 4,
 // 6, 8) or per loop step (valu: 32). t: device, 4 * blocks unsigned 64-bit
@@ -212,5 +244,7 @@ extern "C" int attn_probe(int kind, int op, int nv, int blocks, int threads, int
   if (kind == 2) return run(op == 1 ? probe_lds_kernel<true> : probe_lds_kernel<false>, blocks, threads, iters, t, sink,
                             stream);
   if (kind == 3) return run(probe_mfma16_kernel, blocks, threads, iters, t, sink, stream);
+  if (kind == 4) return run(op == 2 ? probe_mfma_chain_kernel<2> : probe_mfma_chain_kernel<1>, blocks, threads, iters, t,
+                            sink, stream);
   return 1;
 }
