@@ -17,9 +17,11 @@
 //            P    = exp2(S c - LSE log2 e), 0 where masked
 //            dS   = P (dP - D)
 //            dQ^T += K^T dS^T      (MFMA, K^T by the transposing LDS read)
-//   dkdv   one workgroup of 4 wave64s per 128 keys; each wave keeps its 32
-//          keys of K and V in registers and walks the 32-row Q blocks that
-//          can see them (Q, dO and the rows' (LSE, D) through the LDS ring):
+//   dkdv   (d = 128) one workgroup of 8 wave64s per 256 keys; each wave keeps
+//          its 32 keys of K in registers and of V in an LDS block, and walks
+//          the 32-row Q blocks that can see them (Q, dO and the rows' (LSE, D)
+//          through the LDS ring); (d = 64) 4 wave64s per 128 keys, K and V in
+//          registers, software pipelined across blocks:
 //            S  = Q K^T, dP = dO V^T   (lane = key, 16 query rows per lane)
 //            P, dS as above
 //            dV^T += dO^T P,  dK^T += Q^T dS   (dO^T, Q^T by the transposing read)
