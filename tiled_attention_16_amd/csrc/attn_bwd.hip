@@ -9,7 +9,7 @@
 //   delta  per row (LSE * log2 e, D_i) with D_i = sum_d dO_id * O_id (fp32), the
 //          row sum of P * dP that the softmax Jacobian needs
 //          (sum_j P_ij dP_ij = dO_i . O_i).
-//   dq     one workgroup of 4 wave64s per 128 query rows; each wave keeps its
+//   dq     one workgroup of 8 wave64s per 256 query rows; each wave keeps its
 //          32 rows of Q and dO in registers and walks the 32-key blocks its
 //          rows can see (K and V copied straight into a 4-deep LDS ring):
 //            S^T  = K Q^T          (MFMA, lane = query row, 16 keys per lane)
@@ -245,15 +245,21 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const uint16_t* __r
 // its 32 rows' words of the block with the block (one more copy per block).
 // Mode 2 (Sparse): the key slices the block mask keeps for the tile's
 // 256-row block-mask tile are compacted into an LDS list that the ring walks.
+// Waves per dQ workgroup (32 query rows each). Eight waves (256 rows, one
+// workgroup per CU) share one K/V ring: half the copies and LDS writes per
+// flop of two 4-wave workgroups per CU, and measured +0.3 to +2.3 % over them.
+constexpr int waves_q(int) { return 8; }
+
 template <int D, int Mode>   // 0: rules only; 1: dense mask (Dense); 2: block-sparse (Sparse)
-__global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(64 * waves_q(D)) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const f32x2* __restrict__ stats, uint16_t* __restrict__ dQ, int H, int N_q,
     int N_k, float c, float scale, int causal, int coff, const int32_t* __restrict__ seqlens_k,
     const int32_t* __restrict__ q_start, int n_qt, DenseMask dm, BlockMask bmk) {
   constexpr bool Dense = Mode == 1, Sparse = Mode == 2;
-  using R = Ring<D>;
-  constexpr int kMaskBytes = Dense ? kWaves * 256 : 0;
+  constexpr int kWQ = waves_q(D), kThreadsQ = 64 * kWQ, kTileQ = kBlk * kWQ;
+  using R = Ring<D, kWQ>;
+  constexpr int kMaskBytes = Dense ? kWQ * 256 : 0;
   constexpr int kStage = 2 * R::kBlkBytes + kMaskBytes;   // [K block][V block][mask words of each wave]
   constexpr int kCpb = R::kCpw + (Dense ? 1 : 0);         // copies per wave per block
   constexpr int kListBytes = Sparse ? 4 * (kMaxSparse + kListPad + 4) : 0;
@@ -273,8 +279,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
   int qs = 0;
   if (q_start) qs = min(max(q_start[b], 0), N_q);
   const size_t q_base = (size_t)bh * N_q * D, k_base = (size_t)bh * N_k * D;
-  const int q0 = qt * kTile;
-  const int q_end = min(q0 + kTile, N_q);
+  const int q0 = qt * kTileQ;
+  const int q_end = min(q0 + kTileQ, N_q);
   int kv_end = kv;
   if (causal) kv_end = min(kv_end, max(q_end + coff, 0));   // row i sees keys <= i + coff
   if (qs >= q_end) kv_end = 0;
@@ -350,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(
   // Keys past kv_end fetch nothing, so a stage keeps rows no copy wrote: zero
   // the ring once, then such rows hold zeros or keys of an earlier block, all
   // finite, and their probabilities are 0.
-  for (int i = tid; i < kDepth * kStage / 16; i += kThreads) *(lds_u32x4*)(smem + 16 * i) = (u32x4){0u, 0u, 0u, 0u};
+  for (int i = tid; i < kDepth * kStage / 16; i += kThreadsQ) *(lds_u32x4*)(smem + 16 * i) = (u32x4){0u, 0u, 0u, 0u};
   __syncthreads();
   const i32x4 k_rs = rsrc(K + k_base, (uint32_t)kv_end * 2 * D), v_rs = rsrc(V + k_base, (uint32_t)kv_end * 2 * D);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
@@ -1089,10 +1095,11 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
   if (has_k && (!k || !v || !dk || !dv)) return ATTN_ERR_NULL;
   if (bh > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   const int tkv = d == 128 ? kTileKV : kTile;   // keys per dK/dV workgroup
-  const long long n_qt = (N_q + kTile - 1) / kTile, n_kt = (N_k + tkv - 1) / tkv;
+  const int tq = kBlk * waves_q(d);   // query rows per dQ workgroup
+  const long long n_qt = (N_q + tq - 1) / tq, n_kt = (N_k + tkv - 1) / tkv;
   if (bh * n_qt > 0x7fffffffLL || bh * n_kt > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   // per-head byte offsets of the copies are 32-bit
-  if ((long long)(N_q + kTile) * d * 2 > 0x7fffffffLL || (long long)(N_k + tkv) * d * 2 > 0x7fffffffLL)
+  if ((long long)(N_q + 256) * d * 2 > 0x7fffffffLL || (long long)(N_k + tkv) * d * 2 > 0x7fffffffLL)
     return ATTN_ERR_SHAPE;
   const size_t qb = (size_t)bh * N_q * d * 2, kb = (size_t)bh * N_k * d * 2, rb = (size_t)bh * N_q * 4;
   if (((uintptr_t)q | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq) & 15) return ATTN_ERR_ALIGN;
@@ -1135,7 +1142,7 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
                                                                              : attn_bwd_dq_kernel<128, 0>)
                        : (mode == 1 ? attn_bwd_dq_kernel<64, 1> : mode == 2 ? attn_bwd_dq_kernel<64, 2>
                                                                             : attn_bwd_dq_kernel<64, 0>);
-    e = attn_launch::launch(kq, dim3((unsigned)(bh * n_qt)), dim3(kThreads), stream, qp, kp, vp, gp, (const f32x2*)stp,
+    e = attn_launch::launch(kq, dim3((unsigned)(bh * n_qt)), dim3(64 * waves_q(d)), stream, qp, kp, vp, gp, (const f32x2*)stp,
                             dqp, Hi, Nq, Nk, cc, sc, causal01, coff, seqlens_k, q_start, (int)n_qt, dm, bmk);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
   }
@@ -1175,7 +1182,7 @@ extern "C" int attn_bwd_masked(const void* q, const void* k, const void* v, cons
   if ((uintptr_t)mask_bits & 15) return ATTN_ERR_ALIGN;
   if (mask_row_words < (N_k + 31) / 32 || mask_row_words % 8 != 0 || mask_stride_b < 0 || mask_stride_h < 0)
     return ATTN_ERR_MASK;
-  if ((long long)(N_q + kTile) * mask_row_words * 4 > 0x7fffffffLL) return ATTN_ERR_SHAPE;   // 32-bit offsets
+  if ((long long)(N_q + 256) * mask_row_words * 4 > 0x7fffffffLL) return ATTN_ERR_SHAPE;   // 32-bit offsets
   return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N_q, N_k, d, scale, causal, seqlens_k, q_start,
                     DenseMask{mask_bits, mask_stride_b, mask_stride_h, mask_row_words}, BlockMask{nullptr, 0, 0, 0},
                     stream);
