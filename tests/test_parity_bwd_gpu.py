@@ -118,6 +118,28 @@ def test_bwd_every_element_written():
         assert not torch.isnan(t).any().item()
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_padding_keys_never_used(d, causal):
+    # Keys at or past seqlens_k hold NaN (K) and +inf (V): every gradient must
+    # be bit-identical to the run with ordinary values there. Lengths end
+    # inside a 32-key block and inside a 256-key dK/dV tile; N_k spans three
+    # such tiles.
+    B, H, nq, nk = 2, 2, 300, 600
+    q, k, v = make_random(B, H, nq, nk, d, seed=60 + d)
+    g = make_dout((B, H, nq, d), seed=61 + d)
+    seqlens = np.array([290, 531], np.int32)
+    k2, v2 = k.copy(), v.copy()
+    for b, n in enumerate(seqlens):
+        k2[b, :, n:] = 0x7FC0   # NaN
+        v2[b, :, n:] = 0x7F80   # +inf
+    scale = np.float32(d ** -0.5)
+    ref = compare(q, k, v, g, scale, causal, seqlens)
+    got = run_bwd(q, k2, v2, g, scale, causal, seqlens)
+    for x, y in zip(ref, got):
+        np.testing.assert_array_equal(x, y)
+
+
 def test_bwd_repeatable_bitwise():
     q, k, v = make_random(1, 2, 500, 500, 128, seed=47)
     g = make_dout((1, 2, 500, 128), seed=48)
