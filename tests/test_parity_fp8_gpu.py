@@ -62,8 +62,8 @@ def bars(x, scale, causal, rows=None):
     k = e4m3_decode(x.k8) * x.k_descale
     v = np.swapaxes(e4m3_decode(x.vt8), -1, -2) * x.v_descale
     o_ref, lse_ref, p = attention(q, k, v, scale, causal, rows=rows, return_probs=True)
-    a = np.einsum("bhrj,bhjc->bhrc", p, np.abs(v))            # sum_j p_j |v_j| (p sums to 1)
-    t = np.sqrt(np.einsum("bhrj,bhjc->bhrc", p * p, v * v))   # sqrt(sum_j p_j^2 v_j^2)
+    a = p @ np.abs(v)                # sum_j p_j |v_j| (p sums to 1)
+    t = np.sqrt((p * p) @ (v * v))   # sqrt(sum_j p_j^2 v_j^2)
     n = (p > 0).sum(axis=-1, keepdims=True)
     vmax = np.abs(v).max() if v.size else 0.0
     qa = np.abs(q if rows is None else q[:, :, rows])
@@ -72,11 +72,11 @@ def bars(x, scale, causal, rows=None):
         1e-6 * (a + 1e-30)
     rms = 1.5 * (2.0 ** -4 / np.sqrt(3) * np.sqrt(np.mean(t ** 2)) + 2.0 ** -8 / np.sqrt(3) *
                  np.sqrt(np.mean(o_ref ** 2))) + 1e-9
-    return o_ref, lse_ref, elem, rms, mag
+    return o_ref, lse_ref, elem, rms, mag, t
 
 
 def check(o, lse, x, scale, causal, rows=None):
-    o_ref, lse_ref, elem, rms, mag = bars(x, scale, causal, rows)
+    o_ref, lse_ref, elem, rms, mag, _ = bars(x, scale, causal, rows)
     if rows is not None:
         o, lse = o[:, :, rows], lse[:, :, rows]
     assert np.isfinite(o).all()
@@ -147,10 +147,54 @@ def test_fp8_no_keys():
 def test_fp8_matches_oracle_function():
     """The bars' own reference is the oracle's attention_fp8."""
     x = make_fp8(1, 1, 50, 70, 64, seed=15)
-    o_ref, lse_ref, _, _, _ = bars(x, 0.125, 1)
+    o_ref, lse_ref, *_ = bars(x, 0.125, 1)
     o2, l2 = attention_fp8(x.q8, x.k8, x.vt8, 0.125, x.q_descale, x.k_descale, x.v_descale, 1)
     np.testing.assert_allclose(o_ref, o2, rtol=1e-12, atol=1e-15)
     np.testing.assert_allclose(lse_ref, l2, rtol=1e-12)
+
+
+def check_whole(o, lse, x, scale, causal, row_block=1024):
+    """check() over every element of a large output: per (b, h) and row
+    block for the elementwise and LSE bars (the oracle's probabilities of one
+    block at a time), the RMS bar over all elements together."""
+    from workloads import Fp8Inputs
+    B, H, N_q, _ = x.q8.shape
+    err2 = t2 = o2 = 0.0
+    count = 0
+    for b in range(B):
+        for h in range(H):
+            xs = Fp8Inputs(q8=x.q8[b:b + 1, h:h + 1], k8=x.k8[b:b + 1, h:h + 1], vt8=x.vt8[b:b + 1, h:h + 1],
+                           q_descale=x.q_descale, k_descale=x.k_descale, v_descale=x.v_descale)
+            for r0 in range(0, N_q, row_block):
+                rows = np.arange(r0, min(r0 + row_block, N_q))
+                o_ref, lse_ref, elem, _, mag, t = bars(xs, scale, causal, rows)
+                ob, lb = o[b:b + 1, h:h + 1, rows], lse[b:b + 1, h:h + 1, rows]
+                assert np.isfinite(ob).all()
+                err = np.abs(ob - o_ref)
+                worst = np.unravel_index(np.argmax(err - elem), err.shape)
+                assert np.all(err <= elem), f"(b, h) = ({b}, {h}) rows {r0}+: {err[worst]} > {elem[worst]}"
+                dead = np.isneginf(lse_ref)
+                np.testing.assert_array_equal(np.isneginf(lb), dead)
+                lerr = np.abs(lb[~dead] - lse_ref[~dead])
+                assert np.all(lerr <= (1e-3 + 2.0 ** -12 * mag)[~dead])
+                # the RMS model's two terms, summed over every element
+                t2 += float(np.sum(t ** 2))
+                o2 += float(np.sum(o_ref ** 2))
+                err2 += float(np.sum(err ** 2))
+                count += err.size
+    rms_bar = 1.5 * (2.0 ** -4 / np.sqrt(3) * np.sqrt(t2 / count) + 2.0 ** -8 / np.sqrt(3) * np.sqrt(o2 / count)) + 1e-9
+    got = np.sqrt(err2 / count)
+    print(f"   fp8 whole output: RMS error {got:.3e}, bar {rms_bar:.3e}", flush=True)
+    assert got <= rms_bar
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [(1, 32, 4096, 128, 1), (1, 16, 2048, 64, 0)])
+def test_fp8_full_size_every_element(B, H, N, d, causal):
+    """The benchmark's launch (and a non-causal d = 64 one), every element of O and LSE."""
+    x = make_fp8(B, H, N, N, d, seed=21 if d == 128 else 23)
+    print(f"fp8 whole {(B, H, N, d, causal)}", flush=True)
+    o, lse = run_gpu(x, d ** -0.5, causal)
+    check_whole(o, lse, x, d ** -0.5, causal)
 
 
 def test_fp8_full_size_sampled_rows():
