@@ -198,6 +198,8 @@ CONT = [
     (2, 2, 512, 128, False, None, None),
     (2, 1, 768, 64, False, [512, 256], [100, 0]),
     (2, 1, 768, 128, True, [768, 700], [0, 260]),
+    # the first tile sees 16 slices, the second none (q_start past its rows)
+    (1, 2, 512, 128, True, [512], [300]),
 ]
 
 
@@ -308,6 +310,41 @@ def test_full_size_workload_every_element(name):
         assert np.all(np.isfinite(lse))
 
 
+# Rules-only d = 128 launches without per-batch lengths and with more slots
+# (pairs of query tiles) than the GPU has CUs run one workgroup per CU, each
+# walking several slots; a tile that spans whole ring turns fetches the next
+# item's first K/V slices and its Q (the next head's included) while it
+# computes. Compared whole, one batch at a time.
+PERSIST = [
+    # B, H, N_q, N_k, causal     (slots = B*H*ceil(ceil(N_q/256)/2); 256 CUs)
+    (2, 150, 256, 256, 1),       # 300 one-tile slots: every tile continues into the next head's
+    (2, 140, 512, 512, 0),       # 280 two-tile slots, regrouped over the XCDs
+    (1, 130, 600, 768, 0),       # three tiles: two-tile slots and one-tile middle slots, ragged rows
+    (1, 130, 1024, 256, 2),      # bottom-right: a continued tile that sees no key, keyless tiles
+    (1, 300, 300, 300, 1),       # ragged: no tile spans whole ring turns, no continuation
+]
+
+
+@pytest.mark.parametrize("case", PERSIST, ids=[f"{c[0]}x{c[1]}x{c[2]}x{c[3]}_c{c[4]}" for c in PERSIST])
+def test_persistent_grid_every_element(case):
+    B, H, nq, nk, causal = case
+    d = 128
+    q, k, v = make_random(B, H, nq, nk, d, seed=nq + 7 * nk + H)
+    scale = np.float32(d ** -0.5)
+    o, lse = run(q, k, v, scale, causal)
+    parts = []
+    for b in range(B):
+        ro, rl = attention(bf16_bits_to_f64(q[b:b + 1]), bf16_bits_to_f64(k[b:b + 1]), bf16_bits_to_f64(v[b:b + 1]),
+                           float(scale), causal)
+        parts.append(check(o[b:b + 1], ro, lse[b:b + 1], rl, mean_bar=False))
+    r = merge(parts)
+    print("  ", r, flush=True)
+    assert r.ok, str(r)
+    if causal == 2 and nq > nk:
+        dead = nq - nk
+        assert np.all(o[:, :, :dead] == 0) and np.all(np.isneginf(lse[:, :, :dead]))
+
+
 # Grids whose workgroup count is a multiple of 8 take the XCD regrouping of the
 # workgroup order (consecutive ids go to different XCDs; each XCD is given a
 # contiguous range of (head, tile pair) indices). Small enough to compare whole.
@@ -363,6 +400,7 @@ BR = [
     (1, 1, 300, 77, 128, None, None),        # rows i < 223 see no key
     (2, 2, 257, 511, 128, [511, 300], [0, 40]),
     (2, 1, 640, 1200, 64, [1000, 1200], None),
+    (1, 2, 1024, 256, 128, None, None),      # tile 3 sees 8 slices, tile 0 of its pair none
 ]
 
 

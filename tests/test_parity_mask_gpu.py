@@ -206,3 +206,58 @@ def test_block_sparse_full_size_sampled():
         r = check(o[b:b + 1, h:h + 1, rows], ro, lse[b:b + 1, h:h + 1, rows], rl)
         print(f"  block-sparse b={b} h={h}: {r}", flush=True)
         assert r.ok, str(r)
+
+
+# Run as the first launches of a fresh process (cold caches and address
+# translations, freshly allocated inputs): the boolean-mask d = 64 shapes whose
+# first tiles, in a build that awaited only the oldest of a tile's first copies
+# before its first barrier, read stale K/V or mask words on such launches.
+_FIRST_LAUNCH = r'''
+import sys
+import numpy as np
+import torch
+import tiled_attention_16_amd as ta
+from oracle import attention, bf16_bits_to_f64, check
+from workloads import make_random
+
+def to_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+ok = True
+for case in range(2):
+    if case == 0:
+        B, H, n_q, n_k, d = 2, 2, 200, 777, 64
+        q, k, v = make_random(B, H, n_q, n_k, d, seed=n_q + n_k + d)
+        mask = np.random.default_rng(n_q * 3 + n_k).random((2, 1, n_q, n_k)) < 0.9
+        mask[0, 0, 5] = False
+    else:
+        B, H, n_q, n_k, d = 1, 2, 400, 400, 64
+        q, k, v = make_random(B, H, n_q, n_k, d, seed=97 + d, sigma=(4.0, 1.0, 1.0))
+        rng = np.random.default_rng(98)
+        mask = rng.random((1, 1, n_q, n_k)) < 0.3
+        first = rng.integers(40, 300, size=n_q)
+        for i in range(1, n_q, 2):
+            mask[0, 0, i, :first[i]] = False
+    o, lse = ta.attn_fwd(to_dev(q), to_dev(k), to_dev(v), causal=0, scale=float(d ** -0.5),
+                         attn_mask=torch.from_numpy(mask).cuda())
+    torch.cuda.synchronize()
+    o = bf16_bits_to_f64(o.view(torch.int16).cpu().numpy().view(np.uint16))
+    ro, rl = attention(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), d ** -0.5, 0, attn_mask=mask)
+    r = check(o, ro, lse.cpu().numpy().astype(np.float64), rl)
+    print(f"case {case}: {r}", flush=True)
+    ok = ok and r.ok
+print("OK" if ok else "FAIL", flush=True)
+sys.exit(0 if ok else 1)
+'''
+
+
+def test_first_launch_in_a_fresh_process():
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, PYTHONPATH=root + os.pathsep + os.environ.get("PYTHONPATH", ""))
+    r = subprocess.run([sys.executable, "-u", "-c", _FIRST_LAUNCH], cwd=root, env=env, capture_output=True,
+                       text=True, timeout=240)
+    print(r.stdout, flush=True)
+    assert r.returncode == 0 and "OK" in r.stdout, r.stdout + r.stderr[-2000:]

@@ -14,7 +14,11 @@
 // (t, n-1-t), so every workgroup carries the same number of key slices. The
 // workgroup walks the 32-key K/V slices its rows can see; slices above the
 // causal diagonal and past the batch's valid key length are never visited,
-// and a wave stops computing at the last slice its own rows can see.
+// and a wave stops computing at the last slice its own rows can see. When a
+// launch has more such pairs than the GPU has CUs and all carry the same work
+// (rules only, d = 128, no per-batch lengths), one workgroup per CU walks its
+// share of them; a tile spanning whole turns of the ring then fetches the next
+// tile's first K/V slices (the next head's included) during its last steps.
 //
 // Data movement ([MEMWALL] §4.3 double buffering, here an 8-deep ring;
 // [PT2CUDA] step 5): K and V slices go from global memory straight into LDS
@@ -70,7 +74,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
+#include <atomic>
 #include <type_traits>
+#include <utility>
 
 #include "attn.h"
 #include "launch.h"
@@ -147,6 +153,17 @@ __device__ __forceinline__ int swz(int r) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 x) { return __builtin_bit_cast(u32x4, x); }
+
+// f(std::integral_constant<int, i>{}) for i = 0 .. N-1, in order
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   bf16x2 r = __builtin_convertvector((f32x2){a, b}, bf16x2);   // v_cvt_pk_bf16_f32
@@ -238,76 +255,84 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
   constexpr int kMaskLds = Dense ? 2 * kWaves * 1024                              // two 8-slice blocks of mask words per wave
                                  : Sparse ? 4 * (kMaxSparseSlices + kListPad + 16)   // the slice list
                                           : 0;
-  __shared__ __attribute__((aligned(1024))) char smem[T::kLds + kMaskLds];
+  // Continuation (rules-only, d = 128): see the tile loop below
+  constexpr bool kCont = Mode == 0 && D == 128;
+  constexpr int kContLds = kCont ? 32 * 1024 : 0;   // with V stage 7: room to stage four waves' O rows
+  __shared__ __attribute__((aligned(1024))) char smem[T::kLds + kMaskLds + kContLds];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int hf = lane >> 5;
 
-  // ---- work decomposition: blockIdx -> (batch*head, pair of query tiles) ----
+  // ---- work decomposition: slots -> (batch*head, pair of query tiles) ----
+  // Slot s (0 <= s < n_wg) is a pair of query tiles of one head. A workgroup
+  // takes slots blockIdx.x, blockIdx.x + gridDim.x, ...: one slot when the
+  // grid has a workgroup per slot, several when it has one per CU (the host
+  // does that only when every slot carries the same work).
   const int n_pairs = (n_qt + 1) / 2;
-  const int per_b = H * n_pairs;   // workgroups of one batch
+  const int per_b = H * n_pairs;   // slots of one batch
   const int n_b = n_wg / per_b;    // the batch count
-  int bh, pr;
-  int kv = N_k, qs = 0;   // the batch's valid keys and masked leading rows, clamped
-  bool have_kv_qs = false;
-  if (!causal && (seqlens_k || q_start) && n_b <= kMaxRankedBatches) {
-    // Per-batch valid lengths make batches unequal; the workgroups of one
-    // batch are equal. Rank the batches by their work, valid keys times rows
-    // that attend (ties by index), and hand out the workgroups heaviest batch
-    // first: the dispatcher starts workgroups in id order and refills free
-    // slots in the same order, so this is a longest-first schedule. Ids are
-    // dealt round-robin over the 8 XCDs; when the head count allows, whole
-    // heads are dealt that way (all n_pairs workgroups of a head on one XCD,
-    // one after another, so its K/V is fetched into one L2) while every XCD
-    // still gets the same mix of batches.
+  // Per-batch valid lengths make batches unequal; the slots of one batch are
+  // equal. Rank the batches by their work, valid keys times rows that attend
+  // (ties by index), and order the slots heaviest batch first: the dispatcher
+  // starts workgroups in id order and refills free slots in the same order,
+  // so this is a longest-first schedule. Ids are dealt round-robin over the 8
+  // XCDs; when the head count allows, whole heads are dealt that way (all
+  // n_pairs slots of a head on one XCD, one after another, so its K/V is
+  // fetched into one L2) while every XCD still gets the same mix of batches.
+  const bool ranked = !causal && (seqlens_k || q_start) && n_b <= kMaxRankedBatches;
+  int kv_l = N_k, qs_l = 0, rank = 0;   // lane l: batch l's valid keys, masked rows, rank
+  if (ranked) {
     long long wl = -1;   // lane l: the work of batch l
-    int kv_l = N_k, qs_l = 0;
     if (lane < n_b) {
       kv_l = seqlens_k ? min(max(seqlens_k[lane], 0), N_k) : N_k;
       qs_l = q_start ? min(max(q_start[lane], 0), N_q) : 0;
       wl = (long long)kv_l * (N_q - qs_l);
     }
-    int rank = 0;
     for (int j = 0; j < n_b; ++j) {
       const long long wj = ((long long)__builtin_amdgcn_readlane((int)(wl >> 32), j) << 32) |
                            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)wl, j);
       rank += (wj > wl || (wj == wl && j < lane)) ? 1 : 0;
     }
-    // j: position in the heaviest-first order (batch rank, head, tile pair)
-    int j = blockIdx.x;
-    if (((n_b * H) & 7) == 0) {
-      const int x = j & 7, sx = j >> 3;                 // XCD, position within it
-      const int gx = sx / n_pairs;
-      j = ((gx << 3) + x) * n_pairs + (sx - gx * n_pairs);
+  }
+  struct SlotW { int bh, pr, kv, qs; };   // head, tile pair, the batch's valid keys and masked rows (clamped)
+  auto slot_of = [&](int sl) __attribute__((always_inline)) {
+    SlotW r;
+    if (ranked) {
+      // j: position in the heaviest-first order (batch rank, head, tile pair)
+      int j = sl;
+      if (((n_b * H) & 7) == 0) {
+        const int x = j & 7, sx = j >> 3;                 // XCD, position within it
+        const int gx = sx / n_pairs;
+        j = ((gx << 3) + x) * n_pairs + (sx - gx * n_pairs);
+      }
+      const int r0 = j / per_b;                          // the slot's batch rank
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < n_b && rank == r0);
+      const int b_r = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+      const int rem = j - r0 * per_b;
+      r.bh = b_r * H + rem / n_pairs;
+      r.pr = rem % n_pairs;
+      r.kv = __builtin_amdgcn_readlane(kv_l, b_r);
+      r.qs = __builtin_amdgcn_readlane(qs_l, b_r);
+    } else {
+      // Consecutive ids are dealt round-robin over the 8 XCDs; regroup so that
+      // each XCD gets a contiguous range of (head, tile) pairs and the K/V of
+      // a head stay in one XCD's L2 (a grid of one workgroup per CU keeps
+      // each workgroup on the XCD of its slots when the CU count is a
+      // multiple of 8, which the host checks).
+      int lin = sl;
+      if ((n_wg & 7) == 0) lin = (lin & 7) * (n_wg >> 3) + (lin >> 3);
+      r.bh = lin / n_pairs;
+      r.pr = lin - r.bh * n_pairs;
+      const int b = r.bh / H;
+      r.kv = seqlens_k ? min(max(seqlens_k[b], 0), N_k) : N_k;
+      r.qs = q_start ? min(max(q_start[b], 0), N_q) : 0;
     }
-    const int r0 = j / per_b;                          // this workgroup's batch rank
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < n_b && rank == r0);
-    const int b_r = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
-    const int rem = j - r0 * per_b;
-    bh = b_r * H + rem / n_pairs;
-    pr = rem % n_pairs;
-    kv = __builtin_amdgcn_readlane(kv_l, b_r);
-    qs = __builtin_amdgcn_readlane(qs_l, b_r);
-    have_kv_qs = true;
-  } else {
-    // Consecutive workgroup ids are dealt round-robin over the 8 XCDs; regroup
-    // so that each XCD gets a contiguous range of (head, tile) pairs and the
-    // K/V of a head stay in one XCD's L2.
-    int lin = blockIdx.x;
-    if ((n_wg & 7) == 0) lin = (lin & 7) * (n_wg >> 3) + (lin >> 3);
-    bh = lin / n_pairs;
-    pr = lin - bh * n_pairs;
-  }
-  const int b = bh / H;
-  const char* kg = (const char*)(K + (size_t)bh * N_k * D);
-  const char* vg = (const char*)(V + (size_t)bh * N_k * D);
-
-  if (!have_kv_qs) {
-    if (seqlens_k) kv = min(max(seqlens_k[b], 0), N_k);
-    if (q_start) qs = min(max(q_start[b], 0), N_q);
-  }
+    return r;
+  };
+  // the current item (a query tile): its head, batch, the batch's key bounds
+  int bh = 0, b = 0, kv = N_k, qs = 0;
 
   // ---- K/V slice copies: global -> LDS, 1 KB per wave instruction ----
   // Copy q of this wave fills LDS bytes [1024*qi, 1024*qi + 1024) of a stage,
@@ -334,7 +359,10 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
   // every LDS address (it would then wait for it before each LDS read);
   // completion is awaited explicitly with wait_copies() before the barrier
   // that publishes the slice.
-  const uint32_t lds_wave = (uint32_t)(wave * T::kCopiesPerWave * 1024);
+  // LDS address of this wave's share of a stage at stage offset 0; a copy
+  // writes M0 = lds_wave + the stage's offset (an immediate), one scalar add
+  const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)smem + (uint32_t)(wave * T::kCopiesPerWave * 1024));
   // (readfirstlane returns a signed int: widen through uint32_t so the low
   // half is zero-extended, never sign-extended into the high half)
   auto sgpr64 = [&](const char* p) __attribute__((always_inline)) {
@@ -342,44 +370,57 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uintptr_t)p >> 32));
     return ((uint64_t)hi << 32) | (uint64_t)lo;
   };
-  const int kv_bytes = __builtin_amdgcn_readfirstlane(kv * T::kRowBytes);
-  auto rsrc_of = [&](const char* base) __attribute__((always_inline)) {
-    const uint64_t a = sgpr64(base);
+  // descriptor of a head's K or V whose byte 0 is `skip` bytes before `base`
+  // and which covers `bytes` bytes from there
+  auto rsrc_of = [&](const char* base, uint32_t skip, uint32_t bytes) __attribute__((always_inline)) {
+    const uint64_t a = sgpr64(base) - skip;
     i32x4 r;
     r[0] = (int)(uint32_t)a;
     r[1] = (int)(uint32_t)(a >> 32);   // base bits 32..47; stride 0
-    r[2] = kv_bytes;                    // num_records, in bytes
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);   // num_records, in bytes
     r[3] = 0x00020000;                  // 32-bit data format, no swizzle
     return r;
   };
-  // (the empty asm makes the two descriptors opaque, so the compiler keeps
-  // each in its own four SGPRs instead of rebuilding the shared words per copy)
-  i32x4 k_rsrc = rsrc_of(kg), v_rsrc = rsrc_of(vg);
-  asm volatile("" : "+s"(k_rsrc), "+s"(v_rsrc));
-  auto copy_slice = [&](const i32x4& rs, int sl, const char* dst) __attribute__((always_inline)) {
+  // the current item's descriptors, set per item (their empty asm makes them
+  // opaque, so the compiler keeps each in its own four SGPRs instead of
+  // rebuilding the shared words per copy)
+  i32x4 k_rsrc = {0, 0, 0, 0}, v_rsrc = {0, 0, 0, 0};
+  // Copy into the stage at byte offset `off` of smem (a compile-time
+  // constant: the stage's address is an immediate added to lds_wave, so no
+  // stage address is held in a register through the loop).
+  auto copy_slice = [&](const i32x4& rs, int sl, auto off) __attribute__((always_inline)) {
     if (T::kCopyWaves < kWaves && wave >= T::kCopyWaves) return;
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)dst + lds_wave;
+    constexpr uint32_t kOff = decltype(off)::value;
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)sl * (uint32_t)T::kBytes);
+    const uint32_t lw = lds_wave;
 #pragma unroll
     for (int q = 0; q < T::kCopiesPerWave; ++q) {
       // (the lane offset is added after the M0 write: that add is the wait
       // state the LDS copy needs after M0 changes)
+      const int co = cp_off[q];
       uint32_t voff;
-      asm volatile("s_mov_b32 m0, %1\n\tv_add_u32 %0, %2, %3\n\tbuffer_load_dwordx4 %0, %4, 0 offen lds"
-                   : "=&v"(voff) : "s"(lds0 + q * 1024), "s"(soff), "v"(cp_off[q]), "s"(rs) : "memory", "m0");
+      asm volatile("s_add_u32 m0, %1, %5\n\tv_add_u32 %0, %2, %3\n\tbuffer_load_dwordx4 %0, %4, 0 offen lds"
+                   : "=&v"(voff)
+                   : "s"(lw), "s"(soff), "v"(co), "s"(rs), "n"(kOff + q * 1024u)
+                   : "memory", "m0", "scc");
     }
   };
-  // Slice s lives in stage s % kStages: K rows at kst(st), V rows at vst(st).
+  // Slice s lives in stage s % kStages: K rows at kst(st), V rows at vst(st);
+  // kso / vso: their byte offsets in smem as compile-time constants.
   auto kst = [&](int st) __attribute__((always_inline)) { return (const char*)smem + st * T::kBytes; };
   auto vst = [&](int st) __attribute__((always_inline)) { return (const char*)smem + (kStages + st) * T::kBytes; };
+  auto kso = [](auto st) { return std::integral_constant<uint32_t, (uint32_t)(decltype(st)::value % kStages) * T::kBytes>{}; };
+  auto vso = [](auto st) {
+    return std::integral_constant<uint32_t, (uint32_t)(kStages + decltype(st)::value % kStages) * T::kBytes>{};
+  };
   // the V stage base relative to the folded-in kVBase (see v_off below)
   auto vst_rel = [&](int st) __attribute__((always_inline)) { return (const char*)smem + st * T::kBytes; };
   constexpr int kC = 2 * T::kCopiesPerWave;   // copies per wave per K+V slice
-  // K and V of key slice sl into the stage of ring position s
-  auto copy_slices = [&](int s, int sl) __attribute__((always_inline)) {
-    const int st = s & (kStages - 1);
-    copy_slice(k_rsrc, sl, kst(st));
-    copy_slice(v_rsrc, sl, vst(st));
+  // K and V of key slice sl into the stage of ring position s (a compile-time
+  // std::integral_constant: only its value modulo kStages matters)
+  auto copy_slices = [&](auto s, int sl) __attribute__((always_inline)) {
+    copy_slice(k_rsrc, sl, kso(s));
+    copy_slice(v_rsrc, sl, vso(s));
   };
 
   // ---- per-lane LDS offsets of the MFMA operand reads ----
@@ -420,28 +461,113 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
     v_off[1][db] = (v_off1 ^ (64 * db)) + kVBase;
   }
 
-  // A workgroup owns the pair of query tiles (n_qt-1-pr, pr): under a causal
-  // mask their key counts add up to the same total for every pair, so all
-  // workgroups carry equal work and none is left running alone at the end.
-  // The tile with more keys goes first.
-  const int n_mine = (n_qt - 1 - pr != pr) ? 2 : 1;
+  // A slot is the pair of query tiles (n_qt-1-pr, pr) of a head: under a
+  // causal mask their key counts add up to the same total for every pair, so
+  // all slots carry equal work and no workgroup is left running alone at the
+  // end. The tile with more keys goes first.
   // Lanes whose key row is past kv fetch nothing, so a stage can keep rows no
   // copy wrote. Zero the stages once: such rows then hold zeros or keys of an
   // earlier slice, always finite, and their zero probabilities keep them out.
   for (int i = tid; i < T::kLds / 16; i += kThreads)
     *(__attribute__((address_space(3))) u32x4*)(smem + 16 * i) = (u32x4){0u, 0u, 0u, 0u};
   __syncthreads();
+  // keys the rows of query tile t can see (kv_, qs_: its batch's valid keys and masked rows)
+  auto kv_end_of = [&](int t, int kv_, int qs_) __attribute__((always_inline)) {
+    const int q_end_t = min(t * kBM + kBM, N_q);
+    int e = kv_;
+    if (causal) e = min(e, max(q_end_t + coff, 0));   // row i sees keys <= i + coff
+    if (qs_ >= q_end_t) e = 0;                        // every row of the tile is masked
+    return e;
+  };
+  // ---- Q rows -> VGPRs as the B operand of S^T = K Q^T ----
+  // An item's Q rows are loaded once the previous item's last MFMA has read
+  // qreg (the first item's before the item loop), so the loads overlap that
+  // item's epilogue; nothing reads them until the item's first score product.
+  // (Q is loaded at this one point only, so the compiler keeps one set of
+  // registers for it and has no copy to make, which would wait for the loads.)
+  // Lanes of rows past N_q load row N_q - 1, so every load is unconditional
+  // and a load into registers still awaiting earlier loads needs no wait
+  // (loads complete in order); such rows are given Q = 0 once the rows have
+  // arrived (prep_q), as if they had been loaded as zeros.
+  bf16x8 qreg[kRB][D / 16];
+  auto load_q = [&](int bh_, int row_lo_t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      const int row = min(row_lo_t + 32 * rb + (lane & 31), N_q - 1);
+      const u32x4* src = (const u32x4*)(Q + (size_t)bh_ * N_q * D + (size_t)row * D + hf * 8);
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) qreg[rb][kc] = as_bf16x8(src[2 * kc]);
+    }
+  };
+  // At the start of every item that computes, after q_read() (on every path
+  // the compiler has then waited for the loads before the slice loop, never
+  // inside it): a negative scale negates Q exactly (XOR with 0 otherwise), and
+  // rows past N_q get Q = 0, so their scores are 0 whatever their mask words.
+  const uint32_t qflip = neg_scale ? 0x80008000u : 0u;
+  // a read of the Q registers that stays in order with the copies' asm
+  auto q_read = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) asm volatile("" :: "v"(qreg[rb][kc]));
+  };
+  auto prep_q = [&](int row_lo_t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      const bool pad = row_lo_t + 32 * rb + (lane & 31) >= N_q;
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) {
+        const u32x4 x = as_u32x4(qreg[rb][kc]) ^ qflip;
+        qreg[rb][kc] = as_bf16x8(pad ? (u32x4){0u, 0u, 0u, 0u} : x);
+      }
+    }
+  };
+  // The workgroup's items are the tiles of its slots, in order. Continuation
+  // (rules-only, d = 128): when a tile spans a whole number of ring turns and
+  // another item follows, the tile's last seven steps copy the next item's
+  // slices 0..6 into stages 0..6 (they would otherwise fetch nothing), the
+  // next item's Q rows are loaded before this tile's epilogue, and that
+  // epilogue stages O outside stages 0..6; the next item then starts without
+  // refilling the ring, its K/V arriving while this tile still computes.
+  // Only the slot and the tile index carry over from one item to the next
+  // (the rest is recomputed per item, which keeps scalar registers free
+  // through the slice loop).
+  int slot = blockIdx.x;
+  int it = 0;           // the item's tile in its slot: 0 the one with more keys, 1 the other
+  {
+    const SlotW s0 = slot_of(slot);
+    load_q(s0.bh, (n_qt - 1 - s0.pr) * kBM + kRows * wave);
+  }
+  bool ahead = false;   // this item's Q and slices 0..6 were issued by the previous item
 #pragma nounroll
-  for (int it = 0; it < n_mine; ++it) {
+  for (int item = 0;; ++item) {
+  const SlotW cur = slot_of(slot);
+  const int pr = cur.pr;
+  bh = cur.bh;
+  b = bh / H;
+  kv = cur.kv;
+  qs = cur.qs;
+  const int n_mine = (n_qt - 1 - pr != pr) ? 2 : 1;
+  // the next item: the slot's other tile, else the first tile of the
+  // workgroup's next slot; its head, query tile and visible keys
+  const int slot_n = it + 1 < n_mine ? slot : slot + (int)gridDim.x;
+  const int it_n = it + 1 < n_mine ? it + 1 : 0;
+  const bool has_next = slot_n < n_wg;
+  int nbh = 0, qt_n = 0, n_end = 0;
+  if (has_next) {
+    const SlotW nxt = it_n == 0 ? slot_of(slot_n) : cur;
+    nbh = nxt.bh;
+    qt_n = it_n == 0 ? n_qt - 1 - nxt.pr : nxt.pr;
+    n_end = kv_end_of(qt_n, nxt.kv, nxt.qs);
+  }
   const int qt = it == 0 ? n_qt - 1 - pr : pr;
   const int q0 = qt * kBM;
   const int q_end = min(q0 + kBM, N_q);
-  int kv_end = kv;                                 // keys this workgroup can see
-  if (causal) kv_end = min(kv_end, max(q_end + coff, 0));   // row i sees keys <= i + coff
-  if (qs >= q_end) kv_end = 0;                     // every row of the tile is masked
+  const int kv_end = kv_end_of(qt, kv, qs);        // keys this workgroup can see
   // The copies only need the keys the tile can see: keys past kv_end (beyond
   // the causal limit of the tile's last row) come back as nothing.
-  k_rsrc[2] = v_rsrc[2] = __builtin_amdgcn_readfirstlane(kv_end * T::kRowBytes);
+  k_rsrc = rsrc_of((const char*)(K + (size_t)bh * N_k * D), 0u, (uint32_t)kv_end * T::kRowBytes);
+  v_rsrc = rsrc_of((const char*)(V + (size_t)bh * N_k * D), 0u, (uint32_t)kv_end * T::kRowBytes);
   asm volatile("" : "+s"(k_rsrc), "+s"(v_rsrc));
 
   // This wave's rows: row_lo .. row_lo + 31, one MFMA block of 32 rows; lane L
@@ -457,13 +583,15 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
   int nh = wave_live ? nh_wg : 0;
   if (causal) nh = min(nh, row_hi + coff < 0 ? 0 : (row_hi + coff) / kSlice + 1);
   nh = __builtin_amdgcn_readfirstlane(nh);
+  // this tile's last steps copy the next item's first slices
+  const bool cont = kCont && has_next && nsl > 0 && (nsl & (kStages - 1)) == 0;
   // Sparse: the list of the tile's computed slices (ring position -> slice),
   // then nh_wg = its length and nh = its entries at or below this wave's
   // last slice. Entries past the list are nsl: their copies fetch nothing.
   [[maybe_unused]] int* lst = (int*)(smem + T::kLds);
   [[maybe_unused]] int lst_v = 0;   // entries h0 .. h0+63 of the list, one per lane
   if constexpr (Sparse) {
-    if (it > 0) __syncthreads();   // every wave is done with the previous tile's list
+    if (item > 0) __syncthreads();   // every wave is done with the previous tile's list
     if (wave == 0) {
       const uint8_t* fl = bmask + (size_t)b * bsb + (size_t)(bh - b * H) * bsh + (size_t)qt * n_ks;
       uint32_t bits = 0;
@@ -506,20 +634,6 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
     else return h;
   };
 
-  // ---- Q rows -> VGPRs as the B operand of S^T = K Q^T ----
-  bf16x8 qreg[kRB][D / 16];
-#pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    const int row = row_lo + 32 * rb + (lane & 31);
-    const uint32_t flip = neg_scale ? 0x80008000u : 0u;   // negative scale: negate Q exactly
-#pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < N_q) x = *(const u32x4*)(Q + q_base + (size_t)row * D + kc * 16 + hf * 8);
-      x ^= flip;
-      qreg[rb][kc] = as_bf16x8(x);
-    }
-  }
 
   f32x16 o_acc[kRB][D / 32];
 #pragma unroll
@@ -774,7 +888,7 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
     wait_copies<4 * kC>();
     __syncthreads();   // slices <= h+2 have landed; slice h-1's stage is no longer read
     if (h >= nh) {   // this wave's rows are done; it still copies its share
-      copy_slices(h + kStages - 1, slice_of(h + kStages - 1, Hm + kStages - 1));
+      copy_slices(std::integral_constant<int, Hm + kStages - 1>{}, slice_of(h + kStages - 1, Hm + kStages - 1));
       return;
     }
     // ---- phase A ----
@@ -812,7 +926,7 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
     // freed. The copies go out between the phases and at the end of the step,
     // where the waves arrive at different times, so the workgroup's copies
     // reach the address unit spread out rather than all at once.
-    copy_slice(k_rsrc, slice_of(h + kStages - 1, Hm + kStages - 1), kst((Hm + kStages - 1) % kStages));
+    copy_slice(k_rsrc, slice_of(h + kStages - 1, Hm + kStages - 1), kso(std::integral_constant<int, Hm + kStages - 1>{}));
     // Dense: the next 8-slice block's mask words (used from step h+7 on; the
     // copies issued in between make the waits of those steps cover it).
     if constexpr (Dense && Hm == 0) copy_mask((h >> 3) + 1);
@@ -850,17 +964,31 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    copy_slice(v_rsrc, slice_of(h + kStages - 1, Hm + kStages - 1), vst((Hm + kStages - 1) % kStages));   // the V share
+    copy_slice(v_rsrc, slice_of(h + kStages - 1, Hm + kStages - 1), vso(std::integral_constant<int, Hm + kStages - 1>{}));   // the V share
   };
 
   f32x16 sa[kRB], sb[kRB];
   if (nh_wg > 0) {
-    if (it > 0) __syncthreads();   // every wave is done reading the previous tile's stages
+    if (item > 0) __syncthreads();   // every wave is done reading the previous tile's stages
+    // The item's Q rows are read here first, so the compiler's wait for their
+    // loads comes before this tile's copies are issued and does not cover them
+    // (vector memory operations complete in order).
+    q_read();
+    prep_q(row_lo);
     copy_mask(0);   // Dense: the first block's mask words, ahead of the copies the wait below covers
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s) copy_slices(s, slice_of(s, s));
-    wait_copies<4 * kC>();
-    __syncthreads();   // slices 0 .. 2 have landed
+    if (!ahead) {
+      static_for<kStages - 1>([&](auto s) { copy_slices(s, slice_of(decltype(s)::value, decltype(s)::value)); });
+    }
+    // A tile that was not continued waits for all of its first copies here
+    // (slices 0..6 and the mask words); a wait for only the oldest of them let
+    // rows of the first tiles of a cold launch see stale K/V or mask words
+    // (measured, boolean-mask d = 64), and every build before that waited for
+    // all of them anyway. After a continuation the copies of slices 0..6 are
+    // older than the Q loads and the previous tile's O stores, so the partial
+    // wait covers all of them.
+    if (ahead) wait_copies<4 * kC>();
+    else wait_copies<0>();
+    __syncthreads();   // slices 0 .. 6 have landed
     if (nh > 0) {
       load_k(std::integral_constant<int, 0>{});
       qk(sa);
@@ -875,6 +1003,20 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
       if constexpr (Sparse) lst_v = lst[h0 + lane];   // list entries h0 .. h0+63
       step(std::integral_constant<int, 0>{}, h0, sa, sb);
       if (h0 + 1 >= nh_wg) break;
+      // From here on the copies (ring positions h0 + 8 ..) are the next
+      // item's: ring position nsl + s is stage s, where its slice s goes. They
+      // use descriptors whose byte 0 lies nsl slices before the next item's K
+      // (V), so position nsl + s addresses its slice s, and num_records bounds
+      // it by the keys that item can see.
+      if constexpr (kCont) {
+        if (cont && h0 + kStages == nsl) {
+          const uint32_t skip = (uint32_t)nsl * (uint32_t)T::kBytes;
+          const uint32_t lim = skip + (uint32_t)n_end * T::kRowBytes;
+          k_rsrc = rsrc_of((const char*)(K + (size_t)nbh * N_k * D), skip, lim);
+          v_rsrc = rsrc_of((const char*)(V + (size_t)nbh * N_k * D), skip, lim);
+          asm volatile("" : "+s"(k_rsrc), "+s"(v_rsrc));
+        }
+      }
       step(std::integral_constant<int, 1>{}, h0 + 1, sb, sa);
       if (h0 + 2 >= nh_wg) break;
       step(std::integral_constant<int, 2>{}, h0 + 2, sa, sb);
@@ -889,9 +1031,19 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
       if (h0 + 7 >= nh_wg) break;
       step(std::integral_constant<int, 7>{}, h0 + 7, sb, sa);
     }
-    wait_copies<0>();   // no copy may still be writing LDS when the next tile (or wave) starts
+  } else {
+    // The rows loaded for this item go unused: read them here, so that on
+    // every path the loads are complete before the next item's rows are
+    // loaded into the same registers (that load then waits for nothing).
+    q_read();
   }
+  // No copy may still be writing LDS when the epilogue stages O or the next
+  // tile starts (also when this tile computed nothing: a continued tile can
+  // have issued its slices 0..6 all the same). A continuing tile's copies
+  // write stages 0..6, which its epilogue leaves alone.
+  if (!cont) wait_copies<0>();
   mfma_result_wait();   // the last P V MFMAs have written o_acc
+  if (has_next) load_q(nbh, qt_n * kBM + kRows * wave);   // the next item's Q rows (qreg is no longer read)
 
   // ---- epilogue: O / l, LSE, bf16 store ----
   // In the accumulator layout a lane holds 8-byte pieces of 32 different rows,
@@ -903,8 +1055,17 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
   constexpr int kORow = 2 * D + 16;
   constexpr int kChunksPerRow = D / 8;                   // 16-byte pieces per row
   static_assert(kWaves * kRows * kORow <= T::kLds, "the O staging area must fit in the stages");
+  static_assert(!kCont || (kWaves / 2) * kRows * kORow <= T::kBytes + kContLds, "half the waves' rows fit the spare room");
   __syncthreads();   // every wave is done with the K/V stages, which the staging area overlaps
-  char* ost = smem + wave * kRows * kORow;
+  // A continued tile stages its rows in V stage 7 and the LDS past the ring
+  // (stages 0..6 hold the next tile's first slices), half the waves at a time.
+  char* const cont_area = smem + (2 * kStages - 1) * T::kBytes;
+  char* ost = cont ? cont_area + (wave % (kWaves / 2)) * kRows * kORow : smem + wave * kRows * kORow;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+  if (half == 1 && !cont) break;
+  if (half == 1) __syncthreads();   // the first half's rows have been read back
+  if (cont && wave / (kWaves / 2) != half) continue;
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     const int r = 32 * rb + (lane & 31);
@@ -931,7 +1092,12 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
     const u32x4 x = *(const __attribute__((address_space(3))) u32x4*)(ost + r * kORow + 16 * ch);
     if (row_lo + r < N_q) *(u32x4*)(O + q_base + (size_t)(row_lo + r) * D + 8 * ch) = x;
   }
-  }   // tiles of the pair
+  }   // halves
+  ahead = cont;
+  if (!has_next) break;
+  slot = slot_n;
+  it = it_n;
+  }   // items
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -955,6 +1121,19 @@ __global__ __launch_bounds__(256) void attn_mask_pack_kernel(const uint8_t* __re
     if (j < n_k && m[r * n_k + j] != 0) x |= 1u << t;
   }
   bits[id] = x;
+}
+
+// compute units of the current device, read once per device (0 if unknown)
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = -1;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n > 0 ? n : 0;
 }
 
 int fwd_launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q, int N_k,
@@ -1002,7 +1181,17 @@ int fwd_launch(const void* q, const void* k, const void* v, void* o, float* lse,
   int causal01 = causal ? 1 : 0, coff = causal == 2 ? N_k - N_q : 0, n_qt_i = (int)n_qt, n_wg_i = (int)n_wg;
   auto kern = d == 128 ? (mode == 1 ? attn_fwd_kernel<128, 1> : mode == 2 ? attn_fwd_kernel<128, 2> : attn_fwd_kernel<128, 0>)
                        : (mode == 1 ? attn_fwd_kernel<64, 1> : mode == 2 ? attn_fwd_kernel<64, 2> : attn_fwd_kernel<64, 0>);
-  const hipError_t e = attn_launch::launch(kern, dim3((unsigned)n_wg), dim3(64 * waves), stream, qp, kp, vp, op, lse, H, N_q,
+  // One workgroup per slot (pair of query tiles), or, for rules-only d = 128
+  // launches with equal slots (no per-batch lengths) and more slots than CUs,
+  // one workgroup per CU that walks its share of them: each tile's last steps
+  // then fetch the next one's first K/V slices and Q while it still computes.
+  // (A multiple of 8 CUs keeps every workgroup's slots on its own XCD.)
+  unsigned grid = (unsigned)n_wg;
+  if (mode == 0 && d == 128 && !seqlens_k && !q_start) {
+    const int n_cu = cu_count();
+    if (n_cu > 0 && n_cu % 8 == 0 && n_wg > n_cu) grid = (unsigned)n_cu;
+  }
+  const hipError_t e = attn_launch::launch(kern, dim3(grid), dim3(64 * waves), stream, qp, kp, vp, op, lse, H, N_q,
                                            N_k, c, neg, causal01, coff, seqlens_k, q_start, n_qt_i, n_wg_i, mbits, msb,
                                            msh, mrw, bmask, bsb, bsh, n_ks);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
