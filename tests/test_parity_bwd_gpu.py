@@ -293,3 +293,68 @@ def test_bwd_block_sparse(case):
     print("  ", r, flush=True)
     assert r.ok, str(r)
     assert np.all(dk[:, :, 128:256] == 0) and np.all(dv[:, :, 128:256] == 0)
+
+
+# The backward's first launches in a fresh process, every input uploaded anew
+# just before them (cold caches and address translations): a rules-only causal
+# d = 128 shape with ragged tails, a boolean-mask d = 64 shape and a varlen
+# d = 64 shape, each compared with the oracle in a child process.
+_FIRST_LAUNCH = r'''
+import sys
+import numpy as np
+import torch
+import tiled_attention_16_amd as ta
+from oracle import attention_bwd, bf16_bits_to_f64, check_grads
+from workloads import make_random
+
+def to_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+def f64(t):
+    return bf16_bits_to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
+
+ok = True
+for case in range(3):
+    mask = sl = qs = None
+    causal = 0
+    if case == 0:
+        B, H, n_q, n_k, d, causal = 1, 2, 600, 600, 128, 1
+    elif case == 1:
+        B, H, n_q, n_k, d = 2, 2, 200, 777, 64
+        mask = np.random.default_rng(n_q * 3 + n_k).random((2, 1, n_q, n_k)) < 0.9
+    else:
+        B, H, n_q, n_k, d = 3, 2, 300, 300, 64
+        sl, qs = np.array([300, 131, 257], np.int32), np.array([0, 40, 0], np.int32)
+    q, k, v = make_random(B, H, n_q, n_k, d, seed=11 + case)
+    g = make_random(B, H, n_q, n_k, d, seed=21 + case)[0]
+    scale = d ** -0.5
+    tm = torch.from_numpy(mask).cuda() if mask is not None else None
+    tsl = torch.from_numpy(sl).cuda() if sl is not None else None
+    tqs = torch.from_numpy(qs).cuda() if qs is not None else None
+    o, lse = ta.attn_fwd(to_dev(q), to_dev(k), to_dev(v), causal=causal, scale=scale, seqlens_k=tsl, q_start=tqs,
+                         attn_mask=tm)
+    torch.cuda.synchronize()
+    o_h, lse_h = o.cpu(), lse.cpu()
+    dq, dk, dv = ta.attn_bwd(to_dev(q), to_dev(k), to_dev(v), o_h.cuda(), lse_h.cuda(), to_dev(g), causal=causal,
+                             scale=scale, seqlens_k=tsl, q_start=tqs, attn_mask=tm)
+    torch.cuda.synchronize()
+    rq, rk, rv = attention_bwd(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), bf16_bits_to_f64(g),
+                               scale, causal, seqlens_k=sl, q_start=qs, attn_mask=mask)
+    r = check_grads({"dq": f64(dq), "dk": f64(dk), "dv": f64(dv)}, {"dq": rq, "dk": rk, "dv": rv})
+    print(f"case {case}: {r}", flush=True)
+    ok = ok and r.ok
+print("OK" if ok else "FAIL", flush=True)
+sys.exit(0 if ok else 1)
+'''
+
+
+def test_first_launch_in_a_fresh_process():
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, PYTHONPATH=root + os.pathsep + os.environ.get("PYTHONPATH", ""))
+    r = subprocess.run([sys.executable, "-u", "-c", _FIRST_LAUNCH], cwd=root, env=env, capture_output=True,
+                       text=True, timeout=240)
+    print(r.stdout, flush=True)
+    assert r.returncode == 0 and "OK" in r.stdout, r.stdout + r.stderr[-2000:]
