@@ -322,15 +322,19 @@ PERSIST = [
     (1, 130, 600, 768, 0),       # three tiles: two-tile slots and one-tile middle slots, ragged rows
     (1, 130, 1024, 256, 2),      # bottom-right: a continued tile that sees no key, keyless tiles
     (1, 300, 300, 300, 1),       # ragged: no tile spans whole ring turns, no continuation
+    (2, 150, 512, 512, -1),      # negative scale (Q negated per tile), causal, continued tiles
 ]
 
 
-@pytest.mark.parametrize("case", PERSIST, ids=[f"{c[0]}x{c[1]}x{c[2]}x{c[3]}_c{c[4]}" for c in PERSIST])
+@pytest.mark.parametrize("case", PERSIST, ids=[f"{c[0]}x{c[1]}x{c[2]}x{c[3]}_c{c[4]}".replace("c-1", "neg_scale")
+                                         for c in PERSIST])
 def test_persistent_grid_every_element(case):
     B, H, nq, nk, causal = case
     d = 128
     q, k, v = make_random(B, H, nq, nk, d, seed=nq + 7 * nk + H)
     scale = np.float32(d ** -0.5)
+    if causal < 0:   # a negative score factor
+        causal, scale = 1, np.float32(-0.09)
     o, lse = run(q, k, v, scale, causal)
     parts = []
     for b in range(B):
