@@ -909,6 +909,11 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
         const Range ra = sched_a(g);   // second half of slice h's exponentials
 #pragma unroll
         for (int j = ra.lo; j < ra.hi; ++j) exp_one(sc[0], j, pbw_hi, lsum_hi);
+        // order inside the group (measured best of the orders tried): after
+        // the MFMA the exponential, then the V reads, then the rest
+        __builtin_amdgcn_sched_group_barrier(0x400, 4, 1);    // transcendental
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);    // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x002, 24, 1);   // other VALU
         __builtin_amdgcn_sched_barrier(0);
       }
       // keep P and the sums in this phase (the compiler would otherwise sink
@@ -961,6 +966,11 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
         if (rs.hi > rs.lo) shift_part(sn, 0, rs.lo, rs.hi - rs.lo);
 #pragma unroll
         for (int j = rx.lo; j < rx.hi; ++j) exp_one(sn[0], j, pbw_lo[(Hm + 1) & 1], lsum_lo[(Hm + 1) & 1]);
+        // order inside the group: after the MFMA the K read, then the
+        // exponentials, then the shifts, sums and packs
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);    // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x400, 4, 1);    // transcendental
+        __builtin_amdgcn_sched_group_barrier(0x002, 24, 1);   // other VALU
         __builtin_amdgcn_sched_barrier(0);
       }
     }
