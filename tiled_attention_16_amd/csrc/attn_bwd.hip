@@ -57,6 +57,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) float lds_f32;
 
 constexpr int kBlk = 32;          // rows (or keys) per block and per wave
 constexpr int kWaves = 4;
@@ -869,6 +870,9 @@ __global__ __launch_bounds__(64 * kWavesKV) void attn_bwd_dkdv_kernel(
     if constexpr (Sparse) return (__builtin_amdgcn_readfirstlane(lst[n]) & 0xffffff) * kBlk;
     else return (blk0 + n) * kBlk;
   };
+  [[maybe_unused]] auto row0_of_lane = [&](int i) __attribute__((always_inline)) {   // per-lane entry
+    return (lst[i] & 0xffffff) * kBlk;
+  };
   auto wave_in = [&](int n) __attribute__((always_inline)) {
     if constexpr (Sparse) return ((__builtin_amdgcn_readfirstlane(lst[n]) >> (24 + wave)) & 1) != 0;
     else return true;
@@ -942,115 +946,197 @@ __global__ __launch_bounds__(64 * kWavesKV) void attn_bwd_dkdv_kernel(
     if (wave == 0) wait_copies<A * (kCpb + 1)>();
     else wait_copies<A * kCpb>();
   };
-  auto stage_of = [&](int n) { return (const char*)smem + (n % kDepth) * kStage; };
 
-  const Offs<D> off(lane);
+  const Offs<D> off0(lane);
   f32x16 adk[D / 32], adv[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) adk[db] = adv[db] = (f32x16){};
-  // no mask anywhere in block n for this wave: all its keys are valid, all
+  // Block n needs no mask for this wave when all its keys are valid, all
   // rows exist and are past q_start, and (causal) the block starts at or
-  // after the wave's last key
-  auto block_full = [&](int n) {
-    const int r0 = row0_of(n);
-    // one condition (bitwise, not short-circuit): a single branch
-    return wkey_live & (r0 + kBlk <= N_q) & (r0 >= qs) & (!causal | (r0 + coff >= wkey0 + kBlk - 1)) & wave_in(n);
+  // after the wave's last key (block-sparse: and the wave's slice is kept).
+  // The rows of the blocks increase with n, so these blocks are one range
+  // [n_full0, n_full1) per wave; the loop runs in three parts (masked, no
+  // mask, masked), each with one copy of the block code, which keeps the
+  // accumulators' registers the same throughout.
+  auto count_below = [&](int t) {   // ring positions n < nblk whose first row is below t
+    if (t <= 0) return 0;
+    if constexpr (Sparse) {
+      int cnt = 0;
+      for (int i = lane; i < nblk; i += 64) cnt += row0_of_lane(i) < t ? 1 : 0;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+      return __builtin_amdgcn_readfirstlane(cnt);
+    } else {
+      return min(max((t + kBlk - 1) / kBlk - blk0, 0), nblk);
+    }
   };
+  int n_full0 = nblk, n_full1 = nblk;
+  if (!Dense && wkey_live) {
+    n_full0 = count_below(max(qs, causal ? wkey0 + kBlk - 1 - coff : 0));
+    n_full1 = max(count_below(N_q - kBlk + 1), n_full0);
+  }
 
 #pragma unroll
   for (int n = 0; n < kDepth - 1; ++n) issue(n);
-  for (int n = 0; n < nblk; ++n) {
+  auto block = [&](int n, auto full_t) __attribute__((always_inline)) {
     wait_block(std::integral_constant<int, kDepth - 2>{});   // block n (and, before block 0, the V blocks)
     __syncthreads();   // everyone's copies of block n; block n-1's stage is free
     issue(n + kDepth - 1);
-    const char* qb = stage_of(n);
-    const char* gb = qb + R::kBlkBytes;
-    // S = Q K^T, then dP = dO V^T (lane = key, 16 query rows per lane); the
-    // operands are read one step ahead of their MFMAs
-    f32x16 s = {}, dp = {};
-    {
-      bf16x8 qa[2];
-      qa[0] = read_row<D>(qb, off, 0);
-#pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc) {
-        if (kc + 1 < D / 16) qa[(kc + 1) & 1] = read_row<D>(qb, off, kc + 1);
-        s = mfma(qa[kc & 1], kr[kc], s);
-      }
+    if constexpr (Sparse && decltype(full_t)::value) {
+      if (!wave_in(n)) return;   // the wave's slice is dropped: nothing to add
     }
-    {
-      bf16x8 ga[2], va[2];
-      ga[0] = read_row<D>(gb, off, 0);
-      va[0] = read_row<D>(vblk, off, 0);
-#pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc) {
-        if (kc + 1 < D / 16) {
-          ga[(kc + 1) & 1] = read_row<D>(gb, off, kc + 1);
-          va[(kc + 1) & 1] = read_row<D>(vblk, off, kc + 1);
-        }
-        dp = mfma(ga[kc & 1], va[kc & 1], dp);
-      }
-    }
-    // P and dS, packed as the B operands of the dV and dK products; register
-    // r holds query row r0 + 8*(r/4) + 4*hf + r%4
     const int r0 = row0_of(n);
-    const char* sb = qb + 2 * R::kBlkBytes;
-    [[maybe_unused]] const bool in = wave_in(n);
-    [[maybe_unused]] const char* mb = sb + 1024 + wave * 256;   // Dense: word of row r0 + t at 4*t
-    uint32_t wp[8], wd[8];
-    const bool full = !Dense && block_full(n);
+    // The block in an explicit order of slots, each one MFMA with the reads
+    // and the arithmetic placed after it (scheduling fences between them), so
+    // that a wave's softmax arithmetic overlaps its own MFMAs: P while the dP
+    // products run, dS while the dV products run.
+    auto step = [&](auto full_t) __attribute__((always_inline)) {
+      constexpr bool F = decltype(full_t)::value;
+      // The stage offset and the lane offsets pass through this marker, so
+      // that every address is formed next to its read instead of two dozen
+      // of them being held in registers across the loop.
+      uint32_t so = (uint32_t)(n % kDepth) * kStage;
+      Offs<D> off = off0;
+      if constexpr (F)
+        asm volatile("; dkdv block, no mask" : "+s"(so), "+v"(off.row0), "+v"(off.tr[0]), "+v"(off.tr[1]));
+      else
+        asm volatile("; dkdv block, masked" : "+s"(so), "+v"(off.row0), "+v"(off.tr[0]), "+v"(off.tr[1]));
+      const char* qb = (const char*)smem + so;
+      const char* gb = qb + R::kBlkBytes;
+      // register r of S, dP (and P, dS) belongs to query row r0 + 8*(r/4) + 4*hf + r%4,
+      // whose (LSE log2 e, D) pair sits at floats 16*(r/4) + 2*(r%4) + 0, 1 of st
+      const lds_f32* st = (const lds_f32*)(qb + 2 * R::kBlkBytes + 32 * hf);
+      auto sti = [](int r) { return 16 * (r / 4) + 2 * (r % 4); };
+      auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+      [[maybe_unused]] const bool in = wave_in(n);
+      [[maybe_unused]] const char* mb = qb + 2 * R::kBlkBytes + 1024 + wave * 256;   // Dense: row r0 + t at 4*t
+      constexpr int kKC = D / 16;       // MFMAs of S (and of dP)
+      constexpr int kJ = 4 * (D / 32);  // MFMAs of dV and dK
+      static_assert(kKC == 8, "eight pairs of P elements, one per dP MFMA");
+
+      // S = Q K^T (lane = key, 16 query rows per lane); operands are read two
+      // slots ahead of their MFMA (dO and V one slot with a dense mask, whose
+      // words take the registers)
+      constexpr int kPF = Dense ? 1 : 2;
+      f32x16 s = {}, dp = {};
+      bf16x8 qa[3], ga[3], va[3], ta[3];
+      float l2[2], dd[2];
+      qa[0] = read_row<D>(qb, off, 0);
+      qa[1] = read_row<D>(qb, off, 1);
+      fence();
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      // stats of rows 8g + 4hf .. +3: (lse2, D) pairs, 32 bytes
-      const f32x4 s01 = *(const lds_f32x4*)(sb + 8 * (8 * g + 4 * hf));
-      const f32x4 s23 = *(const lds_f32x4*)(sb + 8 * (8 * g + 4 * hf) + 16);
-      const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
-      const float dd[4] = {s01[1], s01[3], s23[1], s23[3]};
-      float p[4], ds[4];
-      if (full) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(s[4 * g + e] * c - l2[e]);
-          ds[e] = p[e] * (dp[4 * g + e] - dd[e]);
+      for (int kc = 0; kc < kKC; ++kc) {
+        if (kc + 2 < kKC) qa[(kc + 2) % 3] = read_row<D>(qb, off, kc + 2);
+        if (kc + kPF >= kKC) {
+          ga[kc + kPF - kKC] = read_row<D>(gb, off, kc + kPF - kKC);
+          va[kc + kPF - kKC] = read_row<D>(vblk, off0, kc + kPF - kKC);
         }
-      } else {
-        // Dense: the words of rows 8g + 4hf .. +3, one 16-byte read
-        [[maybe_unused]] u32x4 mw = {};
-        if constexpr (Dense) mw = *(const lds_u32x4*)(mb + 32 * g + 16 * hf);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          const int qrow = r0 + 8 * g + 4 * hf + e;
-          bool ok = key_live && qrow < N_q && qrow >= qs && (!causal || key <= qrow + coff);
-          if constexpr (Sparse) ok = ok && in;
-          if constexpr (Dense) ok = ok && ((mw[e] >> (lane & 31)) & 1u);
-          p[e] = ok ? __builtin_amdgcn_exp2f(s[r] * c - l2[e]) : 0.f;
-          ds[e] = ok ? p[e] * (dp[r] - dd[e]) : 0.f;
-        }
+        s = mfma(qa[kc % 3], kr[kc], s);
+        fence();
       }
-      wp[2 * g] = pack2(p[0], p[1]);
-      wp[2 * g + 1] = pack2(p[2], p[3]);
-      wd[2 * g] = pack2(ds[0], ds[1]);
-      wd[2 * g + 1] = pack2(ds[2], ds[3]);
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by the transposing read)
-    {
-      bf16x8 ta_g[2], ta_q[2];
-      ta_g[0] = read_tr<D>(gb, off, 0, 0);
-      ta_q[0] = read_tr<D>(qb, off, 0, 0);
+      // P of elements 2i, 2i+1 = exp2(S c - LSE log2 e), 0 where masked; packed
+      // as a B operand of dV
+      float p[16];
+      uint32_t wp[8], wd[8];
+      [[maybe_unused]] u32x4 mw[2] = {};   // Dense: the words of rows 8g + 4hf .. +3
+      auto p_pair = [&](int i) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 2 * (D / 32); ++i) {   // i = cc * (D/32) + db
-        const int cc = i / (D / 32), db = i % (D / 32);
-        if (i + 1 < 2 * (D / 32)) {
-          ta_g[(i + 1) & 1] = read_tr<D>(gb, off, (i + 1) / (D / 32), (i + 1) % (D / 32));
-          ta_q[(i + 1) & 1] = read_tr<D>(qb, off, (i + 1) / (D / 32), (i + 1) % (D / 32));
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * i + e;
+          const float x = s[r] * c - l2[e];
+          if constexpr (F) {
+            p[r] = __builtin_amdgcn_exp2f(x);
+          } else {
+            const int qrow = r0 + 8 * (r / 4) + 4 * hf + r % 4;
+            bool ok = key_live && qrow < N_q && qrow >= qs && (!causal || key <= qrow + coff);
+            if constexpr (Sparse) ok = ok && in;
+            if constexpr (Dense) ok = ok && ((mw[(r / 4) & 1][r % 4] >> (lane & 31)) & 1u);
+            p[r] = ok ? __builtin_amdgcn_exp2f(x) : 0.f;
+          }
         }
-        const bf16x8 bp = __builtin_bit_cast(bf16x8, (u32x4){wp[4 * cc], wp[4 * cc + 1], wp[4 * cc + 2], wp[4 * cc + 3]});
-        const bf16x8 bd = __builtin_bit_cast(bf16x8, (u32x4){wd[4 * cc], wd[4 * cc + 1], wd[4 * cc + 2], wd[4 * cc + 3]});
-        adv[db] = mfma(ta_g[i & 1], bp, adv[db]);
-        adk[db] = mfma(ta_q[i & 1], bd, adk[db]);
+        wp[i] = pack2(p[2 * i], p[2 * i + 1]);
+      };
+      // dS of elements 2i, 2i+1 = P (dP - D); a masked element has P = 0 and
+      // gives 0 even where dP - D is not finite (rows before q_start hold
+      // whatever the caller left there)
+      auto ds_pair = [&](int i) __attribute__((always_inline)) {
+        float ds[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * i + e;
+          ds[e] = p[r] * (dp[r] - dd[e]);
+          if constexpr (!F) ds[e] = p[r] != 0.f ? ds[e] : 0.f;
+        }
+        wd[i] = pack2(ds[0], ds[1]);
+      };
+      // dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by the transposing read),
+      // product j: dV for j < kJ/2, dK after; chunk (16 rows) m % 2, column block j % (D/32)
+      auto tr_of = [&](int j) __attribute__((always_inline)) {
+        const int m = j / (D / 32);
+        return read_tr<D>(m >= 2 ? qb : gb, off, m & 1, j % (D / 32));
+      };
+      // dP = dO V^T. Slot kc: its MFMA; the next operands and the stats of pair
+      // kc; then P of pair kc - 1 (pair 0 waits a slot for S to land).
+#pragma unroll
+      for (int kc = 0; kc < kKC; ++kc) {
+        dp = mfma(ga[kc % 3], va[kc % 3], dp);
+        fence();
+        if (kc + kPF < kKC) {
+          ga[(kc + kPF) % 3] = read_row<D>(gb, off, kc + kPF);
+          va[(kc + kPF) % 3] = read_row<D>(vblk, off0, kc + kPF);
+        }
+        if (kc + 2 >= kKC) ta[kc + 2 - kKC] = tr_of(kc + 2 - kKC);
+        if constexpr (Dense) {
+          if (kc % 2 == 0) mw[(kc / 2) & 1] = *(const lds_u32x4*)(mb + 32 * (kc / 2) + 16 * hf);
+        }
+        float l2n[2] = {st[sti(2 * kc)], st[sti(2 * kc + 1)]};
+        fence();
+        if (kc > 0) p_pair(kc - 1);
+        l2[0] = l2n[0];
+        l2[1] = l2n[1];
+        fence();
       }
-    }
-  }
+      // Slot j: its MFMA; the next operand and the D values of pair j; then P
+      // of pair 7 (j = 0) or dS of pair j - 1. The dV products use P of chunk
+      // m % 2 (ready), the dK products from j = kJ/2 on find dS done.
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        const int m = j / (D / 32), cc = m & 1, db = j % (D / 32);
+        if (m >= 2) {
+          const bf16x8 bd =
+              __builtin_bit_cast(bf16x8, (u32x4){wd[4 * cc], wd[4 * cc + 1], wd[4 * cc + 2], wd[4 * cc + 3]});
+          adk[db] = mfma(ta[j % 3], bd, adk[db]);
+        } else {
+          const bf16x8 bp =
+              __builtin_bit_cast(bf16x8, (u32x4){wp[4 * cc], wp[4 * cc + 1], wp[4 * cc + 2], wp[4 * cc + 3]});
+          adv[db] = mfma(ta[j % 3], bp, adv[db]);
+        }
+        fence();
+        if (j + 2 < kJ) ta[(j + 2) % 3] = tr_of(j + 2);
+        float ddn[2];
+        if (j < 8) {
+          ddn[0] = st[sti(2 * j) + 1];
+          ddn[1] = st[sti(2 * j + 1) + 1];
+        }
+        fence();
+        if (j == 0) p_pair(kKC - 1);
+        else if (j <= 8) ds_pair(j - 1);
+        if (j < 8) {
+          dd[0] = ddn[0];
+          dd[1] = ddn[1];
+        }
+        fence();
+      }
+      if constexpr (F) asm volatile("; dkdv block end, no mask");
+      else asm volatile("; dkdv block end, masked");
+    };
+    step(full_t);
+  };
+  int n = 0;
+  for (; n < n_full0; ++n) block(n, std::false_type{});
+  if constexpr (!Dense)
+    for (; n < n_full1; ++n) block(n, std::true_type{});
+  for (; n < nblk; ++n) block(n, std::false_type{});
   wait_copies<0>();   // no copy may still be writing LDS when the workgroup ends
   // register r of block db holds d = 32*db + 8*(r/4) + 4*hf + r%4 of this lane's key
   if (key_ok) {
