@@ -316,10 +316,10 @@ def test_full_size_workload_every_element(name):
 # item's first K/V slices and its Q (the next head's included) while it
 # computes. Compared whole, one batch at a time.
 PERSIST = [
-    # B, H, N_q, N_k, causal     (slots = B*H*ceil(ceil(N_q/256)/2); 256 CUs)
+    # B, H, N_q, N_k, causal     (slots = B*H*ceil(ceil(N_q/256)/2) causal, B*H*ceil(N_q/256) not; 256 CUs)
     (2, 150, 256, 256, 1),       # 300 one-tile slots: every tile continues into the next head's
-    (2, 140, 512, 512, 0),       # 280 two-tile slots, regrouped over the XCDs
-    (1, 130, 600, 768, 0),       # three tiles: two-tile slots and one-tile middle slots, ragged rows
+    (2, 140, 512, 512, 0),       # 560 one-tile slots, a head's two tiles on one XCD at once
+    (1, 130, 600, 768, 0),       # three one-tile slots per head, ragged rows
     (1, 130, 1024, 256, 2),      # bottom-right: a continued tile that sees no key, keyless tiles
     (1, 300, 300, 300, 1),       # ragged: no tile spans whole ring turns, no continuation
     (2, 150, 512, 512, -1),      # negative scale (Q negated per tile), causal, continued tiles

@@ -11,11 +11,14 @@
 // over key/value blocks): one workgroup of 8 wave64s (two per SIMD) owns a
 // pair of 256-row query tiles of one (batch, head), processed one after the
 // other; each wave owns 32 rows of the tile. Under a causal mask the pair is
-// (t, n-1-t), so every workgroup carries the same number of key slices. The
+// (t, n-1-t), so every workgroup carries the same number of key slices;
+// without a causal mask or per-batch lengths all tiles are equal and a
+// workgroup owns a single tile, the tiles of a head going to workgroups that
+// run at the same time on one XCD (one K/V read from HBM serves them). The
 // workgroup walks the 32-key K/V slices its rows can see; slices above the
 // causal diagonal and past the batch's valid key length are never visited,
 // and a wave stops computing at the last slice its own rows can see. When a
-// launch has more such pairs than the GPU has CUs and all carry the same work
+// launch has more such slots than the GPU has CUs and all carry the same work
 // (rules only, d = 128, no per-batch lengths), one workgroup per CU walks its
 // share of them; a tile spanning whole turns of the ring then fetches the next
 // tile's first K/V slices (the next head's included) during its last steps.
@@ -265,12 +268,18 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int hf = lane >> 5;
 
-  // ---- work decomposition: slots -> (batch*head, pair of query tiles) ----
-  // Slot s (0 <= s < n_wg) is a pair of query tiles of one head. A workgroup
+  // ---- work decomposition: slots -> (batch*head, query tiles) ----
+  // Slot s (0 <= s < n_wg) is a pair of query tiles of one head, or one tile
+  // (below). A workgroup
   // takes slots blockIdx.x, blockIdx.x + gridDim.x, ...: one slot when the
   // grid has a workgroup per slot, several when it has one per CU (the host
   // does that only when every slot carries the same work).
-  const int n_pairs = (n_qt + 1) / 2;
+  // Without a causal mask or per-batch lengths every tile has the same work:
+  // a slot is then one tile, so that the tiles of a head are spread over
+  // workgroups that run at the same time (consecutive ids, one XCD below) and
+  // read its K/V from L2 once, instead of one workgroup reading it per tile.
+  const bool single = !causal && !seqlens_k && !q_start;
+  const int n_pairs = single ? n_qt : (n_qt + 1) / 2;   // slots of one head
   const int per_b = H * n_pairs;   // slots of one batch
   const int n_b = n_wg / per_b;    // the batch count
   // Per-batch valid lengths make batches unequal; the slots of one batch are
@@ -547,7 +556,7 @@ __global__ __launch_bounds__(64 * waves_of(Mode, D), waves_of(Mode, D) == 4 ? 2 
   b = bh / H;
   kv = cur.kv;
   qs = cur.qs;
-  const int n_mine = (n_qt - 1 - pr != pr) ? 2 : 1;
+  const int n_mine = (!single && n_qt - 1 - pr != pr) ? 2 : 1;
   // the next item: the slot's other tile, else the first tile of the
   // workgroup's next slot; its head, query tile and visible keys
   const int slot_n = it + 1 < n_mine ? slot : slot + (int)gridDim.x;
@@ -1160,7 +1169,9 @@ int fwd_launch(const void* q, const void* k, const void* v, void* o, float* lse,
   const int mode = mbits ? 1 : bmask ? 2 : 0;
   const int waves = waves_of(mode, d), bm = kRows * waves;      // workgroup shape of the instance
   const long long n_qt = (N_q + bm - 1) / bm;
-  const long long n_wg = (long long)B * H * ((n_qt + 1) / 2);   // one workgroup per pair of query tiles
+  // one slot per pair of query tiles, or per tile when all tiles are equal (as in the kernel)
+  const bool single = !causal && !seqlens_k && !q_start;
+  const long long n_wg = (long long)B * H * (single ? n_qt : (n_qt + 1) / 2);
   if (n_wg > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   if ((long long)B * H > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   if ((long long)N_k * d * 2 > 0x7fffffffLL) return ATTN_ERR_SHAPE;   // K/V copy offsets are 32-bit
