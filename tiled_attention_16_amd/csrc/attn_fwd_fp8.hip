@@ -122,34 +122,43 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
     qop[cq] = join(lo, hi);
   }
 
-  // global -> register prefetch of one step's tiles
+  // global -> register prefetch of one step's tiles, through buffer loads
+  // bounded by the head's K (rows past N_k read as zeros) and V^T bytes (the
+  // host keeps both below 2^31), so that no load sits behind a branch
+  const __amdgpu_buffer_rsrc_t k_rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(K + k_base), (short)0, N_k * D, 0x00020000);
+  const __amdgpu_buffer_rsrc_t v_rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(Vt + v_base), (short)0, (int)(D * ldv), 0x00020000);
+  const int ldv_i = (int)ldv;
   u32x4 kbuf[kKChunks], vbuf[kVChunks];
   auto fetch = [&](int st) {
     const int k0 = st * kStep;
 #pragma unroll
     for (int j = 0; j < kKChunks; ++j) {
       const int i = tid + kThreads * j, r = i / (D / 16), cc = i % (D / 16);
-      kbuf[j] = (u32x4){0u, 0u, 0u, 0u};
-      if (k0 + r < N_k) kbuf[j] = *(const u32x4*)(K + k_base + (size_t)(k0 + r) * D + 16 * cc);
+      kbuf[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(k_rs, (k0 + r) * D + 16 * cc, 0, 0));
     }
 #pragma unroll
     for (int j = 0; j < kVChunks; ++j) {
       const int i = tid + kThreads * j, d = i / kVRowChunks, cc = i % kVRowChunks;
       const int kk = k0 + 16 * cc;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (kk < N_k) {
-        // the row stride holds whole 16-byte chunks; bytes of keys >= N_k are cleared
-        x = *(const u32x4*)(Vt + v_base + (size_t)d * ldv + kk);
-        const int nv = N_k - kk;
-        if (nv < 16) {
+      // the row stride holds whole 16-byte chunks; bytes of keys >= N_k are cleared
+      const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(v_rs, d * ldv_i + kk, 0, 0));
+      vbuf[j] = kk < N_k ? x : (u32x4){0u, 0u, 0u, 0u};
+    }
+    if (k0 + kStep > N_k) {   // the step holding key N_k: clear the keys past it in its chunk
+#pragma unroll
+      for (int j = 0; j < kVChunks; ++j) {
+        const int i = tid + kThreads * j, cc = i % kVRowChunks;
+        const int nv = N_k - (k0 + 16 * cc);
+        if (nv > 0 && nv < 16) {
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             const int keep = min(max(nv - 4 * w, 0), 4);
-            x[w] = keep == 4 ? x[w] : (x[w] & ((1u << (8 * keep)) - 1u));
+            vbuf[j][w] = keep == 4 ? vbuf[j][w] : (vbuf[j][w] & ((1u << (8 * keep)) - 1u));
           }
         }
       }
-      vbuf[j] = x;
     }
   };
   auto store = [&](int stage) {
@@ -216,7 +225,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
       for (int sl = 0; sl < kSlices; ++sl)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sl][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      {   // with the other half of the row (lane ^ 32): permlane32_swap gives each lane both values
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
       const float m_new = fmaxf(m_run, mx * c);
       // rescale only when some row's max grew
       if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
@@ -308,6 +320,7 @@ extern "C" int attn_fwd_fp8(const void* q, const void* k, const void* vt, long l
   if (bh > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   const long long n_qt = (N_q + kRowsWG - 1) / kRowsWG;
   if (bh * n_qt > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  if ((long long)N_k * d > 0x7fffffffLL || (long long)d * vt_row_stride > 0x7fffffffLL) return ATTN_ERR_SHAPE;   // 32-bit load offsets
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)vt | (uintptr_t)o) & 15) return ATTN_ERR_ALIGN;
   if ((uintptr_t)lse & 3) return ATTN_ERR_ALIGN;
   const size_t qn = (size_t)bh * N_q * d, kn = (size_t)bh * N_k * d, vn = (size_t)bh * d * vt_row_stride;
