@@ -265,6 +265,8 @@ int attn_bwd_block_sparse(const void* q, const void* k, const void* v, const voi
  *       aligned; row (b, h, c) holds V[b, h, j, c] for keys j = 0 .. N_k-1 at
  *       byte j. vt_row_stride is a multiple of 16 and >= N_k rounded up to 16
  *       (else ATTN_ERR_SHAPE); the bytes past N_k in a row are never used.
+ *       N_k * d and d * vt_row_stride (one head's K and V^T bytes) must be
+ *       below 2^31 (else ATTN_ERR_SHAPE).
  *   o   device, [B, H, N_q, d] bf16 output, 16-byte aligned.
  *   lse device, [B, H, N_q] fp32 output, natural log, or NULL.
  *   d   64 or 128. scale and the three descales must be finite (any sign).

@@ -228,6 +228,7 @@ def call_fp8(**kw):
     (dict(o=A16 * 3), ta.ATTN_ERR_ALIAS),            # o on top of vt
     (dict(lse=A16 * 4 + 32), ta.ATTN_ERR_ALIAS),     # lse inside o
     (dict(B=1 << 20, H=1 << 12, N_q=1 << 12), ta.ATTN_ERR_SHAPE),
+    (dict(N_k=1 << 25, vt_row_stride=1 << 25), ta.ATTN_ERR_SHAPE),   # a head's K/V^T past 32-bit load offsets
 ])
 def test_fp8_argument_errors_return_before_any_hip_call(lib, kw, status):
     assert call_fp8(**kw) == status
