@@ -91,6 +91,24 @@ def test_bwd_varlen_and_masked_rows(d, causal):
     assert np.all(dk[2, :, 150:] == 0) and np.all(dv[2, :, 150:] == 0)        # keys past the valid length
 
 
+RANGES = [
+    # B, H, N_q, N_k, causal, seqlens_k, q_start (d = 128, several 256-key workgroups): each wave's
+    # blocks split into a masked prefix (q_start, the causal diagonal), unmasked blocks and a masked
+    # tail (ragged rows); some waves have keys past the valid length and no unmasked block at all
+    (1, 2, 1000, 1000, 1, [900], [100]),
+    (1, 2, 1000, 1000, 0, [777], [333]),
+    (2, 1, 700, 900, 2, [900, 650], [0, 70]),
+]
+
+
+@pytest.mark.parametrize("case", RANGES, ids=[f"{c[0]}x{c[1]}x{c[2]}x{c[3]}_c{c[4]}" for c in RANGES])
+def test_bwd_masked_and_unmasked_block_ranges(case):
+    B, H, nq, nk, causal, sl, qs = case
+    q, k, v = make_random(B, H, nq, nk, 128, seed=nq + 3 * nk + causal)
+    g = make_dout((B, H, nq, 128), seed=nq + 7 * nk)
+    compare(q, k, v, g, np.float32(128 ** -0.5), causal, np.array(sl, np.int32), np.array(qs, np.int32))
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.09, 0.3])
 def test_bwd_scale_values(scale):
     q, k, v = make_random(1, 2, 130, 130, 128, seed=41)
